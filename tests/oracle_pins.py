@@ -1,0 +1,559 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError when the oracle
+disagrees with: values printed in the hand-worked golden files (tests/golden, each with its
+derivation), IEEE conversions done by numpy / torch, exact rational arithmetic
+(fractions.Fraction), closed forms (uniform dyadic tables), and invariants of the method
+(error bound, zero blocks, idempotence, block independence, power-of-two equivariance, dtype
+equivalence).  ``test_oracle_pins.py`` runs them on the oracle; ``test_oracle_mutants.py``
+runs them on copies of the oracle with planted mistakes and requires each copy to fail one.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _f32(s) -> np.float32:
+    s = str(s)
+    if s.startswith(("0x", "-0x")):
+        return np.float32(float.fromhex(s))
+    return np.float32(float(s))
+
+
+def _hand_table() -> np.ndarray:
+    """The 16-entry table of the hand-worked examples: -1, -7/8, ..., 3/4, 1 (double gap at
+    the top, holds -1, 0 and 1)."""
+    return np.float32([float(v) for v in _golden("blockwise_4bit_dyadic.json")["table"]])
+
+
+def _bits32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ------------------------------------------------------------------------------------------
+# IEEE conversions
+# ------------------------------------------------------------------------------------------
+
+def pin_f16_widen_all_patterns(o):
+    """All 65536 binary16 patterns widen like numpy's IEEE float16 -> float32."""
+    h = np.arange(65536, dtype=np.uint16)
+    ref = h.view(np.float16).astype(np.float32)
+    got = np.array([o.f16_to_f32(int(v)) for v in h], dtype=np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(_bits32(got[~nan]), _bits32(ref[~nan]))
+
+
+def pin_bf16_widen_all_patterns(o):
+    """All 65536 bfloat16 patterns widen like torch's bfloat16 -> float32."""
+    h = np.arange(65536, dtype=np.uint16)
+    ref = torch.from_numpy(h.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    got = np.array([o.bf16_to_f32(int(v)) for v in h], dtype=np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(_bits32(got[~nan]), _bits32(ref[~nan]))
+
+
+def _narrow_cases(seed):
+    r = _rng(seed)
+    bits = r.integers(0, 2**32, 60000, dtype=np.uint64).astype(np.uint32)
+    # values near bf16 / fp16 rounding ties and overflow / underflow edges
+    ties = np.arange(0, 65536, dtype=np.uint32) << 16 | 0x8000
+    edge = np.float32([0.0, -0.0, 65504.0, 65519.99, 65520.0, -65520.0, 2.0**-24, 2.0**-25,
+                       3 * 2.0**-26, 2.0**-14, 6.1e-5, 3.3895313e38, 3.3961776e38, 3.4e38,
+                       2.0**-126, 2.0**-133, 2.0**-134, 3 * 2.0**-135, 1.00390625, 1.01171875,
+                       np.inf, -np.inf])
+    return np.concatenate([bits.view(np.float32), ties.view(np.float32), edge])
+
+
+def pin_bf16_narrow_rne(o):
+    """binary32 -> bfloat16 equals torch's round-to-nearest-even (NaN -> quiet NaN, sign kept)."""
+    x = _narrow_cases(1)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([o.f32_to_bf16(float(v)) for v in x], dtype=np.uint16)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], ref[~nan])
+    sign = (_bits32(x[nan]) >> 31).astype(np.uint16) << 15
+    assert np.array_equal(got[nan], sign | 0x7FC0)
+
+
+def pin_f16_narrow_rne(o):
+    """binary32 -> binary16 equals numpy's round-to-nearest-even (NaN -> quiet NaN, sign kept)."""
+    x = _narrow_cases(2)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    got = np.array([o.f32_to_f16(float(v)) for v in x], dtype=np.uint16)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], ref[~nan])
+    sign = (_bits32(x[nan]) >> 31).astype(np.uint16) << 15
+    assert np.array_equal(got[nan], sign | 0x7E00)
+
+
+# ------------------------------------------------------------------------------------------
+# Nearest code
+# ------------------------------------------------------------------------------------------
+
+def _brute_nearest(y: np.float32, table) -> int:
+    """Exhaustive argmin of the exact rational distance, lowest index on ties."""
+    fy = Fraction(float(y))
+    best, best_d = None, None
+    for k, c in enumerate(table):
+        d = abs(fy - Fraction(float(c)))
+        if best_d is None or d < best_d:
+            best, best_d = k, d
+    return best
+
+
+def _probe_values(table, rng, count):
+    """Random values in [-1, 1], exact midpoints, and their binary32 neighbours."""
+    t = np.asarray(table, dtype=np.float64)
+    mids = ((t[:-1] + t[1:]) / 2).astype(np.float32)  # exact: entries are fine multiples of 2^-43
+    near = np.concatenate([np.nextafter(mids, np.float32(-2)), mids, np.nextafter(mids, np.float32(2))])
+    rand = rng.uniform(-1, 1, count).astype(np.float32)
+    return np.concatenate([near, rand, np.float32([0.0, -0.0, 1.0, -1.0, 2.0**-149, -2.0**-149])])
+
+
+def pin_nearest_brute_force(o):
+    """Nearest code equals the Fraction brute force on 16- and 256-entry tables."""
+    rng = _rng(3)
+    for table in (synth.table16(), synth.table256(), synth.dyadic_table(16)):
+        ys = _probe_values(table, rng, 200)
+        if len(table) == 256:
+            ys = np.concatenate([ys[::7], ys[-206:]])
+        for y in ys:
+            assert o.nearest(y, table) == _brute_nearest(y, table), (len(table), float(y))
+
+
+def pin_nearest_dyadic_closed_form(o):
+    """For c_k = -1 + 2k/K the nearest index is min(ceil((y+1)K/2 - 1/2), K-1)."""
+    rng = _rng(4)
+    for K in (16, 256):
+        table = synth.dyadic_table(K)
+        ys = _probe_values(table, rng, 2000)
+        for y in ys:
+            t = (Fraction(float(y)) + 1) * K / 2 - Fraction(1, 2)
+            expect = min(max(math.ceil(t), 0), K - 1)
+            assert o.nearest(y, table) == expect, (K, float(y))
+
+
+def pin_zero_code(o):
+    """Code of 0.0: index of the 0 entry; for a symmetric table without 0, the lower of the
+    two entries closest to 0 (the tie keeps the lower index)."""
+    assert o.zero_code(synth.dyadic_table(16)) == 8
+    t16 = synth.table16()
+    assert o.zero_code(t16) == int(np.nonzero(t16 == 0)[0][0])
+    assert o.zero_code(synth.table256()) == 127
+    assert o.zero_code(np.float32([-1, -0.5, 0.25, 1])) == 2  # 0.25 is strictly closer
+
+
+# ------------------------------------------------------------------------------------------
+# Normalization
+# ------------------------------------------------------------------------------------------
+
+def pin_reciprocal_product_at_most_one(o):
+    """For every binary32 significand, fl(a * fl(1/a)) is 1 or 1 - 2^-24, so |y| <= 1 and the
+    block maximum maps to +-1 (checked with numpy float32 over all 2^23 significands)."""
+    a = (np.arange(2**23, dtype=np.uint32) | 0x3F800000).view(np.float32)
+    with np.errstate(all="ignore"):
+        p = a * (np.float32(1) / a)
+    assert np.all((p == np.float32(1)) | (p == np.float32(1 - 2.0**-24)))
+    for v in (1.0, 1.5, 1.9999999, 3.0, 7.0, 0.1, 2.0**-60, 2.0**-130, 2.0**100):
+        y = o.normalize(v, v)
+        assert y in (np.float32(1), np.float32(1 - 2.0**-24)), (v, y)
+
+
+def _exact_quotient_rounded(x, a) -> np.float32:
+    """x/a rounded once to binary32, from exact rationals."""
+    q = Fraction(float(x)) / Fraction(float(a))
+    f = np.float32(float(q))  # nearest double then nearest float; checked below by bracketing
+    # correct the double-rounding corner explicitly
+    lo, hi = np.nextafter(f, np.float32(-np.inf)), np.nextafter(f, np.float32(np.inf))
+    best = min((lo, f, hi), key=lambda c: (abs(Fraction(float(c)) - q),
+                                           int(np.float32(c).view(np.uint32)) & 1))
+    return np.float32(best)
+
+
+def pin_normalize_exact_for_power_of_two_absmax(o):
+    """When absmax is a power of two, y = x / absmax exactly, across the guard ranges."""
+    rng = _rng(5)
+    for e in (-140, -100, -64, -63, -10, 0, 10, 63, 64, 65, 100, 127):
+        a = np.float32(2.0**e)
+        xs = (rng.uniform(-1, 1, 50) * float(a)).astype(np.float32)
+        for x in xs:
+            assert o.normalize(x, a) == _exact_quotient_rounded(x, a), (e, float(x))
+
+
+def pin_normalize_error_bound(o):
+    """|y - x/a| <= 2^-23 |x/a| + 2^-149 for any absmax (two roundings) and |y| <= 1."""
+    rng = _rng(6)
+    for e in (-145, -130, -70, -64, -20, 0, 20, 64, 70, 120, 127):
+        a = np.float32(rng.uniform(1, 2) * 2.0**e)
+        xs = np.concatenate([(rng.uniform(-1, 1, 40) * float(a)).astype(np.float32), [a, -a]])
+        for x in xs:
+            if not np.isfinite(x):
+                continue
+            y = o.normalize(x, a)
+            q = Fraction(float(x)) / Fraction(float(a))
+            err = abs(Fraction(float(y)) - q)
+            assert err <= Fraction(2) ** -23 * abs(q) + Fraction(2) ** -149, (e, float(x))
+            assert abs(y) <= 1
+
+
+# ------------------------------------------------------------------------------------------
+# Blockwise quantize / dequantize: golden examples
+# ------------------------------------------------------------------------------------------
+
+def pin_golden_blockwise(o):
+    g = _golden("blockwise_4bit_dyadic.json")
+    table = np.float32([float(v) for v in g["table"]])
+    for ex in g["examples"]:
+        x = np.array([_f32(v) for v in ex["x"]], dtype=np.float32)
+        absmax, packed = o.quantize_blockwise(x, oracle.F32, ex["blocksize"], table)
+        assert np.array_equal(_bits32(absmax), _bits32([_f32(v) for v in ex["absmax"]])), ex["name"]
+        assert packed.tobytes().hex() == ex["packed_hex"].replace(" ", ""), ex["name"]
+        assert list(oracle.unpack_codes(packed, x.size, 16)) == ex["codes"], ex["name"]
+        out = o.dequantize_blockwise(packed, absmax, x.size, oracle.F32, ex["blocksize"], table)
+        assert np.array_equal(_bits32(out), _bits32([_f32(v) for v in ex["dequant_f32"]])), ex["name"]
+
+
+def pin_golden_bf16_rounding(o):
+    g = _golden("dequant_rounding_gguf_nested.json")["bf16_rounding"]
+    table = _hand_table()
+    for case in g["cases"]:
+        k = int(np.nonzero(table == np.float32(float(case["code"])))[0][0])
+        packed = np.array([(k << 4) | k], dtype=np.uint8)
+        absmax = np.float32([float(case["absmax"])])
+        out = o.dequantize_blockwise(packed, absmax, 2, oracle.BF16, 32, table)
+        assert int(out[0]) == int(case["bf16_hex"], 16), case
+        assert int(out[1]) == int(case["bf16_hex"], 16), case
+        assert o.bf16_to_f32(int(out[0])) == np.float32(float(case["value"])), case
+
+
+def pin_golden_q32(o):
+    g = _golden("dequant_rounding_gguf_nested.json")["q32"]
+    for blk_hex, vals in zip(g["q4_blocks_hex"], g["q4_values"]):
+        blk = np.frombuffer(bytes.fromhex(blk_hex), dtype=np.uint8)
+        out = o.dequant_q32(blk, 32, 32, oracle.Q4, oracle.F32)
+        assert np.array_equal(_bits32(out), _bits32([_f32(v) for v in vals])), blk_hex
+        out16 = o.dequant_q32(blk, 32, 32, oracle.Q4, oracle.BF16)
+        ref = torch.tensor([float(v) for v in vals], dtype=torch.float32).to(torch.bfloat16)
+        assert np.array_equal(out16, ref.view(torch.int16).numpy().view(np.uint16)), blk_hex
+    for d_hex, codes, vals in zip(g["q8_blocks_hex"], g["q8_codes"], g["q8_values"]):
+        blk = np.concatenate([np.frombuffer(bytes.fromhex(d_hex), dtype=np.uint8),
+                              np.array(codes, dtype=np.int8).view(np.uint8)])
+        out16 = o.dequant_q32(blk, 32, 32, oracle.Q8, oracle.BF16)
+        ref = np.array([o.f32_to_bf16(float(v)) for v in vals], dtype=np.uint16)
+        expect = torch.tensor([float(v) for v in vals]).to(torch.bfloat16)
+        assert np.array_equal(ref, expect.view(torch.int16).numpy().view(np.uint16))
+        assert np.array_equal(out16, ref), d_hex
+
+
+def pin_golden_nested(o):
+    g = _golden("dequant_rounding_gguf_nested.json")["nested"]
+    t16 = _hand_table()
+    t256 = synth.dyadic_table(256)
+    B = g["blocksize"]
+    x = np.zeros(B * len(g["block_heads"]), np.float32)
+    x[::B] = [float(v) for v in g["block_heads"]]
+    r = o.quantize_nested(x, oracle.F32, B, t16, t256, g["blocksize2"])
+    assert np.array_equal(r["absmax"], np.float32([float(v) for v in g["absmax"]]))
+    assert r["mean"] == np.float32(float(g["mean"]))
+    assert list(r["q2"]) == g["q2"]
+    assert np.array_equal(r["absmax2"], np.float32([float(v) for v in g["absmax2"]]))
+    assert r["packed"].tobytes().hex() == g["packed_block_hex"] * len(g["block_heads"])
+    out = o.dequantize_nested(r["packed"], r["q2"], r["absmax2"], r["mean"], x.size, oracle.F32,
+                              B, t16, t256, g["blocksize2"])
+    heads = np.float32([float(v) for v in g["dequant_heads_f32"]])
+    assert np.array_equal(out[::B], heads)
+    assert np.all(np.delete(out, np.arange(0, x.size, B)) == 0)
+
+
+# ------------------------------------------------------------------------------------------
+# Blockwise: exact rational checks and invariants on random data
+# ------------------------------------------------------------------------------------------
+
+def pin_quantize_vs_exact_rational(o):
+    """Codes from the oracle's quantize equal the brute-force nearest code of the exactly
+    rounded quotient fl32(x/a) wherever that quotient is provably the normalized value
+    (power-of-two absmax), and absmax equals the max of |x| over finite x."""
+    rng = _rng(7)
+    for table in (synth.table16(), synth.table256()):
+        K = len(table)
+        x = rng.normal(0, 1, 96).astype(np.float32)
+        x[:32] = np.clip(x[:32], -3.9, 3.9)
+        x[32:64] = np.clip(x[32:64], -0.49, 0.49)
+        x[64:] = np.clip(x[64:], -7.9, 7.9)
+        x[31] = 4.0   # block 0 absmax = 4, a power of two
+        x[63] = -0.5  # block 1 absmax = 0.5
+        x[64] = 8.0   # block 2 absmax = 8
+        x[[5, 40, 77]] = [np.nan, np.inf, -np.inf]
+        absmax, packed = o.quantize_blockwise(x, oracle.F32, 32, table)
+        codes = oracle.unpack_codes(packed, x.size, K)
+        z = _brute_nearest(np.float32(0), table)
+        for b in range(3):
+            blk = x[32 * b:32 * b + 32]
+            fin = blk[np.isfinite(blk)]
+            assert absmax[b] == np.max(np.abs(fin))
+            for i, v in enumerate(blk):
+                if not np.isfinite(v):
+                    assert codes[32 * b + i] == z
+                    continue
+                y = _exact_quotient_rounded(v, absmax[b])
+                assert codes[32 * b + i] == _brute_nearest(y, table), (K, b, i)
+
+
+def _table_max_gap(table):
+    t = np.asarray(table, np.float64)
+    g = np.max(np.diff(t))
+    return max(g / 2, 1 - t[-1], t[0] + 1)
+
+
+def pin_error_bound(o):
+    """|dequant(quant(x)) - x| <= a_b * (max gap / 2) + a_b * 2^-22 (fp32 output)."""
+    rng = _rng(8)
+    for table, B in ((synth.table16(), 64), (synth.table256(), 256), (synth.dyadic_table(16), 32)):
+        x = rng.normal(0, 1, 4096 + 17).astype(np.float32)
+        absmax, packed = o.quantize_blockwise(x, oracle.F32, B, table)
+        y = o.dequantize_blockwise(packed, absmax, x.size, oracle.F32, B, table)
+        a = np.repeat(absmax, B)[:x.size].astype(np.float64)
+        bound = a * _table_max_gap(table) + a * 2.0**-22
+        assert np.all(np.abs(y.astype(np.float64) - x) <= bound)
+
+
+def pin_zero_blocks(o):
+    """All-zero and all-non-finite blocks give absmax +0 and all-zero dequantized output;
+    the sign of a zero output is that of the zero code's entry."""
+    t = synth.table16()
+    x = np.zeros(200, np.float32)
+    x[64:128] = -0.0
+    x[128:192] = [np.nan, np.inf, -np.inf, np.nan] * 16
+    x[192:] = [1, -1, 0.5, 0, 0, 0, 0, 0]
+    absmax, packed = o.quantize_blockwise(x, oracle.F32, 64, t)
+    assert np.array_equal(_bits32(absmax[:3]), np.zeros(3, np.uint32))
+    out = o.dequantize_blockwise(packed, absmax, x.size, oracle.F32, 64, t)
+    assert np.all(out[:192] == 0)
+    assert np.all(np.signbit(out[:192]) == False)  # noqa: E712  (c[z] = +0)
+    t256 = synth.table256()  # no 0 entry: z = index of -p_1, so zeros come back as -0
+    absmax, packed = o.quantize_blockwise(x[:64], oracle.F32, 64, t256)
+    out = o.dequantize_blockwise(packed, absmax, 64, oracle.F32, 64, t256)
+    assert np.all(out == 0) and np.all(np.signbit(out))
+
+
+def pin_idempotence(o):
+    """quant(dequant(quant(x))) reproduces codes and absmax (fp32 output; tables with +-1)."""
+    rng = _rng(9)
+    for table, B in ((synth.table16(), 64), (synth.table256(), 4096), (synth.table16(), 32)):
+        x = rng.normal(0, 0.02, 3 * B + 5).astype(np.float32)
+        absmax, packed = o.quantize_blockwise(x, oracle.F32, B, table)
+        y = o.dequantize_blockwise(packed, absmax, x.size, oracle.F32, B, table)
+        absmax2, packed2 = o.quantize_blockwise(y, oracle.F32, B, table)
+        assert np.array_equal(absmax, absmax2)
+        assert np.array_equal(packed, packed2)
+
+
+def pin_block_independence(o):
+    """Changing one block changes only that block's absmax, codes and outputs."""
+    rng = _rng(10)
+    t = synth.table16()
+    x = rng.normal(0, 1, 640).astype(np.float32)
+    a1, p1 = o.quantize_blockwise(x, oracle.F32, 64, t)
+    x2 = x.copy()
+    x2[192:256] = rng.normal(0, 5, 64)
+    a2, p2 = o.quantize_blockwise(x2, oracle.F32, 64, t)
+    c1, c2 = oracle.unpack_codes(p1, 640, 16), oracle.unpack_codes(p2, 640, 16)
+    keep = np.ones(640, bool)
+    keep[192:256] = False
+    assert np.array_equal(c1[keep], c2[keep])
+    assert np.array_equal(np.delete(a1, 3), np.delete(a2, 3))
+    assert a1[3] != a2[3]
+
+
+def pin_power_of_two_equivariance(o):
+    """x * 2^k gives the same codes and absmax * 2^k (no guard change, no under/overflow)."""
+    rng = _rng(11)
+    t = synth.table256()
+    x = rng.normal(0, 1, 1000).astype(np.float32)
+    a, p = o.quantize_blockwise(x, oracle.F32, 128, t)
+    for k in (-20, -3, 5, 30):
+        s = np.float32(2.0**k)
+        a2, p2 = o.quantize_blockwise(x * s, oracle.F32, 128, t)
+        assert np.array_equal(a * s, a2)
+        assert np.array_equal(p, p2)
+
+
+def pin_dtype_equivalence(o):
+    """The same values given as fp32, fp16 and bf16 give identical codes and absmax."""
+    rng = _rng(12)
+    vals = rng.normal(0, 1, 777).astype(np.float32)
+    vals = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float16).float()
+    vals = vals.to(torch.bfloat16).float()  # exactly representable in both 16-bit types
+    ok = (vals.to(torch.float16).float() == vals) & (vals.to(torch.bfloat16).float() == vals)
+    vals = vals[ok].numpy()
+    vals[[3, 9]] = [np.nan, np.inf]
+    f16 = vals.astype(np.float16).view(np.uint16)
+    bf16 = synth.to_bits16(torch.from_numpy(vals).to(torch.bfloat16))
+    for table in (synth.table16(), synth.table256()):
+        r32 = o.quantize_blockwise(vals, oracle.F32, 64, table)
+        r16 = o.quantize_blockwise(f16, oracle.F16, 64, table)
+        rb = o.quantize_blockwise(bf16, oracle.BF16, 64, table)
+        for r in (r16, rb):
+            assert np.array_equal(r32[0], r[0]) and np.array_equal(r32[1], r[1])
+
+
+def pin_dequant_vs_library_rounding(o):
+    """Dequantized fp16/bf16 outputs equal numpy's float32 product rounded by numpy / torch."""
+    rng = _rng(13)
+    for table, B in ((synth.table16(), 64), (synth.table256(), 256)):
+        K = len(table)
+        n = 3001
+        absmax = np.abs(rng.normal(0, 3, -(-n // B))).astype(np.float32)
+        absmax[0] = 70000.0  # overflows fp16 for large codes
+        codes = rng.integers(0, K, n).astype(np.uint8)
+        if K == 16:
+            cc = np.concatenate([codes, np.zeros(n % 2, np.uint8)])
+            packed = ((cc[0::2] << 4) | cc[1::2]).astype(np.uint8)
+        else:
+            packed = codes
+        prod = table[codes] * np.repeat(absmax, B)[:n]
+        out_bf = o.dequantize_blockwise(packed, absmax, n, oracle.BF16, B, table)
+        ref_bf = synth.to_bits16(torch.from_numpy(prod).to(torch.bfloat16))
+        assert np.array_equal(out_bf, ref_bf)
+        out_h = o.dequantize_blockwise(packed, absmax, n, oracle.F16, B, table)
+        with np.errstate(over="ignore"):
+            ref_h = prod.astype(np.float16).view(np.uint16)
+        assert np.array_equal(out_h, ref_h)
+        out_f = o.dequantize_blockwise(packed, absmax, n, oracle.F32, B, table)
+        assert np.array_equal(_bits32(out_f), _bits32(prod))
+
+
+def pin_packing_layout(o):
+    """Packed bytes: first element of each pair in the high nibble, odd n padded with 0,
+    ceil(n/2) bytes (33 values -> 17 bytes); 8-bit codes are one byte each."""
+    t = synth.dyadic_table(16)
+    x = (np.arange(33, dtype=np.float32) % 16 - 8) / 8  # y = x (absmax 1): codes k = 8x + 8
+    x[0] = 1.0
+    _, packed = o.quantize_blockwise(x, oracle.F32, 64, t)
+    assert packed.size == 17
+    expect = [min(int(8 * v + 8), 15) for v in x] + [0]
+    assert list(packed) == [(expect[2 * j] << 4) | expect[2 * j + 1] for j in range(17)]
+    t256 = synth.dyadic_table(256)
+    _, p8 = o.quantize_blockwise(x, oracle.F32, 64, t256)
+    assert p8.size == 33
+    assert list(p8) == [min(int(128 * v + 128), 255) for v in x]
+
+
+# ------------------------------------------------------------------------------------------
+# Nested statistics
+# ------------------------------------------------------------------------------------------
+
+def _pairwise_bottom_up(a: np.ndarray) -> float:
+    """Second implementation of the padded pairwise sum: iterative, level by level."""
+    v = np.asarray(a, np.float64)
+    P = 1
+    while P < v.size:
+        P *= 2
+    v = np.concatenate([v, np.zeros(P - v.size)])
+    while v.size > 1:
+        v = v[0::2] + v[1::2]
+    return float(v[0])
+
+
+def pin_pairwise_sum(o):
+    """S is the padded pairwise sum: [2^53, 1, 1, 2] gives (2^53 + 1) + (1 + 2) = 2^53 + 4
+    (2^53 + 1 rounds to 2^53, then 2^53 + 3 ties to the even 2^53 + 4), where a left-to-right
+    sum would give 2^53 + 2; random data matches an independent bottom-up evaluation."""
+    assert o.pairwise_sum(np.float32([2.0**53, 1, 1, 2])) == 2.0**53 + 4
+    # padded to [2^53, 1, 1, 0]: (2^53 + 1) + (1 + 0); each 2^53 + 1 ties to the even 2^53
+    assert o.pairwise_sum(np.float32([2.0**53, 1, 1])) == 2.0**53
+    rng = _rng(16)
+    for nb in (1, 5, 1000, 4097):
+        a = np.abs(rng.normal(0, 1, nb) * rng.choice([1e-6, 1, 1e6], nb)).astype(np.float32)
+        assert o.pairwise_sum(a) == _pairwise_bottom_up(a), nb
+
+
+def pin_nested_mean(o):
+    """Nested mean equals RN32(pairwise / nb) from an independent bottom-up pairwise sum, and
+    lies within one binary32 ulp of the exact mean."""
+    rng = _rng(14)
+    for nb in (1, 2, 3, 255, 256, 257, 1000, 4097, 65536 + 3):
+        a = np.abs(rng.normal(0, 1, nb) * rng.choice([1e-3, 1, 1e3], nb)).astype(np.float32)
+        m = o.nested_mean(a)
+        assert m == np.float32(_pairwise_bottom_up(a) / nb), nb
+        exact = sum(Fraction(float(v)) for v in a) / nb if nb <= 4097 else \
+            Fraction(math.fsum(a.astype(np.float64))) / nb
+        ulp = Fraction(float(np.spacing(np.float32(float(exact)))))
+        assert abs(Fraction(float(m)) - exact) <= ulp, nb
+
+
+def pin_nested_composition(o):
+    """Nested statistics equal: the blockwise absmax; the pairwise mean; the 256-entry
+    blockwise quantization of d = fl32(a - mean) in groups; and the nested dequantization
+    equals the blockwise dequantization with a' = fl32(fl32(c2[q2] * a2) + mean) computed in
+    numpy float32."""
+    rng = _rng(15)
+    t16, t256 = synth.table16(), synth.table256()
+    x = rng.normal(0, 0.02, 64 * 600 + 7).astype(np.float32)
+    r = o.quantize_nested(x, oracle.F32, 64, t16, t256, 256)
+    a, packed = o.quantize_blockwise(x, oracle.F32, 64, t16)
+    assert np.array_equal(r["absmax"], a) and np.array_equal(r["packed"], packed)
+    assert r["mean"] == np.float32(_pairwise_bottom_up(a) / a.size)
+    d = (a - r["mean"]).astype(np.float32)
+    a2, q2 = o.quantize_blockwise(d, oracle.F32, 256, t256)
+    assert np.array_equal(r["absmax2"], a2) and np.array_equal(r["q2"], q2)
+    assert np.all(r["absmax2"] == np.array([np.max(np.abs(d[g:g + 256])) for g in range(0, d.size, 256)]))
+    rebuilt = (t256[r["q2"]] * np.repeat(r["absmax2"], 256)[:a.size]).astype(np.float32) + r["mean"]
+    for dt in (oracle.F32, oracle.BF16):
+        out = o.dequantize_nested(r["packed"], r["q2"], r["absmax2"], r["mean"], x.size, dt, 64,
+                                  t16, t256, 256)
+        ref = o.dequantize_blockwise(r["packed"], rebuilt.astype(np.float32), x.size, dt, 64, t16)
+        assert np.array_equal(out.view(np.uint8), ref.view(np.uint8))
+
+
+# ------------------------------------------------------------------------------------------
+# GGUF-style blocks
+# ------------------------------------------------------------------------------------------
+
+def pin_q32_closed_form(o):
+    """Q4 / Q8 dequant equals numpy float32 (q-8)*d or q*d (exact), rounded by torch to bf16,
+    with element j < 16 the low nibble of byte j and element 16+j its high nibble."""
+    for fmt, name in ((oracle.Q4, "q4"), (oracle.Q8, "q8")):
+        nblk = 700
+        blocks = synth.q32_blocks(nblk, name, seed=21).numpy()
+        bs = 18 if name == "q4" else 34
+        b = blocks.reshape(nblk, bs)
+        d = b[:, :2].copy().view(np.float16).astype(np.float32).reshape(nblk, 1)
+        if name == "q4":
+            lo = (b[:, 2:] & 15).astype(np.float32) - 8
+            hi = (b[:, 2:] >> 4).astype(np.float32) - 8
+            q = np.concatenate([lo, hi], axis=1)
+        else:
+            q = b[:, 2:].view(np.int8).astype(np.float32)
+        prod = (q * d).reshape(-1)
+        ref = synth.to_bits16(torch.from_numpy(prod).to(torch.bfloat16))
+        out = o.dequant_q32(blocks, nblk * 32, 32 * 7, fmt, oracle.BF16)
+        assert np.array_equal(out, ref), name
+        out32 = o.dequant_q32(blocks, nblk * 32, 32 * 7, fmt, oracle.F32)
+        assert np.array_equal(_bits32(out32), _bits32(prod)), name
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

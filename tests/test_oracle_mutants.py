@@ -1,0 +1,61 @@
+"""Mutation test of the oracle's pins.
+
+Each case plants one plausible mistake in a copy of oracle/bq_oracle.c (on the CPU, in a
+temporary directory), builds it, and requires at least one pin of oracle_pins.py to fail on
+it.  A mutant that every pin accepts would mean the pins cannot see that kind of mistake.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = {
+    "nibble_order_swapped": ("(uint8_t)((hi << 4) | lo)", "(uint8_t)((lo << 4) | hi)"),
+    "pad_nibble_not_zero": ("codes[2 * j + 1] : 0;", "codes[2 * j + 1] : 15;"),
+    "ties_to_higher_index": ("if (2.0 * (double)y > (double)c[best]",
+                             "if (2.0 * (double)y >= (double)c[best]"),
+    "absmax_keeps_infinities": ("if (isfinite(v) && fabsf(v) > a)", "if (!isnan(v) && fabsf(v) > a)"),
+    "absmax_signed_max": ("if (isfinite(v) && fabsf(v) > a) a = fabsf(v);",
+                          "if (isfinite(v) && v > a) a = v;"),
+    "divide_instead_of_reciprocal": ("float y = xs * r;", "float y = xs / as;"),
+    "guard_dropped": ("if (a < 0x1p-64f) return 0x1p64f;", "if (0) return 0x1p64f;"),
+    "zero_code_is_index_0": ("int bqo_zero_code(const float* c, int K) { return bqo_nearest(0.0f, c, K); }",
+                             "int bqo_zero_code(const float* c, int K) { (void)c; (void)K; return 0; }"),
+    "narrowing_truncates": ("return rint(a / quantum) * quantum;", "return floor(a / quantum) * quantum;"),
+    "f16_subnormal_scale": ("mag = ldexpf((float)m, -24);", "mag = ldexpf((float)m, -25);"),
+    "bf16_exponent_bias": ("mag = ldexpf((float)(128 + m), e - 134);", "mag = ldexpf((float)(128 + m), e - 133);"),
+    "sequential_sum": ("return pairwise_sum(a, n, 0, len);",
+                       "double S = 0; for (int64_t i = 0; i < n; ++i) S += a[i]; return S;"),
+    "mean_in_binary32": ("return (float)(S / (double)nb);", "return (float)S / (float)nb;"),
+    "mean_not_subtracted": ("for (int64_t b = 0; b < nb; ++b) d[b] = absmax[b] - m;",
+                            "for (int64_t b = 0; b < nb; ++b) d[b] = absmax[b];"),
+    "mean_not_added_back": ("a[b] = scaled + mean;", "a[b] = scaled;"),
+    "q32_nibbles_swapped": ("int lo = blk[2 + j] & 0x0f, hi = blk[2 + j] >> 4;",
+                            "int hi = blk[2 + j] & 0x0f, lo = blk[2 + j] >> 4;"),
+    "q32_offset_7": ("(float)(lo - 8) * d", "(float)(lo - 7) * d"),
+    "q8_unsigned_codes": ("int q = (int8_t)blk[2 + j];", "int q = (uint8_t)blk[2 + j];"),
+    "dequant_wrong_block": ("* absmax[i / B];", "* absmax[(i + 1) / B];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    with open(oracle.SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, "mutation target not found (or not unique): %r" % old
+    path = os.path.join(tmp_path, "mutant.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib = oracle.load(oracle.build(path, os.path.join(tmp_path, "libmutant.so")))
+    o = oracle.Oracle(lib)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(o)
+        except Exception:  # any rejection counts
+            caught.append(pin.__name__)
+            break
+    assert caught, "no pin detects the planted mistake %s" % name
