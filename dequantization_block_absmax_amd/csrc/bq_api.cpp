@@ -1,0 +1,197 @@
+// bq_api.cpp -- the C ABI of libbq (declared in include/bq.h).
+//
+// Each entry point validates everything on the host first (validation once, at the
+// interface: the boundary checks of "[OMNIML-5899] Add CUDA kernels for IQ packing"), then
+// enqueues its kernels on the caller's stream ("Respect the current CUDA stream in blockwise
+// quantization", bitsandbytes PR 2052).  Tables are passed to kernels by value: no
+// allocation, no host-to-device copy and no synchronization per call (the per-call constant
+// upload measured in "Cache device-side constants in dequant kernels", ComfyUI-GGUF PR 472,
+// "Problem", and the graph-capture limitation in PR 2052, "Limitations").
+#include <hip/hip_runtime_api.h>
+#include <string.h>
+
+#include "../../include/bq.h"
+#include "bq_internal.h"
+
+namespace {
+
+bool valid_dtype(bq_dtype d) { return d == BQ_F32 || d == BQ_F16 || d == BQ_BF16; }
+
+bool valid_blocksize(int32_t b) {
+  for (int v = 32; v <= 4096; v *= 2)
+    if (b == v) return true;
+  return false;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+thread_local int g_last_hip_error = 0;
+
+bq_status hip_status(int e) {
+  if (e == 0) return BQ_OK;
+  g_last_hip_error = e;
+  return BQ_ERR_HIP;
+}
+
+int64_t nblocks(int64_t n, int32_t b) { return (n + b - 1) / b; }
+
+// Offsets inside the nested workspace: binary32 absmax[nb], then binary64 partial sums.
+size_t ws_partials_offset(int64_t nb) { return ((size_t)nb * 4 + 255) & ~(size_t)255; }
+
+size_t ws_bytes(int64_t nb) { return ws_partials_offset(nb) + (size_t)((nb + 255) / 256) * 8; }
+
+bq_status check_table(const bq_code_table* t, bq::PreparedTable* out) {
+  if (t == nullptr || t->entries == nullptr) return BQ_ERR_NULL;
+  return bq::prepare_table(t->entries, t->size, out) ? BQ_OK : BQ_ERR_TABLE;
+}
+
+// Scratch for prepared tables: prepared per call on the host, never shared between calls.
+struct Tables {
+  bq::PreparedTable data, stats;
+};
+
+}  // namespace
+
+extern "C" {
+
+int bq_last_hip_error(void) { return g_last_hip_error; }
+
+const char* bq_status_string(bq_status s) {
+  switch (s) {
+    case BQ_OK: return "ok";
+    case BQ_ERR_NULL: return "a required pointer is NULL";
+    case BQ_ERR_DTYPE: return "unknown dtype";
+    case BQ_ERR_SIZE: return "invalid element count";
+    case BQ_ERR_BLOCKSIZE: return "block size must be a power of two in [32, 4096]";
+    case BQ_ERR_TABLE: return "invalid code table";
+    case BQ_ERR_ALIGNMENT: return "misaligned device pointer";
+    case BQ_ERR_FORMAT: return "unknown block format or row length";
+    case BQ_ERR_WORKSPACE: return "nested workspace missing or too small";
+    case BQ_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+bq_status bq_quantize_blockwise(const void* in, bq_dtype dtype, int64_t n, int32_t blocksize,
+                                const bq_code_table* code_table, float* absmax, uint8_t* packed,
+                                hipStream_t stream) {
+  if (!valid_dtype(dtype)) return BQ_ERR_DTYPE;
+  if (n < 0) return BQ_ERR_SIZE;
+  if (!valid_blocksize(blocksize)) return BQ_ERR_BLOCKSIZE;
+  Tables t;
+  bq_status st = check_table(code_table, &t.data);
+  if (st != BQ_OK) return st;
+  if (n == 0) return BQ_OK;
+  if (in == nullptr || absmax == nullptr || packed == nullptr) return BQ_ERR_NULL;
+  if (nblocks(n, blocksize) > INT32_MAX) return BQ_ERR_SIZE;
+  if (!aligned(in, 16) || !aligned(packed, 16) || !aligned(absmax, 4)) return BQ_ERR_ALIGNMENT;
+  return hip_status(bq::launch_quantize(in, dtype, n, blocksize, t.data, absmax, packed, stream));
+}
+
+bq_status bq_dequantize_blockwise(void* out, bq_dtype dtype, int64_t n, int32_t blocksize,
+                                  const bq_code_table* code_table, const float* absmax,
+                                  const uint8_t* packed, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return BQ_ERR_DTYPE;
+  if (n < 0) return BQ_ERR_SIZE;
+  if (!valid_blocksize(blocksize)) return BQ_ERR_BLOCKSIZE;
+  Tables t;
+  bq_status st = check_table(code_table, &t.data);
+  if (st != BQ_OK) return st;
+  if (n == 0) return BQ_OK;
+  if (out == nullptr || absmax == nullptr || packed == nullptr) return BQ_ERR_NULL;
+  if (nblocks(n, blocksize) > INT32_MAX) return BQ_ERR_SIZE;
+  if (!aligned(out, 16) || !aligned(packed, 16) || !aligned(absmax, 4)) return BQ_ERR_ALIGNMENT;
+  bq::DequantArgs a;
+  memset(&a, 0, sizeof(a));
+  memcpy(a.c, t.data.c, sizeof(float) * t.data.K);
+  a.K = t.data.K;
+  return hip_status(bq::launch_dequantize(out, dtype, n, blocksize, a, absmax, packed, stream));
+}
+
+size_t bq_nested_workspace_bytes(int64_t n, int32_t blocksize, int32_t blocksize2) {
+  (void)blocksize2;
+  if (n <= 0 || !valid_blocksize(blocksize)) return 0;
+  return ws_bytes(nblocks(n, blocksize));
+}
+
+static bq_status check_nested(const bq_nested_stats* stats, bq::PreparedTable* t2, bool need_ws,
+                              int64_t n, int32_t blocksize) {
+  if (stats == nullptr) return BQ_ERR_NULL;
+  if (!valid_blocksize(stats->blocksize2)) return BQ_ERR_BLOCKSIZE;
+  bq_status st = check_table(stats->table, t2);
+  if (st != BQ_OK) return st;
+  if (t2->K != 256) return BQ_ERR_TABLE;
+  if (n == 0) return BQ_OK;
+  if (stats->qabsmax == nullptr || stats->absmax2 == nullptr || stats->mean == nullptr) return BQ_ERR_NULL;
+  if (!aligned(stats->absmax2, 4) || !aligned(stats->mean, 4)) return BQ_ERR_ALIGNMENT;
+  if (need_ws) {
+    if (stats->workspace == nullptr) return BQ_ERR_WORKSPACE;
+    if (!aligned(stats->workspace, 256)) return BQ_ERR_ALIGNMENT;
+    if (stats->workspace_bytes < ws_bytes(nblocks(n, blocksize))) return BQ_ERR_WORKSPACE;
+  }
+  return BQ_OK;
+}
+
+bq_status bq_quantize_nested(const void* in, bq_dtype dtype, int64_t n, int32_t blocksize,
+                             const bq_code_table* code_table, bq_nested_stats* stats,
+                             uint8_t* packed, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return BQ_ERR_DTYPE;
+  if (n < 0) return BQ_ERR_SIZE;
+  if (!valid_blocksize(blocksize)) return BQ_ERR_BLOCKSIZE;
+  Tables t;
+  bq_status st = check_table(code_table, &t.data);
+  if (st != BQ_OK) return st;
+  st = check_nested(stats, &t.stats, true, n, blocksize);
+  if (st != BQ_OK) return st;
+  if (n == 0) return BQ_OK;
+  if (in == nullptr || packed == nullptr) return BQ_ERR_NULL;
+  const int64_t nb = nblocks(n, blocksize);
+  if (nb > INT32_MAX) return BQ_ERR_SIZE;
+  if (!aligned(in, 16) || !aligned(packed, 16)) return BQ_ERR_ALIGNMENT;
+  float* ws_absmax = static_cast<float*>(stats->workspace);
+  double* ws_partials = reinterpret_cast<double*>(static_cast<uint8_t*>(stats->workspace) + ws_partials_offset(nb));
+  int e = bq::launch_quantize(in, dtype, n, blocksize, t.data, ws_absmax, packed, stream);
+  if (e != 0) return hip_status(e);
+  e = bq::launch_nested_stats(ws_absmax, nb, stats->blocksize2, t.stats, ws_partials, stats->qabsmax,
+                              stats->absmax2, stats->mean, stream);
+  return hip_status(e);
+}
+
+bq_status bq_dequantize_nested(void* out, bq_dtype dtype, int64_t n, int32_t blocksize,
+                               const bq_code_table* code_table, const bq_nested_stats* stats,
+                               const uint8_t* packed, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return BQ_ERR_DTYPE;
+  if (n < 0) return BQ_ERR_SIZE;
+  if (!valid_blocksize(blocksize)) return BQ_ERR_BLOCKSIZE;
+  Tables t;
+  bq_status st = check_table(code_table, &t.data);
+  if (st != BQ_OK) return st;
+  st = check_nested(stats, &t.stats, false, n, blocksize);
+  if (st != BQ_OK) return st;
+  if (n == 0) return BQ_OK;
+  if (out == nullptr || packed == nullptr) return BQ_ERR_NULL;
+  if (nblocks(n, blocksize) > INT32_MAX) return BQ_ERR_SIZE;
+  if (!aligned(out, 16) || !aligned(packed, 16)) return BQ_ERR_ALIGNMENT;
+  bq::NestedDequantArgs a;
+  memset(&a, 0, sizeof(a));
+  memcpy(a.c, t.data.c, sizeof(float) * t.data.K);
+  memcpy(a.c2, t.stats.c, sizeof(float) * 256);
+  a.K = t.data.K;
+  return hip_status(bq::launch_dequantize_nested(out, dtype, n, blocksize, stats->blocksize2, a, stats->qabsmax,
+                                                 stats->absmax2, stats->mean, packed, stream));
+}
+
+bq_status bq_dequant_q32(const void* blocks, bq_dtype dtype, int64_t n, int32_t row_len,
+                         bq_q32_format format, void* out, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return BQ_ERR_DTYPE;
+  if (format != BQ_Q32_Q4 && format != BQ_Q32_Q8) return BQ_ERR_FORMAT;
+  if (row_len <= 0 || row_len % 32 != 0) return BQ_ERR_FORMAT;
+  if (n < 0 || n % row_len != 0) return BQ_ERR_SIZE;
+  if (n == 0) return BQ_OK;
+  if (blocks == nullptr || out == nullptr) return BQ_ERR_NULL;
+  if (n / 32 > INT32_MAX) return BQ_ERR_SIZE;
+  if (!aligned(blocks, 16) || !aligned(out, 16)) return BQ_ERR_ALIGNMENT;
+  return hip_status(bq::launch_q32(blocks, dtype, n, (int)format, out, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// bq_device.h -- device helpers shared by the quantize and statistics kernels: the
+// per-workgroup LUT of the nearest-code search and the search itself.  The bucket functions
+// and the LUT contents are described in bq_internal.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "bq_internal.h"
+
+namespace bq {
+
+template <int M>
+struct Entry { typedef uint4 type; };
+template <>
+struct Entry<1> { typedef uint2 type; };
+
+// Nearest code of y (see bq_internal.h for the bucket functions).
+template <int MODE, int M>
+__device__ __forceinline__ uint32_t nearest_code(float y, const QuantArgs& qa,
+                                                 const typename Entry<M>::type* lut,
+                                                 const float* s_thr) {
+  if constexpr (MODE == SEARCH) {
+    if (!(fabsf(y) <= 1.0f)) return (uint32_t)qa.z;
+    int q = 0;
+    for (int step = qa.K >> 1; step >= 1; step >>= 1) q += (y >= s_thr[q + step - 1]) ? step : 0;
+    return (uint32_t)q;
+  } else {
+    uint32_t idx;
+    if constexpr (MODE == LIN) {
+      float zz = __builtin_fmaf(y, kLinAlpha, kLinBeta);
+      zz = fminf(fmaxf(zz, 0.0f), 1.0f);
+      idx = __builtin_amdgcn_ubfe(f32_bits(zz), (uint32_t)qa.sh, (uint32_t)(24 - qa.sh));
+    } else {
+      uint32_t u = f32_bits(y);
+      uint32_t a = min(max(u & 0x7fffffffu, qa.lo), qa.hi);
+      idx = ((a - qa.lo) >> qa.sh) + ((u >> 31) ? (uint32_t)qa.nj : 0u);
+    }
+    typename Entry<M>::type e = lut[idx];
+    uint32_t q = e.x + (y >= bits_f32(e.y) ? 1u : 0u);
+    if constexpr (M >= 2) q += (y >= bits_f32(e.z) ? 1u : 0u);
+    if constexpr (M >= 3) q += (y >= bits_f32(e.w) ? 1u : 0u);
+    return q;
+  }
+}
+
+// Copies the thresholds into LDS and expands the per-bucket bases of the kernel arguments
+// into LDS entries (base, T[base], T[base+1], T[base+2]); special buckets get (z, NaN, ...).
+// Must be called by every thread of the workgroup; ends with a barrier.
+template <int MODE, int M>
+__device__ __forceinline__ void build_lut(const QuantArgs& qa, typename Entry<M>::type* s_lut, float* s_thr,
+                                          int tid, int nthreads) {
+  using E = typename Entry<M>::type;
+  for (int i = tid; i < 260; i += nthreads) s_thr[i] = qa.thr[i];
+  __syncthreads();
+  if constexpr (MODE != SEARCH) {
+    for (int i = tid; i < qa.nbuckets; i += nthreads) {
+      uint32_t b = qa.base[i];
+      bool sp = (i == qa.special0) || (i == qa.special1);
+      const uint32_t nan = 0x7fc00000u;
+      E e;
+      e.x = sp ? (uint32_t)qa.z : b;
+      e.y = sp ? nan : f32_bits(s_thr[b]);
+      if constexpr (M >= 2) {
+        e.z = sp ? nan : f32_bits(s_thr[b + 1]);
+        e.w = sp ? nan : f32_bits(s_thr[b + 2]);
+      }
+      s_lut[i] = e;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace bq

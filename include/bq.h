@@ -1,0 +1,160 @@
+/*
+ * bq.h -- blockwise absmax quantization and dequantization for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libbq.so.  Every entry point validates its arguments on the host, then enqueues
+ * its kernels on the caller's HIP stream and returns without waiting.  The library never
+ * allocates or frees device memory, never copies between host and device, and never
+ * synchronizes, so every call can be captured in a HIP graph.
+ *
+ * Conventions shared by all entry points
+ *   - Device pointers (marked [device]) must be device memory of the current device, and
+ *     data arrays must be 16-byte aligned (fp32 statistic arrays: 4-byte aligned).  The
+ *     caller owns every buffer and keeps it alive until the enqueued work completes.
+ *   - Host pointers (marked [host]) are read during the call only.
+ *   - `stream` is the HIP stream to enqueue on; 0 is the legacy null stream.  This follows
+ *     "Respect the current CUDA stream in blockwise quantization" (bitsandbytes PR 2052),
+ *     Summary: quantization must run on the caller's current stream, not stream 0.
+ *   - Errors: every check happens before any HIP call; on error nothing is enqueued and no
+ *     output is written.  A failed launch returns BQ_ERR_HIP.  n == 0 is valid and enqueues
+ *     nothing.  Element data is never inspected on the host (that would need a sync).
+ *   - Determinism: outputs are bit-identical across runs, streams and devices of this kind.
+ *
+ * The arithmetic (each rule is also written where it is implemented):
+ *   blocks      element i belongs to block i / B of the flattened 1-D array; the last
+ *               block may be partial ("full blocks, and tails", PR 2052, "Correctness and
+ *               safety"); B is a power of two from 32 to 4096 (PR 2052, Summary).
+ *   absmax      a_b = max |x_i| over the finite elements of block b; +0 if there are none.
+ *   normalize   y_i = fl32(fl32(x_i * s) * fl32(1 / fl32(a_b * s))), s = 2^64 if
+ *               a_b < 2^-64, s = 2^-64 if a_b > 2^64, else 1 (|y_i| <= 1).
+ *   nearest     q_i = the smallest index k minimizing |y_i - c_k| exactly (equal distances
+ *               resolve to the lowest index, as in "[OMNIML-5899] Add CUDA kernels for IQ
+ *               packing", review item "Search equivalence").  Non-finite x_i and every
+ *               element of a block with a_b = 0 take z = the nearest code to 0.0.
+ *   packing     16-entry table: two codes per byte, the first element of each pair in the
+ *               high nibble, ceil(n/2) bytes, a zero pad nibble for odd n (33 values fill
+ *               17 bytes, as in onnxruntime/mobius PR 794, finding F3).  256-entry table:
+ *               one byte per element.
+ *   dequantize  out_i = RN(fl32(c[q_i] * a_b)): one binary32 multiply, then one
+ *               round-to-nearest-even to the output type (overflow to infinity, signed zeros
+ *               and subnormals kept, NaN to a quiet NaN of the same sign).
+ */
+#ifndef BQ_H
+#define BQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of the unquantized side. */
+typedef enum { BQ_F32 = 0, BQ_F16 = 1, BQ_BF16 = 2 } bq_dtype;
+
+typedef enum {
+  BQ_OK = 0,
+  BQ_ERR_NULL = 1,      /* a required pointer is NULL */
+  BQ_ERR_DTYPE = 2,     /* dtype is not a bq_dtype */
+  BQ_ERR_SIZE = 3,      /* n < 0, more than INT32_MAX blocks, or n not a whole number of rows */
+  BQ_ERR_BLOCKSIZE = 4, /* blocksize not a power of two in [32, 4096] */
+  BQ_ERR_TABLE = 5,     /* code table: size, order, range or spacing (see bq_code_table) */
+  BQ_ERR_ALIGNMENT = 6, /* a device pointer is not aligned as required */
+  BQ_ERR_FORMAT = 7,    /* unknown bq_q32_format, or row_len not a multiple of 32 */
+  BQ_ERR_WORKSPACE = 8, /* nested workspace missing or smaller than bq_nested_workspace_bytes */
+  BQ_ERR_HIP = 9        /* the HIP runtime rejected a launch */
+} bq_status;
+
+/* A code table in host memory: `size` (16 or 256) binary32 entries, strictly ascending,
+ * each finite and within [-1, 1], every nonzero entry of magnitude >= 2^-20 (so that sums
+ * of two entries are exact in binary64); -0.0 is read as +0.0.  16 entries select 4-bit
+ * codes (packed two per byte), 256 entries 8-bit codes.  The table is read during the call
+ * and passed to the kernels by value; nothing is uploaded. */
+typedef struct {
+  const float* entries; /* [host] */
+  int32_t size;
+} bq_code_table;
+
+/* Blockwise quantization (General8 / FP4 / NF4 family of "Respect the current CUDA stream
+ * in blockwise quantization", bitsandbytes PR 2052, Summary and "Correctness and safety").
+ *   in         [device] n elements of `dtype`, read only.
+ *   absmax     [device] out: ceil(n / blocksize) binary32 block maxima.
+ *   packed     [device] out: ceil(n / 2) bytes (16-entry table) or n bytes (256 entries). */
+bq_status bq_quantize_blockwise(const void* in, bq_dtype dtype, int64_t n, int32_t blocksize,
+                                const bq_code_table* code_table, float* absmax, uint8_t* packed,
+                                hipStream_t stream);
+
+/* Blockwise dequantization, the inverse of bq_quantize_blockwise: one binary32 multiply of
+ * the code's table entry by the block absmax, rounded once to `dtype`.
+ *   out        [device] out: n elements of `dtype`.
+ *   absmax     [device] ceil(n / blocksize) binary32 values (any values; NaN propagates).
+ *   packed     [device] codes laid out as bq_quantize_blockwise writes them. */
+bq_status bq_dequantize_blockwise(void* out, bq_dtype dtype, int64_t n, int32_t blocksize,
+                                  const bq_code_table* code_table, const float* absmax,
+                                  const uint8_t* packed, hipStream_t stream);
+
+/* Second-level statistics of nested quantization (nested General8 and compressed-statistics
+ * NF4 of PR 2052, "Reproduced failure").  The block absmax values a_b are replaced by:
+ *   mean     = RN32(S / nb), S the binary64 pairwise sum of a_0 .. a_{nb-1} zero-padded to a
+ *              power-of-two length (sum of a range = sum of its left half + sum of its right);
+ *   d_b      = fl32(a_b - mean), quantized with the 256-entry `table` in groups of
+ *              `blocksize2` blocks by the same absmax / normalize / nearest rules;
+ *   rebuilt  a'_b = fl32(fl32(c2[q2_b] * absmax2_g) + mean), used by the nested dequantize. */
+typedef struct {
+  uint8_t* qabsmax;            /* [device] nb codes q2_b (nb = ceil(n / blocksize)) */
+  float* absmax2;              /* [device] ceil(nb / blocksize2) binary32 group maxima */
+  float* mean;                 /* [device] 1 binary32 value */
+  const bq_code_table* table;  /* [host] 256-entry statistics table */
+  int32_t blocksize2;          /* blocks per statistics group: power of two in [32, 4096] */
+  void* workspace;             /* [device] scratch, 256-byte aligned; quantize only */
+  size_t workspace_bytes;
+} bq_nested_stats;
+
+/* Bytes of device workspace bq_quantize_nested needs (0 for n <= 0).  After the call's
+ * stream work completes, the first ceil(n / blocksize) * 4 bytes of the workspace hold the
+ * binary32 block maxima a_b. */
+size_t bq_nested_workspace_bytes(int64_t n, int32_t blocksize, int32_t blocksize2);
+
+/* Blockwise quantization with nested statistics: packed data codes as bq_quantize_blockwise,
+ * and the statistics of bq_nested_stats written to stats->qabsmax, ->absmax2 and ->mean.
+ * Enqueues four kernels (data, partial sums, mean, statistics) on `stream`. */
+bq_status bq_quantize_nested(const void* in, bq_dtype dtype, int64_t n, int32_t blocksize,
+                             const bq_code_table* code_table, bq_nested_stats* stats,
+                             uint8_t* packed, hipStream_t stream);
+
+/* Dequantization from nested statistics: rebuilds each a'_b from (q2_b, absmax2_g, mean) and
+ * dequantizes with it, in one kernel.  stats->workspace is not used. */
+bq_status bq_dequantize_nested(void* out, bq_dtype dtype, int64_t n, int32_t blocksize,
+                               const bq_code_table* code_table, const bq_nested_stats* stats,
+                               const uint8_t* packed, hipStream_t stream);
+
+/* GGUF-style 32-element blocks (the Q4_0 / Q8_0 shapes of "Cache device-side constants in
+ * dequant kernels", ComfyUI-GGUF PR 472, "Verification" table):
+ *   BQ_Q32_Q4: 18 bytes = binary16 scale d (little-endian) + 16 bytes; element j < 16 is the
+ *              low nibble of byte j, element 16 + j its high nibble (the low-before-high
+ *              nibble order of that page's "Problem" section); value (q - 8) * d.
+ *   BQ_Q32_Q8: 34 bytes = binary16 d + 32 int8; value q * d.
+ * The binary32 product is exact; it is rounded once to `dtype`. */
+typedef enum { BQ_Q32_Q4 = 0, BQ_Q32_Q8 = 1 } bq_q32_format;
+
+/* Dequantizes n / 32 consecutive blocks (row-major rows of row_len elements; row_len a
+ * multiple of 32 dividing n, so no block straddles a row: the per-row alignment check of
+ * "[OMNIML-5899] Add CUDA kernels for IQ packing").
+ *   blocks  [device] (n / 32) * 18 or * 34 bytes, 16-byte aligned.
+ *   out     [device] out: n elements of `dtype`. */
+bq_status bq_dequant_q32(const void* blocks, bq_dtype dtype, int64_t n, int32_t row_len,
+                         bq_q32_format format, void* out, hipStream_t stream);
+
+/* The hipError_t (as int) of the most recent launch that failed on the calling thread with
+ * BQ_ERR_HIP, or 0 if none has. */
+int bq_last_hip_error(void);
+
+/* Static description of a status code (never NULL). */
+const char* bq_status_string(bq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BQ_H */

@@ -1,0 +1,220 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports what include/*.h declares,
+rejects every invalid argument with the documented status before any HIP call, and its host
+table preparation (thresholds + bucket LUT) reproduces the oracle's nearest code."""
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+import dequantization_block_absmax_amd as bq
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20  # an aligned non-null address; never dereferenced by a rejected call
+T16 = synth.table16()
+T256 = synth.table256()
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names.update(re.findall(r"\b(bq_\w+)\s*\(", src))
+    return sorted(names)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("bq_quantize_blockwise", "bq_dequantize_blockwise", "bq_quantize_nested",
+                     "bq_dequant_q32", "bq_dequantize_nested"):
+        assert required in names
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_library_exports_declared_symbol(name):
+    lib = ctypes.CDLL(bq.LIB_PATH)
+    assert hasattr(lib, name)
+    assert name in bq.EXPORTS
+
+
+def test_status_strings():
+    for s in range(10):
+        assert bq.status_string(s)
+    assert bq.status_string(bq.BQ_OK) == "ok"
+
+
+def q(**kw):
+    args = dict(inp=FAKE, dtype=bq.BQ_BF16, n=1000, blocksize=64, table=T16, absmax=FAKE, packed=FAKE,
+                stream=0)
+    args.update(kw)
+    return bq.bq_quantize_blockwise(**args)
+
+
+def dq(**kw):
+    args = dict(out=FAKE, dtype=bq.BQ_BF16, n=1000, blocksize=64, table=T16, absmax=FAKE, packed=FAKE,
+                stream=0)
+    args.update(kw)
+    return bq.bq_dequantize_blockwise(**args)
+
+
+@pytest.mark.parametrize("fn", [q, dq])
+def test_blockwise_validation(fn):
+    assert fn(dtype=7) == bq.BQ_ERR_DTYPE
+    assert fn(n=-1) == bq.BQ_ERR_SIZE
+    for b in (0, 16, 48, 100, 8192, -64):
+        assert fn(blocksize=b) == bq.BQ_ERR_BLOCKSIZE
+    assert fn(table=None) == bq.BQ_ERR_NULL
+    bad_tables = [
+        T16[:15],                                    # size
+        np.concatenate([T16, [1.0]]),                 # size 17
+        T16[::-1],                                    # order
+        np.where(np.arange(16) == 3, T16[2], T16),    # duplicate
+        np.where(np.arange(16) == 5, np.nan, T16),    # non-finite
+        np.where(np.arange(16) == 15, 1.5, T16),      # out of range
+        np.where(np.arange(16) == 9, 1e-7, T16),      # tiny nonzero entry
+        np.float32(np.linspace(-1, 1, 200)),          # size 200
+    ]
+    for t in bad_tables:
+        assert fn(table=np.float32(t)) == bq.BQ_ERR_TABLE
+    assert fn(n=0) == bq.BQ_OK  # nothing enqueued
+    assert fn(n=0, inp=None) == bq.BQ_OK if fn is q else fn(n=0, out=None) == bq.BQ_OK
+    if fn is q:
+        assert fn(inp=None) == bq.BQ_ERR_NULL
+        assert fn(inp=FAKE + 8) == bq.BQ_ERR_ALIGNMENT
+    else:
+        assert fn(out=None) == bq.BQ_ERR_NULL
+        assert fn(out=FAKE + 8) == bq.BQ_ERR_ALIGNMENT
+    assert fn(absmax=None) == bq.BQ_ERR_NULL
+    assert fn(packed=None) == bq.BQ_ERR_NULL
+    assert fn(packed=FAKE + 4) == bq.BQ_ERR_ALIGNMENT
+    assert fn(absmax=FAKE + 2) == bq.BQ_ERR_ALIGNMENT
+    assert fn(n=(2**31) * 32, blocksize=32) == bq.BQ_ERR_SIZE  # more than INT32_MAX blocks
+
+
+def test_negative_zero_table_entry_is_accepted():
+    t = T16.copy()
+    t[t == 0] = -0.0
+    assert q(n=0, table=t) == bq.BQ_OK
+
+
+def nstats(**kw):
+    args = dict(qabsmax=FAKE, absmax2=FAKE, mean=FAKE, table=T256, blocksize2=256, workspace=FAKE,
+                workspace_bytes=bq.bq_nested_workspace_bytes(1000, 64, 256))
+    args.update(kw)
+    return bq.nested_stats(**args)
+
+
+def test_nested_validation():
+    def call(stats=None, **kw):
+        args = dict(inp=FAKE, dtype=bq.BQ_BF16, n=1000, blocksize=64, table=T16,
+                    stats=nstats() if stats is None else stats, packed=FAKE, stream=0)
+        args.update(kw)
+        return bq.bq_quantize_nested(**args)
+
+    assert call(dtype=9) == bq.BQ_ERR_DTYPE
+    assert call(blocksize=65) == bq.BQ_ERR_BLOCKSIZE
+    assert bq.bq_quantize_nested(FAKE, bq.BQ_BF16, 1000, 64, T16, None, FAKE, 0) == bq.BQ_ERR_NULL
+    assert call(stats=nstats(blocksize2=100)) == bq.BQ_ERR_BLOCKSIZE
+    assert call(stats=nstats(table=T16)) == bq.BQ_ERR_TABLE  # statistics need 256 entries
+    assert call(stats=nstats(table=None)) == bq.BQ_ERR_NULL
+    assert call(stats=nstats(qabsmax=None)) == bq.BQ_ERR_NULL
+    assert call(stats=nstats(absmax2=None)) == bq.BQ_ERR_NULL
+    assert call(stats=nstats(mean=None)) == bq.BQ_ERR_NULL
+    assert call(stats=nstats(workspace=None)) == bq.BQ_ERR_WORKSPACE
+    assert call(stats=nstats(workspace_bytes=10)) == bq.BQ_ERR_WORKSPACE
+    assert call(stats=nstats(workspace=FAKE + 16)) == bq.BQ_ERR_ALIGNMENT
+    assert call(stats=nstats(mean=FAKE + 1)) == bq.BQ_ERR_ALIGNMENT
+    assert call(inp=None) == bq.BQ_ERR_NULL
+    assert call(n=0) == bq.BQ_OK
+    # the nested dequantize needs no workspace but checks the rest
+    st = nstats(workspace=None, workspace_bytes=0)
+    assert bq.bq_dequantize_nested(FAKE, bq.BQ_BF16, 0, 64, T16, st, FAKE, 0) == bq.BQ_OK
+    assert bq.bq_dequantize_nested(FAKE, bq.BQ_BF16, 1000, 64, T16, nstats(absmax2=None), FAKE, 0) == bq.BQ_ERR_NULL
+    assert bq.bq_dequantize_nested(None, bq.BQ_BF16, 1000, 64, T16, st, FAKE, 0) == bq.BQ_ERR_NULL
+
+
+def test_workspace_bytes():
+    assert bq.bq_nested_workspace_bytes(0, 64, 256) == 0
+    nb = -(-(2**29) // 64)
+    ws = bq.bq_nested_workspace_bytes(2**29, 64, 256)
+    assert ws >= nb * 4 + (-(-nb // 256)) * 8
+    assert ws < nb * 4 + (-(-nb // 256)) * 8 + 512
+
+
+def test_q32_validation():
+    def call(**kw):
+        args = dict(blocks=FAKE, dtype=bq.BQ_BF16, n=4096 * 64, row_len=4096, fmt=bq.BQ_Q32_Q4, out=FAKE,
+                    stream=0)
+        args.update(kw)
+        return bq.bq_dequant_q32(**args)
+
+    assert call(dtype=3) == bq.BQ_ERR_DTYPE
+    assert call(fmt=2) == bq.BQ_ERR_FORMAT
+    assert call(row_len=48) == bq.BQ_ERR_FORMAT
+    assert call(row_len=0) == bq.BQ_ERR_FORMAT
+    assert call(n=4096 * 64 + 32) == bq.BQ_ERR_SIZE
+    assert call(n=-4096) == bq.BQ_ERR_SIZE
+    assert call(n=0) == bq.BQ_OK
+    assert call(blocks=None) == bq.BQ_ERR_NULL
+    assert call(out=None) == bq.BQ_ERR_NULL
+    assert call(blocks=FAKE + 2) == bq.BQ_ERR_ALIGNMENT
+
+
+# ---- host table preparation vs the oracle ------------------------------------------------
+
+def _search_probes(table, rng):
+    t = np.asarray(table, np.float64)
+    mids = ((t[:-1] + t[1:]) / 2).astype(np.float32)
+    near = [mids]
+    for k in range(1, 4):
+        near.append(np.nextafter(near[-1], np.float32(-2)))
+    up = [mids]
+    for k in range(1, 4):
+        up.append(np.nextafter(up[-1], np.float32(2)))
+    entries = np.float32(table)
+    rand = rng.uniform(-1, 1, 20000).astype(np.float32)
+    logs = (rng.choice([-1, 1], 5000) * 2.0 ** rng.uniform(-30, 0, 5000)).astype(np.float32)
+    special = np.float32([0.0, -0.0, 1.0, -1.0, 2.0**-149, -2.0**-149, 2.0**-126, 1 - 2.0**-24,
+                          -(1 - 2.0**-24), np.nan, np.inf, -np.inf])
+    return np.concatenate(near + up + [entries, rand, logs, special])
+
+
+def _oracle_codes(o, y, table):
+    return np.array([o.zero_code(table) if not np.isfinite(v) else o.nearest(v, table) for v in y], np.int32)
+
+
+TABLES = {
+    "table16": T16,
+    "table256": T256,
+    "hand16": np.float32([-1, -0.875, -0.75, -0.625, -0.5, -0.375, -0.25, -0.125, 0, 0.125, 0.25, 0.375, 0.5,
+                          0.625, 0.75, 1]),
+    "dyadic256": synth.dyadic_table(256),
+    "nf4_like": np.float32(np.sort(np.concatenate([[-1, 0, 1], np.linspace(-0.7, 0.72, 13)]))),
+    "tiny_entries": np.float32(np.sort(np.concatenate([[-1, 0, 1, 2.0**-20, -2.0**-20, 2.0**-19],
+                                                       np.linspace(0.1, 0.9, 10)]))),
+    # 200 entries packed into [0.5, 0.5 + 2e-4]: no bucketing keeps <= 3 compares -> search
+    "clustered256": np.float32(np.sort(np.concatenate([np.linspace(-1, 0.45, 56),
+                                                       0.5 + np.arange(200) * 2.0**-23 * 8]))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(TABLES))
+def test_host_search_matches_oracle(name):
+    table = TABLES[name]
+    assert len(np.unique(table)) == len(table) in (16, 256)
+    o = oracle.Oracle()
+    y = _search_probes(table, np.random.default_rng(len(name)))
+    st, codes, mode, cmp = bq.bq_debug_nearest_codes(table, y)
+    assert st == bq.BQ_OK
+    expect = _oracle_codes(o, y, table)
+    bad = np.nonzero(codes != expect)[0]
+    assert bad.size == 0, (name, mode, [(float(y[i]), codes[i], expect[i]) for i in bad[:5]])
+    if name == "clustered256":
+        assert mode == 2
+    if name in ("table16", "hand16"):
+        assert mode == 0 and cmp == 1
