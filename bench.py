@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Benchmark of blockwise absmax quantization / dequantization on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+  1. bq_quantize_nested    bf16, n = 2^29 (1 GiB), 4-bit codes, B = 64, nested statistics
+                           (256-entry table, groups of 256 blocks)
+  2. bq_dequantize_nested  the same tensor back to bf16
+  3. bq_dequant_q32        4096 x 14336 GGUF-style 4-bit blocks (18 B) to bf16
+  4. bq_dequant_q32        4096 x 14336 GGUF-style 8-bit blocks (34 B) to bf16
+Inputs are generated on the device before timing (they are resident in HBM when the timed
+region starts).  `value` is input bytes of the step / step time (the metric's "effective
+GB/s (input bytes)"); every call's algorithmic read+write bytes against the 8 TB/s HBM peak
+is in `detail`.  `roofline` is the slower of the two 1 GiB kernels (data quantize, nested
+dequantize), timed with HIP events on the stream it runs on; `cpu_baseline` is the CPU
+oracle on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-detail] [--no-cpu-baseline]
+    python bench.py --profile     (a few launches of each kernel plus a 1 GiB copy, for rocprofv3)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective GB/s (input bytes) and % of HBM peak, quantize + dequantize"
+PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+KERNEL_SOURCES = {
+    "quantize_kernel": "dequantization_block_absmax_amd/csrc/k_quant.hip",
+    "dequantize_nested_kernel": "dequantization_block_absmax_amd/csrc/k_dequant.hip",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse_args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-detail", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--profile", action="store_true")
+    return p.parse_args()
+
+
+class Workload:
+    """C5 (1 GiB bf16, nested 4-bit) and C4 (GGUF 4096 x 14336) buffers, resident on the device."""
+
+    N5, B5, B2 = 1 << 29, 64, 256
+    ROWS, COLS = 4096, 14336
+
+    def __init__(self, bq, synth, torch, dev):
+        self.bq, self.torch = bq, torch
+        self.t16, self.t256 = synth.table16(), synth.table256()
+        n, B, B2 = self.N5, self.B5, self.B2
+        self.nb = bq.num_blocks(n, B)
+        self.ng = bq.num_blocks(self.nb, B2)
+        self.x = synth.blockwise_input(n, "bfloat16", 5, std=0.02, device=dev)
+        self.packed = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+        self.ws_bytes = bq.bq_nested_workspace_bytes(n, B, B2)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.q2 = torch.empty(self.nb, dtype=torch.uint8, device=dev)
+        self.absmax2 = torch.empty(self.ng, dtype=torch.float32, device=dev)
+        self.mean = torch.empty(1, dtype=torch.float32, device=dev)
+        self.out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        self.stats = bq.nested_stats(self.q2, self.absmax2, self.mean, self.t256, B2, self.ws, self.ws_bytes)
+        self.absmax = self.ws[: self.nb * 4].view(torch.float32)
+        self.n4 = self.ROWS * self.COLS
+        self.q4 = synth.q32_blocks(self.n4 // 32, "q4", seed=4, device=dev)
+        self.q8 = synth.q32_blocks(self.n4 // 32, "q8", seed=4, device=dev)
+        self.out4 = torch.empty(self.n4, dtype=torch.bfloat16, device=dev)
+        e = 2 ** 29
+        # input bytes and algorithmic read+write bytes of each call
+        self.calls = {
+            "quantize_nested": dict(inp=2 * e, rw=2 * e + e // 2 + self.nb + 4 * self.ng + 4),
+            "dequantize_nested": dict(inp=e // 2 + self.nb + 4 * self.ng + 4, rw=2 * e + e // 2 + self.nb + 4 * self.ng + 4),
+            "dequant_q32_q4": dict(inp=self.n4 // 32 * 18, rw=self.n4 // 32 * 18 + 2 * self.n4),
+            "dequant_q32_q8": dict(inp=self.n4 // 32 * 34, rw=self.n4 // 32 * 34 + 2 * self.n4),
+        }
+
+    def run(self, name):
+        bq = self.bq
+        if name == "quantize_nested":
+            st = bq.bq_quantize_nested(self.x, bq.BQ_BF16, self.N5, self.B5, self.t16, self.stats, self.packed)
+        elif name == "dequantize_nested":
+            st = bq.bq_dequantize_nested(self.out, bq.BQ_BF16, self.N5, self.B5, self.t16, self.stats, self.packed)
+        elif name == "dequant_q32_q4":
+            st = bq.bq_dequant_q32(self.q4, bq.BQ_BF16, self.n4, self.COLS, bq.BQ_Q32_Q4, self.out4)
+        elif name == "dequant_q32_q8":
+            st = bq.bq_dequant_q32(self.q8, bq.BQ_BF16, self.n4, self.COLS, bq.BQ_Q32_Q8, self.out4)
+        elif name == "quantize_kernel":  # the data kernel of quantize_nested on its own
+            st = bq.bq_quantize_blockwise(self.x, bq.BQ_BF16, self.N5, self.B5, self.t16, self.absmax, self.packed)
+        else:
+            raise KeyError(name)
+        bq.check(st, name)
+
+
+STEP = ["quantize_nested", "dequantize_nested", "dequant_q32_q4", "dequant_q32_q8"]
+
+
+def timed_step_loop(w: Workload, torch, steps: int):
+    """Runs `steps` steps with an event before and after every call; returns the elapsed ms
+    of the whole region and the per-call mean ms."""
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STEP) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        evs[s][0].record()
+        for i, name in enumerate(STEP):
+            w.run(name)
+            evs[s][i + 1].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    total = evs[0][0].elapsed_time(evs[-1][-1])
+    per = {name: sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)) / steps
+           for i, name in enumerate(STEP)}
+    return total, per, wall_ms
+
+
+def time_calls(fn, torch, reps: int) -> float:
+    """Mean ms of fn() over reps back-to-back calls, HIP events on the current stream."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def source_digest(path: str) -> str:
+    h = hashlib.sha256()
+    for p in sorted([os.path.join(ROOT, path), os.path.join(ROOT, "dequantization_block_absmax_amd/csrc/bq_device.h"),
+                     os.path.join(ROOT, "dequantization_block_absmax_amd/csrc/bq_internal.h")]):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % kernel)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != source_digest(KERNEL_SOURCES[kernel]):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def detail_configs(bq, synth, torch, dev, peak):
+    """C1, C2 (every block size), C3 and C4/C5 calls on their own, with buffer sets rotated
+    so that each call's data is not resident in the 256 MB last-level cache."""
+    out = {}
+    t16, t256 = synth.table16(), synth.table256()
+
+    def rotate(make, footprint, fn, reps):
+        k = max(1, min(64, -(-(1 << 30) // footprint)))
+        sets = [make() for _ in range(k)]
+        i = [0]
+
+        def call():
+            fn(sets[i[0] % k])
+            i[0] += 1
+        return time_calls(call, torch, reps)
+
+    def rec(name, ms, inp, rw):
+        out[name] = dict(us=round(ms * 1e3, 2), input_gbs=round(inp / ms / 1e6, 1), rw_gbs=round(rw / ms / 1e6, 1),
+                         pct_hbm_peak=round(100 * rw / ms / 1e6 / peak, 1))
+
+    def blockwise(tag, n, dtype, B, table, seed, std, p_out=0.0, p_nf=0.0, reps=50):
+        es = {"float32": 4, "float16": 2, "bfloat16": 2}[dtype]
+        tdt = {"float32": torch.float32, "float16": torch.float16, "bfloat16": torch.bfloat16}[dtype]
+        code = {"float32": bq.BQ_F32, "float16": bq.BQ_F16, "bfloat16": bq.BQ_BF16}[dtype]
+        x0 = synth.blockwise_input(n, dtype, seed, std=std, p_out=p_out, p_nf=p_nf, device=dev)
+        K = len(table)
+        nb = bq.num_blocks(n, B)
+        pb = bq.packed_bytes(n, K)
+
+        def make():
+            return dict(x=x0.clone(), a=torch.empty(nb, dtype=torch.float32, device=dev),
+                        p=torch.empty(pb + 16, dtype=torch.uint8, device=dev), o=torch.empty(n, dtype=tdt, device=dev))
+        foot = n * es * 2 + pb + nb * 4
+        qms = rotate(make, foot, lambda s: bq.check(bq.bq_quantize_blockwise(s["x"], code, n, B, table, s["a"], s["p"])), reps)
+        sets_once = make()
+        bq.check(bq.bq_quantize_blockwise(sets_once["x"], code, n, B, table, sets_once["a"], sets_once["p"]))
+        dms = rotate(lambda: dict(a=sets_once["a"].clone(), p=sets_once["p"].clone(), o=torch.empty(n, dtype=tdt, device=dev)),
+                     foot, lambda s: bq.check(bq.bq_dequantize_blockwise(s["o"], code, n, B, table, s["a"], s["p"])), reps)
+        rw = n * es + pb + nb * 4
+        rec(tag + " quantize", qms, n * es, rw)
+        rec(tag + " dequantize", dms, pb + nb * 4, rw)
+
+    blockwise("C1 fp32 n=524288 B=64", 524288, "float32", 64, t16, 1, 1.0, reps=200)
+    for B in (32, 64, 128, 256, 512, 1024, 2048, 4096):
+        blockwise("C2 fp16 n=8388609 B=%d" % B, 8388609, "float16", B, t16, 2, 1.0, 1e-3, 1e-4, reps=100)
+    blockwise("C3 bf16 n=2^26 8-bit B=4096", 1 << 26, "bfloat16", 4096, t256, 3, 0.02, reps=50)
+    return out
+
+
+def cpu_baseline(w: Workload, torch):
+    """The CPU oracle (single-threaded, as it stands) on a bounded sample of the step."""
+    import numpy as np
+
+    import oracle
+    o = oracle.Oracle()
+    n5 = 1 << 25
+    rows = 256
+    xs = w.x[:n5].cpu().view(torch.int16).numpy().view(np.uint16)
+    m4 = rows * w.COLS
+    b4 = w.q4[: m4 // 32 * 18].cpu().numpy()
+    b8 = w.q8[: m4 // 32 * 34].cpu().numpy()
+    t0 = time.perf_counter()
+    r = o.quantize_nested(xs, oracle.BF16, w.B5, w.t16, w.t256, w.B2)
+    o.dequantize_nested(r["packed"], r["q2"], r["absmax2"], r["mean"], n5, oracle.BF16, w.B5, w.t16, w.t256, w.B2)
+    o.dequant_q32(b4, m4, w.COLS, oracle.Q4, oracle.BF16)
+    o.dequant_q32(b8, m4, w.COLS, oracle.Q8, oracle.BF16)
+    dt = time.perf_counter() - t0
+    nb = n5 // w.B5
+    inp = 2 * n5 + (n5 // 2 + nb + 4 * (-(-nb // w.B2)) + 4) + b4.size + b8.size
+    return dict(value=round(inp / dt / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample="first 2^25 elements of the 2^29 bf16 tensor (nested quantize + dequantize) and the first "
+                       "256 of 4096 rows of both GGUF matrices; %.1f s single-threaded" % dt)
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the method needs no cross-GPU communication and this build "
+              "targets a single MI355X; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import dequantization_block_absmax_amd as bq
+    import synth
+
+    dev = torch.device("cuda:0")
+    log("generating inputs on", torch.cuda.get_device_name(0))
+    w = Workload(bq, synth, torch, dev)
+    torch.cuda.synchronize()
+
+    if args.profile:
+        for name in STEP + ["quantize_kernel"]:
+            for _ in range(3):
+                w.run(name)
+        src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)  # a plain 1 GiB copy for counter calibration
+        torch.cuda.synchronize()
+        log("profile pass done")
+        return
+
+    for _ in range(args.warmup):
+        for name in STEP:
+            w.run(name)
+    total_ms, per, wall_ms = timed_step_loop(w, torch, args.steps)
+    ms_per_step = total_ms / args.steps
+    step_input = sum(w.calls[c]["inp"] for c in STEP)
+    value = step_input / (ms_per_step / 1e3) / 1e9
+    log("step %.3f ms (wall %.3f ms/step)" % (ms_per_step, wall_ms / args.steps))
+
+    detail = {}
+    for name in STEP:
+        ms = per[name]
+        c = w.calls[name]
+        detail[name] = dict(us=round(ms * 1e3, 2), input_gbs=round(c["inp"] / ms / 1e6, 1),
+                            rw_gbs=round(c["rw"] / ms / 1e6, 1), pct_hbm_peak=round(100 * c["rw"] / ms / 1e6 / PEAK_GBS, 1))
+
+    # Roofline of the dominant kernel: the slower of the data quantize kernel (timed on its own,
+    # same launch as inside quantize_nested) and the nested dequantize kernel (one launch per call).
+    qk_ms = time_calls(lambda: w.run("quantize_kernel"), torch, max(args.steps, 10))
+    n = w.N5
+    q_bytes = 2 * n + n // 2 + 4 * w.nb
+    dq_bytes = w.calls["dequantize_nested"]["rw"]
+    detail["quantize_kernel"] = dict(us=round(qk_ms * 1e3, 2), rw_gbs=round(q_bytes / qk_ms / 1e6, 1),
+                                     pct_hbm_peak=round(100 * q_bytes / qk_ms / 1e6 / PEAK_GBS, 1))
+    if qk_ms >= per["dequantize_nested"]:
+        kname, kbytes, kms = "quantize_kernel", q_bytes, qk_ms
+    else:
+        kname, kbytes, kms = "dequantize_nested_kernel", dq_bytes, per["dequantize_nested"]
+    achieved = kbytes / kms / 1e6
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_GBS, 4), traffic=traffic_for(kname), kernel=kname,
+                    bytes_per_launch=kbytes, us_per_launch=round(kms * 1e3, 2))
+
+    if not args.no_detail:
+        log("timing the individual workloads")
+        detail.update(detail_configs(bq, synth, torch, dev, PEAK_GBS))
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        cpu = cpu_baseline(w, torch)
+
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "bf16 2^29 (1 GiB) 4-bit blockwise B=64 nested-statistics quantize + dequantize, "
+                               "plus GGUF-style 4096x14336 Q4 and Q8 block dequant to bf16",
+                   "n": w.N5, "blocksize": w.B5, "blocksize2": w.B2, "gguf_shape": [w.ROWS, w.COLS],
+                   "step_input_bytes": step_input},
+        "roofline": roofline, "cpu_baseline": cpu, "detail": detail,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

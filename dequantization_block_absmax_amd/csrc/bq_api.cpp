@@ -10,7 +10,9 @@
 #include <hip/hip_runtime_api.h>
 #include <string.h>
 
-#include "../../include/bq.h"
+#include <mutex>
+
+#include "bq.h"
 #include "bq_internal.h"
 
 namespace {
@@ -35,14 +37,64 @@ bq_status hip_status(int e) {
 
 int64_t nblocks(int64_t n, int32_t b) { return (n + b - 1) / b; }
 
-// Offsets inside the nested workspace: binary32 absmax[nb], then binary64 partial sums.
+// Nested workspace: binary32 absmax[nb], then one binary64 partial sum per quantize
+// workgroup (at most one per 8192-element tile).
 size_t ws_partials_offset(int64_t nb) { return ((size_t)nb * 4 + 255) & ~(size_t)255; }
 
-size_t ws_bytes(int64_t nb) { return ws_partials_offset(nb) + (size_t)((nb + 255) / 256) * 8; }
+size_t ws_bytes(int64_t n, int64_t nb) {
+  return ws_partials_offset(nb) + (size_t)((n + bq::kQuantTileElems - 1) / bq::kQuantTileElems) * 8;
+}
+
+// log2 of the 8192-element tiles each quantize workgroup processes: two tiles amortize the
+// LUT prologue once there are enough tiles to fill the GPU several times over (measured
+// best on MI355X for the 2^26 and 2^29 element workloads).
+int quantize_log2tiles(int64_t n) { return (n + bq::kQuantTileElems - 1) / bq::kQuantTileElems >= 4096 ? 1 : 0; }
+
+// Preparing a table (validation, thresholds, bucket LUT) costs more host time than a small
+// launch, so the last few prepared tables are kept, keyed by their entries.  This is a
+// host-side memo only: results never depend on it.
+struct TableCache {
+  static constexpr int kSlots = 8;
+  struct Slot {
+    int size = 0;
+    float entries[256];
+    bq::PreparedTable table;
+  };
+  std::mutex mu;
+  Slot slots[kSlots];
+  int next = 0;
+
+  bool lookup(const float* e, int size, bq::PreparedTable* out) {
+    std::lock_guard<std::mutex> g(mu);
+    for (Slot& s : slots)
+      if (s.size == size && memcmp(s.entries, e, sizeof(float) * size) == 0) {
+        memcpy(out, &s.table, sizeof(*out));
+        return true;
+      }
+    return false;
+  }
+  void insert(const float* e, int size, const bq::PreparedTable& t) {
+    std::lock_guard<std::mutex> g(mu);
+    Slot& s = slots[next];
+    next = (next + 1) % kSlots;
+    s.size = size;
+    memcpy(s.entries, e, sizeof(float) * size);
+    memcpy(&s.table, &t, sizeof(t));
+  }
+};
+
+TableCache& table_cache() {
+  static TableCache* c = new TableCache();  // never destroyed: usable during process exit
+  return *c;
+}
 
 bq_status check_table(const bq_code_table* t, bq::PreparedTable* out) {
   if (t == nullptr || t->entries == nullptr) return BQ_ERR_NULL;
-  return bq::prepare_table(t->entries, t->size, out) ? BQ_OK : BQ_ERR_TABLE;
+  if (t->size != 16 && t->size != 256) return BQ_ERR_TABLE;
+  if (table_cache().lookup(t->entries, t->size, out)) return BQ_OK;
+  if (!bq::prepare_table(t->entries, t->size, out)) return BQ_ERR_TABLE;
+  table_cache().insert(t->entries, t->size, *out);
+  return BQ_OK;
 }
 
 // Scratch for prepared tables: prepared per call on the host, never shared between calls.
@@ -85,7 +137,8 @@ bq_status bq_quantize_blockwise(const void* in, bq_dtype dtype, int64_t n, int32
   if (in == nullptr || absmax == nullptr || packed == nullptr) return BQ_ERR_NULL;
   if (nblocks(n, blocksize) > INT32_MAX) return BQ_ERR_SIZE;
   if (!aligned(in, 16) || !aligned(packed, 16) || !aligned(absmax, 4)) return BQ_ERR_ALIGNMENT;
-  return hip_status(bq::launch_quantize(in, dtype, n, blocksize, t.data, absmax, packed, stream));
+  return hip_status(bq::launch_quantize(in, dtype, n, blocksize, t.data, absmax, packed, nullptr,
+                                        quantize_log2tiles(n), stream));
 }
 
 bq_status bq_dequantize_blockwise(void* out, bq_dtype dtype, int64_t n, int32_t blocksize,
@@ -111,7 +164,7 @@ bq_status bq_dequantize_blockwise(void* out, bq_dtype dtype, int64_t n, int32_t 
 size_t bq_nested_workspace_bytes(int64_t n, int32_t blocksize, int32_t blocksize2) {
   (void)blocksize2;
   if (n <= 0 || !valid_blocksize(blocksize)) return 0;
-  return ws_bytes(nblocks(n, blocksize));
+  return ws_bytes(n, nblocks(n, blocksize));
 }
 
 static bq_status check_nested(const bq_nested_stats* stats, bq::PreparedTable* t2, bool need_ws,
@@ -127,7 +180,7 @@ static bq_status check_nested(const bq_nested_stats* stats, bq::PreparedTable* t
   if (need_ws) {
     if (stats->workspace == nullptr) return BQ_ERR_WORKSPACE;
     if (!aligned(stats->workspace, 256)) return BQ_ERR_ALIGNMENT;
-    if (stats->workspace_bytes < ws_bytes(nblocks(n, blocksize))) return BQ_ERR_WORKSPACE;
+    if (stats->workspace_bytes < ws_bytes(n, nblocks(n, blocksize))) return BQ_ERR_WORKSPACE;
   }
   return BQ_OK;
 }
@@ -150,10 +203,11 @@ bq_status bq_quantize_nested(const void* in, bq_dtype dtype, int64_t n, int32_t 
   if (!aligned(in, 16) || !aligned(packed, 16)) return BQ_ERR_ALIGNMENT;
   float* ws_absmax = static_cast<float*>(stats->workspace);
   double* ws_partials = reinterpret_cast<double*>(static_cast<uint8_t*>(stats->workspace) + ws_partials_offset(nb));
-  int e = bq::launch_quantize(in, dtype, n, blocksize, t.data, ws_absmax, packed, stream);
+  const int lt = quantize_log2tiles(n);
+  int e = bq::launch_quantize(in, dtype, n, blocksize, t.data, ws_absmax, packed, ws_partials, lt, stream);
   if (e != 0) return hip_status(e);
-  e = bq::launch_nested_stats(ws_absmax, nb, stats->blocksize2, t.stats, ws_partials, stats->qabsmax,
-                              stats->absmax2, stats->mean, stream);
+  e = bq::launch_nested_stats(ws_absmax, nb, stats->blocksize2, t.stats, ws_partials, bq::quantize_grid(n, lt),
+                              stats->qabsmax, stats->absmax2, stats->mean, stream);
   return hip_status(e);
 }
 

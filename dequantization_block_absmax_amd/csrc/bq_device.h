@@ -14,6 +14,12 @@ struct Entry { typedef uint4 type; };
 template <>
 struct Entry<1> { typedef uint2 type; };
 
+// LDS size of the LUT, in entries.
+template <int MODE, int M>
+struct LutLayout {
+  static constexpr int kSize = MODE == LIN ? kLinLutMax : (MODE == LOG ? kLutMax : 1);
+};
+
 // Nearest code of y (see bq_internal.h for the bucket functions).
 template <int MODE, int M>
 __device__ __forceinline__ uint32_t nearest_code(float y, const QuantArgs& qa,
@@ -45,26 +51,49 @@ __device__ __forceinline__ uint32_t nearest_code(float y, const QuantArgs& qa,
 
 // Copies the thresholds into LDS and expands the per-bucket bases of the kernel arguments
 // into LDS entries (base, T[base], T[base+1], T[base+2]); special buckets get (z, NaN, ...).
+// s_lut holds LutLayout<MODE, M>::kSize entries.
 // Must be called by every thread of the workgroup; ends with a barrier.
-template <int MODE, int M>
+template <int MODE, int M, int NT>
 __device__ __forceinline__ void build_lut(const QuantArgs& qa, typename Entry<M>::type* s_lut, float* s_thr,
-                                          int tid, int nthreads) {
+                                          int tid) {
   using E = typename Entry<M>::type;
-  for (int i = tid; i < 260; i += nthreads) s_thr[i] = qa.thr[i];
+  // Every argument word a thread needs is loaded in one batch (fixed trip counts), so the
+  // prologue waits for memory once rather than once per loop iteration.
+  constexpr int kThrIt = (260 + NT - 1) / NT;
+  constexpr int kLutIt = MODE == SEARCH ? 0 : (LutLayout<MODE, M>::kSize + NT - 1) / NT;
+  float th[kThrIt];
+  uint32_t bs[kLutIt > 0 ? kLutIt : 1];
+#pragma unroll
+  for (int k = 0; k < kThrIt; ++k) {
+    const int i = tid + k * NT;
+    th[k] = i < 260 ? qa.thr[i] : 0.0f;
+  }
+#pragma unroll
+  for (int k = 0; k < kLutIt; ++k) {
+    const int i = tid + k * NT;
+    bs[k] = i < qa.nbuckets ? qa.base[i] : 0u;
+  }
+#pragma unroll
+  for (int k = 0; k < kThrIt; ++k)
+    if (tid + k * NT < 260) s_thr[tid + k * NT] = th[k];
   __syncthreads();
   if constexpr (MODE != SEARCH) {
-    for (int i = tid; i < qa.nbuckets; i += nthreads) {
-      uint32_t b = qa.base[i];
-      bool sp = (i == qa.special0) || (i == qa.special1);
-      const uint32_t nan = 0x7fc00000u;
-      E e;
-      e.x = sp ? (uint32_t)qa.z : b;
-      e.y = sp ? nan : f32_bits(s_thr[b]);
-      if constexpr (M >= 2) {
-        e.z = sp ? nan : f32_bits(s_thr[b + 1]);
-        e.w = sp ? nan : f32_bits(s_thr[b + 2]);
+#pragma unroll
+    for (int k = 0; k < kLutIt; ++k) {
+      const int i = tid + k * NT;
+      if (i < qa.nbuckets) {
+        const uint32_t b = bs[k];
+        const bool sp = (i == qa.special0) || (i == qa.special1);
+        const uint32_t nan = 0x7fc00000u;
+        E e;
+        e.x = sp ? (uint32_t)qa.z : b;
+        e.y = sp ? nan : f32_bits(s_thr[b]);
+        if constexpr (M >= 2) {
+          e.z = sp ? nan : f32_bits(s_thr[b + 1]);
+          e.w = sp ? nan : f32_bits(s_thr[b + 2]);
+        }
+        s_lut[i] = e;
       }
-      s_lut[i] = e;
     }
     __syncthreads();
   }

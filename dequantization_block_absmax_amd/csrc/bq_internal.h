@@ -32,7 +32,8 @@ enum Mode : int { LIN = 0, LOG = 1, SEARCH = 2 };
 
 constexpr float kLinAlpha = 0.2421875f;  // 31/128
 constexpr float kLinBeta = 0.75f;
-constexpr int kLutMax = 1600;            // LUT entries that fit the kernel-argument block
+constexpr int kLutMax = 2100;            // LUT entries carried in the kernel arguments
+constexpr int kLinLutMax = 513;          // uniform buckets: H <= 512, plus the +inf bucket
 
 struct QuantArgs {
   // Table-derived data (built on the host per call, passed by value).
@@ -96,11 +97,15 @@ BQ_HD float bits_f32(uint32_t u) {
 // Launchers (k_*.hip).  Each returns the hipError_t of its launches as an int.
 namespace bq {
 int launch_quantize(const void* in, int dtype, int64_t n, int blocksize, const PreparedTable& t,
-                    float* absmax, uint8_t* packed, void* stream);
+                    float* absmax, uint8_t* packed, double* partials, int log2tiles, void* stream);
+// Workgroups (and so partial sums) of a quantize launch over n elements.
+int quantize_grid(int64_t n, int log2tiles);
+constexpr int64_t kQuantTileElems = 8192;  // elements per quantize tile
 int launch_dequantize(void* out, int dtype, int64_t n, int blocksize, const DequantArgs& a,
                       const float* absmax, const uint8_t* packed, void* stream);
 int launch_nested_stats(const float* absmax, int64_t nb, int blocksize2, const PreparedTable& t2,
-                        double* partials, uint8_t* q2, float* absmax2, float* mean, void* stream);
+                        double* partials, int64_t npart, uint8_t* q2, float* absmax2, float* mean,
+                        void* stream);
 int launch_dequantize_nested(void* out, int dtype, int64_t n, int blocksize, int blocksize2,
                              const NestedDequantArgs& a, const uint8_t* q2, const float* absmax2,
                              const float* mean, const uint8_t* packed, void* stream);

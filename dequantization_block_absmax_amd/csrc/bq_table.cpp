@@ -111,9 +111,9 @@ bool prepare_table(const float* entries, int size, PreparedTable* out) {
   best.M = 0;
   int best_cost = 4 * (size == 16 ? 4 : 8) + 2;
 
-  for (int sh : {15, 14, 13}) {
+  for (int sh : {15, 14}) {
     int H = 1 << (23 - sh);
-    if (H + 1 > kLutMax) continue;
+    if (H + 1 > kLinLutMax) continue;
     std::vector<int> ranks(size - 1);
     for (int k = 0; k + 1 < size; ++k) ranks[k] = (int)lin_bucket(thr[k], sh);
     Choice ch;
@@ -124,7 +124,8 @@ bool prepare_table(const float* entries, int size, PreparedTable* out) {
     int cost = 3 + 2 * ch.M;
     if (ch.M <= 3 && cost < best_cost) { best = ch; best_cost = cost; }
   }
-  for (auto se : {std::pair<int, int>{18, 24}, std::pair<int, int>{17, 12}}) {
+  for (auto se : {std::pair<int, int>{17, 16}, std::pair<int, int>{18, 16}, std::pair<int, int>{18, 24},
+                  std::pair<int, int>{17, 12}}) {
     LogParams lp = log_params(se.first, se.second);
     if (2 * lp.nj > kLutMax) continue;
     std::vector<int> ranks(size - 1);
@@ -171,7 +172,7 @@ bool prepare_table(const float* entries, int size, PreparedTable* out) {
 
 // ---- host replay of the kernels' search (test hook of include/bq_debug.h) ----------------
 
-#include "../../include/bq_debug.h"
+#include "bq_debug.h"
 
 namespace {
 

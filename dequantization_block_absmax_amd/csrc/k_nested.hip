@@ -7,15 +7,13 @@
 //   d_b   = fl32(a_b - mean);  per group of B2 blocks: a2_g = max |d_b|,
 //   q2_b  = nearest code of fl32(fl32(d_b * s) * fl32(1 / fl32(a2_g * s))) in the 256 table
 //
-// The mean is a grid-wide dependency, so three kernels run in order on the stream:
-//   partial_sums: one wave per aligned run of 256 leaves.  Lane l adds its 4 leaves as
-//                 (a0 + a1) + (a2 + a3); xor-butterfly steps 1, 2, .., 32 then add aligned
-//                 subtrees of 8, 16, .., 256 leaves: exactly the pairwise tree (binary64
-//                 addition is commutative, so both partners compute the same bits).
-//   mean:         one workgroup continues the same tree over the partial sums.
-//   stats:        one wave per group; same absmax / guard / LUT search as the data kernel.
-// Zero padding is exact inside the tree (x + 0 = x for x >= 0), so padding the 256-leaf runs
-// and the partial sums to larger powers of two leaves S unchanged.
+// The data quantize kernel already writes, per workgroup, the pairwise sum of its blocks'
+// maxima: an aligned subtree of 2^k leaves of the mean's tree (blocks past n hold +0, and
+// x + 0 = x, so padding never changes a sum).  Two kernels finish the statistics:
+//   run_sum_kernel, mean_kernel: continue the same tree over the per-workgroup partials;
+//   stats_kernel: one wave per 2048 or 4096 blocks (4 consecutive per lane per run of 256),
+//                 the same absmax / guard / LUT search as the data kernel, writing q2 and
+//                 the group maxima.
 #include <hip/hip_runtime.h>
 
 #include "bq_device.h"
@@ -25,97 +23,184 @@ namespace bq {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kMeanThreads = 1024;
+constexpr int kLeaves = 32;                 // sums per lane
+constexpr int kWaveLeaves = 64 * kLeaves;   // 2048: leaves per wave
+constexpr int kChunk = 16 * kWaveLeaves;    // 32768: leaves per pass of mean_kernel
 
-__global__ __launch_bounds__(kThreads) void partial_sums_kernel(const float* __restrict__ absmax, int64_t nb,
-                                                                double* __restrict__ partials, int64_t nchunks) {
-  const int lane = threadIdx.x & 63;
-  const int64_t chunk = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (chunk >= nchunks) return;  // whole waves exit together
-  const int64_t i0 = chunk * 256 + lane * 4;
-  double v[4];
+// Lane l of a wave adds leaves [32l, 32l+32) of a 2048-leaf run as a 5-level tree in
+// registers, and the xor butterfly adds aligned runs of 32, 64, .., 2048 leaves (a + b and
+// b + a round alike, so every lane ends with the same value).  Leaves at or past `count`
+// read as +0, which leaves every sum unchanged.
+__device__ __forceinline__ double wave_tree(const double* __restrict__ leaves, int64_t stride, int64_t i0,
+                                            int64_t count, int lane) {
+  const int64_t j0 = i0 + (int64_t)lane * kLeaves;
+  double v[kLeaves];
+  if (stride == 1 && j0 + kLeaves <= count) {
+    const double2* p = reinterpret_cast<const double2*>(leaves + j0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = (i0 + i < nb) ? (double)absmax[i0 + i] : 0.0;
-  double s = (v[0] + v[1]) + (v[2] + v[3]);
+    for (int i = 0; i < kLeaves / 2; ++i) {
+      const double2 d = p[i];
+      v[2 * i] = d.x;
+      v[2 * i + 1] = d.y;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kLeaves; ++i) v[i] = (j0 + i < count) ? leaves[(j0 + i) * stride] : 0.0;
+  }
+#pragma unroll
+  for (int width = kLeaves; width > 1; width >>= 1)
+#pragma unroll
+    for (int i = 0; i < width / 2; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+  double s = v[0];
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) s = s + __shfl_xor(s, m);
-  if (lane == 0) partials[chunk] = s;
+  return s;
 }
 
-// One workgroup of 1024 threads.  Thread t owns leaves [t*L, (t+1)*L) of the partial sums
-// padded to 1024*L (L a power of two) and sums them pairwise with a binary-counter stack;
-// then the wave butterfly and a 16-leaf tree over the waves finish the same tree.
-__global__ __launch_bounds__(1024) void mean_kernel(const double* __restrict__ partials, int64_t nchunks,
-                                                    int64_t L, int64_t nb, float* __restrict__ mean) {
-  __shared__ double s_w[16];
+// First level over many per-workgroup partial sums: wave w replaces leaf 2048w by the sum of
+// leaves [2048w, 2048w + 2048), an aligned subtree of the same tree (it reads its whole run
+// before lane 0 writes, and no other wave reads that run).
+__global__ __launch_bounds__(64) void run_sum_kernel(double* __restrict__ partials, int64_t npart) {
+  const int64_t i0 = (int64_t)blockIdx.x * kWaveLeaves;
+  const double s = wave_tree(partials, 1, i0, npart, threadIdx.x);
+  if (threadIdx.x == 0) partials[i0] = s;
+}
+
+// Sum of `count` leaves leaves[i * stride]: 16 waves add a 32768-leaf chunk (wave sums
+// joined as a 4-level tree by thread 0), and a binary counter in LDS joins the chunks (zero
+// chunks pad the count to a power of two; they leave every sum unchanged).  mean = RN32(S / nb).
+__global__ __launch_bounds__(kMeanThreads) void mean_kernel(const double* __restrict__ leaves, int64_t stride,
+                                                            int64_t count, int64_t nb, float* __restrict__ mean) {
+  __shared__ double s_w[kMeanThreads / 64];
+  __shared__ double s_stack[40];
+  __shared__ int s_has[40];
   const int t = threadIdx.x;
-  double stack[40];
-  for (int64_t i = 0; i < L; ++i) {
-    const int64_t leaf = (int64_t)t * L + i;
-    double v = leaf < nchunks ? partials[leaf] : 0.0;
-    int lvl = 0;
-    for (int64_t k = i; k & 1; k >>= 1, ++lvl) v = stack[lvl] + v;
-    stack[lvl] = v;
+  if (t < 40) s_has[t] = 0;
+  const int64_t nchunks = (count + kChunk - 1) / kChunk;
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const double s = wave_tree(leaves, stride, c * kChunk + (int64_t)(t >> 6) * kWaveLeaves, count, t & 63);
+    if ((t & 63) == 0) s_w[t >> 6] = s;
+    __syncthreads();
+    if (t == 0) {
+      double w[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w[i] = s_w[i];
+#pragma unroll
+      for (int width = 16; width > 1; width >>= 1)
+#pragma unroll
+        for (int i = 0; i < width / 2; ++i) w[i] = w[2 * i] + w[2 * i + 1];
+      double cs = w[0];
+      int lvl = 0;
+      for (int64_t k = c; k & 1; k >>= 1, ++lvl) {
+        cs = s_stack[lvl] + cs;
+        s_has[lvl] = 0;
+      }
+      s_stack[lvl] = cs;
+      s_has[lvl] = 1;
+    }
+    __syncthreads();
   }
-  int top = 0;
-  while ((int64_t(1) << top) < L) ++top;
-  double s = stack[top];
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) s = s + __shfl_xor(s, m);
-  if ((t & 63) == 0) s_w[t >> 6] = s;
-  __syncthreads();
   if (t == 0) {
-    double w[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) w[i] = s_w[i];
-#pragma unroll
-    for (int width = 16; width > 1; width >>= 1)
-#pragma unroll
-      for (int i = 0; i < width / 2; ++i) w[i] = w[2 * i] + w[2 * i + 1];
-    *mean = (float)(w[0] / (double)nb);
+    // Pad with zero chunks: carry the lowest pending subtree upwards; a pending subtree at a
+    // level is the left neighbour of everything below it.
+    double carry = 0.0;
+    bool any = false;
+    for (int l = 0; l < 40; ++l) {
+      if (s_has[l]) {
+        carry = any ? s_stack[l] + carry : s_stack[l];
+        any = true;
+      }
+    }
+    *mean = (float)(carry / (double)nb);
   }
 }
 
-template <int MODE, int M>
+// One wave covers KR runs of 256 consecutive blocks (lane l holds blocks 4l..4l+3 of each run);
+// a group of B2 blocks is ceil(B2 / 256) whole runs, or B2 / 4 lanes of one run.  All of a
+// wave's loads are issued before the LUT prologue.
+template <int MODE, int M, int KR>
 __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict__ absmax, int64_t nb,
                                                          const float* __restrict__ mean, int log2b2,
                                                          int64_t ngroups, uint8_t* __restrict__ q2,
                                                          float* __restrict__ absmax2, QuantArgs qa) {
   using E = typename Entry<M>::type;
   __shared__ float s_thr[260];
-  __shared__ E s_lut[MODE == SEARCH ? 1 : kLutMax];
+  __shared__ E s_lut[LutLayout<MODE, M>::kSize];
   const int tid = threadIdx.x;
-  build_lut<MODE, M>(qa, s_lut, s_thr, tid, kThreads);
-
   const int lane = tid & 63;
-  const float m = *mean;
   const int B2 = 1 << log2b2;
-  const int per = B2 >= 64 ? B2 / 64 : 1;
-  for (int64_t g = (int64_t)blockIdx.x * (kThreads / 64) + (tid >> 6); g < ngroups;
-       g += (int64_t)gridDim.x * (kThreads / 64)) {
-    const int64_t b0 = g << log2b2;
-    uint32_t key = 0;  // |d| bit patterns; all d are finite
-    for (int i = 0; i < per; ++i) {
-      const int64_t v = i * 64 + lane;
-      const int64_t b = b0 + v;
-      if (v < B2 && b < nb) {
-        const float d = absmax[b] - m;
-        key = max(key, f32_bits(d) & 0x7fffffffu);
-      }
-    }
+  const int R = B2 > 256 ? B2 >> 8 : 1;       // runs per group
+  const int lg = B2 >= 256 ? 64 : (B2 >> 2);  // lanes per group inside a run
+  const int64_t b0 = ((int64_t)blockIdx.x * (kThreads / 64) + (tid >> 6)) * 256 * KR + lane * 4;
+  const bool active = b0 - lane * 4 < nb;
+
+  float4 v[KR];
 #pragma unroll
-    for (int k = 1; k < 64; k <<= 1) key = max(key, (uint32_t)__shfl_xor((int)key, k));
-    const float a2 = bits_f32(key);
-    if (lane == 0) absmax2[g] = a2;
+  for (int r = 0; r < KR; ++r) {
+    const int64_t b = b0 + r * 256;
+    v[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (b + 4 <= nb) {
+      v[r] = *reinterpret_cast<const float4*>(absmax + b);
+    } else if (b < nb) {
+      v[r].x = absmax[b];
+      if (b + 1 < nb) v[r].y = absmax[b + 1];
+      if (b + 2 < nb) v[r].z = absmax[b + 2];
+    }
+  }
+  build_lut<MODE, M, kThreads>(qa, s_lut, s_thr, tid);
+  if (!active) return;  // whole waves
+  const float m = *mean;
+
+  // d = a - mean; blocks past nb contribute nothing to a group maximum.
+  uint32_t key[KR];
+#pragma unroll
+  for (int r = 0; r < KR; ++r) {
+    const int64_t b = b0 + r * 256;
+    float d[4] = {v[r].x - m, v[r].y - m, v[r].z - m, v[r].w - m};
+    key[r] = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (b + i < nb) key[r] = max(key[r], f32_bits(d[i]) & 0x7fffffffu);
+    v[r] = make_float4(d[0], d[1], d[2], d[3]);
+  }
+#pragma unroll
+  for (int r = 0; r < KR; ++r)
+    for (int k = 1; k < lg; k <<= 1) key[r] = max(key[r], (uint32_t)__shfl_xor((int)key[r], k));
+#pragma unroll
+  for (int st = 1; st < KR; st <<= 1)
+    if (st < R) {
+#pragma unroll
+      for (int r = 0; r < KR; ++r)
+        if ((r & st) == 0) {
+          const uint32_t k2 = max(key[r], key[r | st]);
+          key[r] = k2;
+          key[r | st] = k2;
+        }
+    }
+
+#pragma unroll
+  for (int r = 0; r < KR; ++r) {
+    const int64_t b = b0 + r * 256;
+    if (b >= nb) continue;
+    const float a2 = bits_f32(key[r]);
+    const int64_t g = b >> log2b2;
+    if ((lane & (lg - 1)) == 0 && (r & (R - 1)) == 0 && g < ngroups) absmax2[g] = a2;
     const float s = a2 < 0x1p-64f ? 0x1p64f : (a2 > 0x1p64f ? 0x1p-64f : 1.0f);
-    const float r = 1.0f / (a2 * s);
-    for (int i = 0; i < per; ++i) {
-      const int64_t v = i * 64 + lane;
-      const int64_t b = b0 + v;
-      if (v < B2 && b < nb) {
-        const float d = absmax[b] - m;
-        const float y = (s == 1.0f) ? d * r : (d * s) * r;
-        q2[b] = (uint8_t)nearest_code<MODE, M>(y, qa, s_lut, s_thr);
-      }
+    const float rc = 1.0f / (a2 * s);
+    const float d[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float y = (s == 1.0f) ? d[i] * rc : (d[i] * s) * rc;
+      w |= nearest_code<MODE, M>(y, qa, s_lut, s_thr) << (8 * i);
+    }
+    if (b + 4 <= nb) {
+      *reinterpret_cast<uint32_t*>(q2 + b) = w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (b + i < nb) q2[b + i] = (uint8_t)(w >> (8 * i));
     }
   }
 }
@@ -123,24 +208,35 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
 template <int MODE, int M>
 hipError_t launch_stats(const float* absmax, int64_t nb, const float* mean, int log2b2, int64_t ngroups,
                         uint8_t* q2, float* absmax2, const QuantArgs& qa, hipStream_t s) {
-  int64_t grid = (ngroups + 3) / 4;
-  if (grid > 2048) grid = 2048;
-  return launch_kernel(stats_kernel<MODE, M>, dim3((unsigned)grid), dim3(kThreads), s, absmax, nb, mean, log2b2,
-                       ngroups, q2, absmax2, qa);
+  if (log2b2 > 11) {
+    const int64_t grid = (nb + 4 * 256 * 16 - 1) / (4 * 256 * 16);
+    return launch_kernel(stats_kernel<MODE, M, 16>, dim3((unsigned)grid), dim3(kThreads), s, absmax, nb, mean,
+                         log2b2, ngroups, q2, absmax2, qa);
+  }
+  const int64_t grid = (nb + 4 * 256 * 8 - 1) / (4 * 256 * 8);
+  return launch_kernel(stats_kernel<MODE, M, 8>, dim3((unsigned)grid), dim3(kThreads), s, absmax, nb, mean,
+                       log2b2, ngroups, q2, absmax2, qa);
 }
 
 }  // namespace
 
-int launch_nested_stats(const float* absmax, int64_t nb, int blocksize2, const PreparedTable& t2, double* partials,
-                        uint8_t* q2, float* absmax2, float* mean, void* stream) {
+int launch_nested_stats(const float* absmax, int64_t nb, int blocksize2, const PreparedTable& t2,
+                        double* partials, int64_t npart, uint8_t* q2, float* absmax2, float* mean,
+                        void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t nchunks = (nb + 255) / 256;
-  hipError_t e = launch_kernel(partial_sums_kernel, dim3((unsigned)((nchunks + 3) / 4)), dim3(kThreads), s, absmax,
-                               nb, partials, nchunks);
-  if (e != hipSuccess) return (int)e;
-  int64_t L = 1;
-  while (L * 1024 < nchunks) L *= 2;
-  e = launch_kernel(mean_kernel, dim3(1), dim3(1024), s, partials, nchunks, L, nb, mean);
+  // One workgroup reading many partials is bound by a single CU's bandwidth; above one run,
+  // runs of 2048 are first summed in place by one wave each.
+  hipError_t e;
+  double* leaves = const_cast<double*>(partials);
+  int64_t stride = 1, count = npart;
+  if (npart > kWaveLeaves) {
+    const int64_t runs = (npart + kWaveLeaves - 1) / kWaveLeaves;
+    e = launch_kernel(run_sum_kernel, dim3((unsigned)runs), dim3(64), s, leaves, npart);
+    if (e != hipSuccess) return (int)e;
+    stride = kWaveLeaves;
+    count = runs;
+  }
+  e = launch_kernel(mean_kernel, dim3(1), dim3(kMeanThreads), s, (const double*)leaves, stride, count, nb, mean);
   if (e != hipSuccess) return (int)e;
   int log2b2 = 0;
   while ((1 << log2b2) < blocksize2) ++log2b2;

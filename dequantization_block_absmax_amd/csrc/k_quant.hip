@@ -65,7 +65,7 @@ __device__ __forceinline__ uint32_t chunk_key(const uint32_t* w) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       u16x2 h = __builtin_bit_cast(u16x2, w[i]);
-      u16x2 k = (h << (unsigned short)1) + (u16x2){off, off};
+      u16x2 k = h * (u16x2){2, 2} + (u16x2){off, off};  // one packed multiply-add per pair
       acc = __builtin_elementwise_max(acc, k);
     }
     return max((uint32_t)acc.x, (uint32_t)acc.y);
@@ -85,165 +85,247 @@ __device__ __forceinline__ float key_to_absmax(uint32_t k) {
   }
 }
 
+// Loads the 32 elements of this lane's chunk (first element elem0) into w with 16-byte loads;
+// returns how many are < n.  The ragged end loads element by element; elements past n read
+// as NaN, which the absmax key excludes.
+template <int DT>
+__device__ __forceinline__ int load_chunk(const uint8_t* __restrict__ in, int64_t n, int64_t elem0, uint32_t* w) {
+  using Tr = Traits<DT>;
+  if (elem0 + kEPT <= n) {
+    const uint4* src = reinterpret_cast<const uint4*>(in + elem0 * (DT == F32 ? 4 : 2));
+#pragma unroll
+    for (int i = 0; i < Tr::kWords / 4; ++i) {
+      uint4 v = src[i];
+      w[4 * i] = v.x;
+      w[4 * i + 1] = v.y;
+      w[4 * i + 2] = v.z;
+      w[4 * i + 3] = v.w;
+    }
+    return 32;
+  }
+  const int nvalid = elem0 < n ? (int)(n - elem0) : 0;
+#pragma unroll
+  for (int i = 0; i < Tr::kWords; ++i) w[i] = Tr::kNaNWord;
+  if constexpr (DT == F32) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(in) + elem0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+      if (e < nvalid) w[e] = src[e];
+  } else {
+    const unsigned short* src = reinterpret_cast<const unsigned short*>(in) + elem0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+      if (e < nvalid)
+        w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0xffffu) | ((uint32_t)src[e] << 16)) : ((w[e >> 1] & 0xffff0000u) | src[e]);
+  }
+  return nvalid;
+}
+
+struct QuantShared {
+  uint32_t red[kThreads / 64];
+  double wave[kThreads / 64];  // per-wave subtree sums of the nested mean
+  double stack[8];             // binary counter over the workgroup's tiles
+};
+
+// Quantizes one lane chunk (tile t of the workgroup): block absmax, normalization, codes,
+// packing and stores; with `partials`, adds the tile's block maxima to the binary counter.
 template <int DT, int KB, int MODE, int M>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __restrict__ in, int64_t n,
-                                                            int log2g, int tiles,
-                                                            float* __restrict__ absmax,
-                                                            uint8_t* __restrict__ packed, QuantArgs qa) {
+__device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, int64_t elem0, int64_t n, int log2g,
+                                               int t, float* __restrict__ absmax, uint8_t* __restrict__ packed,
+                                               double* __restrict__ partials, const QuantArgs& qa,
+                                               const typename Entry<M>::type* s_lut, const float* s_thr,
+                                               QuantShared& sh, uint4* stage) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int G = 1 << log2g;
+  const int64_t nb = (n + (kEPT << log2g) - 1) >> (5 + log2g);
+
+  // Block absmax over G lanes.
+  uint32_t key = chunk_key<DT>(w);
+  for (int m = 1; m < G && m < 64; m <<= 1) key = max(key, (uint32_t)__shfl_xor((int)key, m));
+  if (G > 64) {  // B = 4096: two waves per block
+    if (lane == 0) sh.red[tid >> 6] = key;
+    __syncthreads();
+    key = max(sh.red[tid >> 6], sh.red[(tid >> 6) ^ 1]);
+    __syncthreads();
+  }
+  const float a = key_to_absmax<DT>(key);
+  const int64_t blk = elem0 >> (5 + log2g);
+  if ((tid & (G - 1)) == 0 && blk < nb) absmax[blk] = a;
+
+  if (partials != nullptr) {
+    // Pairwise sum of this tile's block maxima (an aligned subtree of the nested mean's tree;
+    // blocks past n hold +0).  Every lane of a block holds its absmax, so xor steps G, 2G,
+    // .., 32 add adjacent subtrees within the wave (commutative: both partners get the same
+    // bits); the four waves then combine as (w0 + w1) + (w2 + w3).
+    double sum = (double)a;
+    for (int m = G; m < 64; m <<= 1) sum = sum + __shfl_xor(sum, m);
+    if (lane == 0) sh.wave[tid >> 6] = sum;
+    __syncthreads();
+    if (tid == 0) {
+      double tsum = G <= 64 ? (sh.wave[0] + sh.wave[1]) + (sh.wave[2] + sh.wave[3])
+                            : sh.wave[0] + sh.wave[2];  // B = 4096: waves 0-1 and 2-3 hold one block each
+      int lvl = 0;
+      for (int k = t; k & 1; k >>= 1, ++lvl) tsum = sh.stack[lvl] + tsum;
+      sh.stack[lvl] = tsum;
+    }
+    __syncthreads();
+  }
+
+  // Normalize with the power-of-two guard; codes are packed into their output word as soon
+  // as they are found (first element of a pair in the high nibble for 4-bit codes).
+  const float s = a < 0x1p-64f ? 0x1p64f : (a > 0x1p64f ? 0x1p-64f : 1.0f);
+  const float r = 1.0f / (a * s);
+  constexpr int kOut = KB == 4 ? 4 : 8;  // output words per lane chunk
+  constexpr int kPer = 32 / kOut;        // codes per output word
+  uint32_t o[kOut];
+  if (s == 1.0f) {
+#pragma unroll
+    for (int i = 0; i < kOut; ++i) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const uint32_t q = nearest_code<MODE, M>(widen<DT>(w, i * kPer + j) * r, qa, s_lut, s_thr);
+        v |= KB == 4 ? q << (8 * (j >> 1) + 4 * (1 - (j & 1))) : q << (8 * j);
+      }
+      o[i] = v;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kOut; ++i) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const uint32_t q = nearest_code<MODE, M>((widen<DT>(w, i * kPer + j) * s) * r, qa, s_lut, s_thr);
+        v |= KB == 4 ? q << (8 * (j >> 1) + 4 * (1 - (j & 1))) : q << (8 * j);
+      }
+      o[i] = v;
+    }
+  }
+  if (nvalid < 32) {  // codes of elements past n are 0 (the pad nibble of an odd n)
+#pragma unroll
+    for (int i = 0; i < kOut; ++i) {
+      const int c = min(max(nvalid - i * kPer, 0), kPer);
+      uint32_t mask;
+      if (KB == 4)
+        mask = c >= 8 ? 0xffffffffu : ((1u << (8 * (c >> 1))) - 1u) | ((c & 1) ? (0xf0u << (8 * (c >> 1))) : 0u);
+      else
+        mask = c >= 4 ? 0xffffffffu : (1u << (8 * c)) - 1u;
+      o[i] &= mask;
+    }
+  }
+
+  // Store.  4-bit: each lane's 16 bytes follow its left neighbour's.  8-bit: a lane holds 32
+  // bytes, so a wave's 2 KB goes through its LDS region and leaves as two 1 KB stores with
+  // consecutive lanes writing consecutive 16 bytes (lane l writes half l & 1 of lane 32k + l/2).
+  const int64_t packed_bytes = KB == 4 ? (n + 1) / 2 : n;
+  constexpr int kBytes = kOut * 4;
+  const int64_t off = KB == 4 ? elem0 >> 1 : elem0;
+  const int64_t wave_off = off - (int64_t)lane * kBytes;
+  if (KB == 8 && wave_off + 64 * kBytes <= packed_bytes) {  // whole wave in range (uniform)
+    stage[2 * lane] = make_uint4(o[0], o[1], o[2], o[3]);
+    stage[2 * lane + 1] = make_uint4(o[4 % kOut], o[5 % kOut], o[6 % kOut], o[7 % kOut]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint4* dst = reinterpret_cast<uint4*>(packed + wave_off);
+    dst[lane] = stage[lane];
+    dst[64 + lane] = stage[64 + lane];
+    __builtin_amdgcn_wave_barrier();  // the next tile's writes come after these reads
+  } else if (KB == 4 && off + kBytes <= packed_bytes) {
+    *reinterpret_cast<uint4*>(packed + off) = make_uint4(o[0], o[1], o[2], o[3]);
+  } else if (KB == 8 && off + kBytes <= packed_bytes) {
+    uint4* dst = reinterpret_cast<uint4*>(packed + off);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4 % kOut], o[5 % kOut], o[6 % kOut], o[7 % kOut]);
+  } else if (off < packed_bytes) {
+#pragma unroll
+    for (int i = 0; i < kBytes; ++i)
+      if (off + i < packed_bytes) packed[off + i] = (uint8_t)(o[i >> 2] >> (8 * (i & 3)));
+  }
+}
+
+// A workgroup quantizes 2^log2tiles consecutive tiles of 8192 elements.
+template <int DT, int KB, int MODE, int M>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __restrict__ in, int64_t n, int log2g,
+                                                            int log2tiles, float* __restrict__ absmax,
+                                                            uint8_t* __restrict__ packed,
+                                                            double* __restrict__ partials, QuantArgs qa) {
   using Tr = Traits<DT>;
   using E = typename Entry<M>::type;
   __shared__ float s_thr[260];
-  __shared__ E s_lut[MODE == SEARCH ? 1 : kLutMax];
-  __shared__ uint32_t s_red[kThreads / 64];
+  __shared__ E s_lut[LutLayout<MODE, M>::kSize];
+  __shared__ uint4 s_stage[KB == 8 ? kThreads * 2 : 1];  // 8-bit codes: store exchange
+  __shared__ QuantShared sh;
 
   const int tid = threadIdx.x;
-  build_lut<MODE, M>(qa, s_lut, s_thr, tid, kThreads);
-
-  const int G = 1 << log2g;
-  const int B = kEPT << log2g;
-  const int64_t nb = (n + B - 1) / B;
-  const int64_t packed_bytes = KB == 4 ? (n + 1) / 2 : n;
-  const int lane = tid & 63;
-
+  const int tiles = 1 << log2tiles;
+  const int64_t tile0 = (int64_t)blockIdx.x << log2tiles;
+  // The first tile's loads are issued before the table prologue, so the two overlap.
+  int64_t elem0 = (tile0 * kThreads + tid) * kEPT;
+  uint32_t w[Tr::kWords];
+  int nvalid = load_chunk<DT>(in, n, elem0, w);
+  build_lut<MODE, M, kThreads>(qa, s_lut, s_thr, tid);
+  uint4* stage = s_stage + (KB == 8 ? (tid >> 6) * 128 : 0);
   for (int t = 0; t < tiles; ++t) {
-    const int64_t elem0 = ((int64_t)(blockIdx.x * tiles + t) * kThreads + tid) * kEPT;
-    uint32_t w[Tr::kWords];
-    int nvalid = 32;
-    if (elem0 + kEPT <= n) {
-      const uint4* src = reinterpret_cast<const uint4*>(in + elem0 * (DT == F32 ? 4 : 2));
-#pragma unroll
-      for (int i = 0; i < Tr::kWords / 4; ++i) {
-        uint4 v = src[i];
-        w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
-      }
-    } else {
-      nvalid = elem0 < n ? (int)(n - elem0) : 0;
-#pragma unroll
-      for (int i = 0; i < Tr::kWords; ++i) w[i] = Tr::kNaNWord;  // NaN pads: excluded from absmax
-      if constexpr (DT == F32) {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(in) + elem0;
-#pragma unroll
-        for (int e = 0; e < 32; ++e)
-          if (e < nvalid) w[e] = src[e];
-      } else {
-        const unsigned short* src = reinterpret_cast<const unsigned short*>(in) + elem0;
-#pragma unroll
-        for (int e = 0; e < 32; ++e)
-          if (e < nvalid)
-            w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0xffffu) | ((uint32_t)src[e] << 16))
-                                : ((w[e >> 1] & 0xffff0000u) | src[e]);
-      }
+    if (t > 0) {
+      elem0 = ((tile0 + t) * kThreads + tid) * kEPT;
+      nvalid = load_chunk<DT>(in, n, elem0, w);
     }
-
-    // Block absmax over G lanes.
-    uint32_t key = chunk_key<DT>(w);
-    for (int m = 1; m < G && m < 64; m <<= 1) key = max(key, (uint32_t)__shfl_xor((int)key, m));
-    if (G > 64) {  // B = 4096: two waves per block
-      if (lane == 0) s_red[tid >> 6] = key;
-      __syncthreads();
-      key = max(s_red[tid >> 6], s_red[(tid >> 6) ^ 1]);
-      __syncthreads();
-    }
-    const float a = key_to_absmax<DT>(key);
-    const int64_t blk = elem0 >> (5 + log2g);
-    if ((tid & (G - 1)) == 0 && blk < nb) absmax[blk] = a;
-
-    // Normalize with the power-of-two guard.
-    const float s = a < 0x1p-64f ? 0x1p64f : (a > 0x1p64f ? 0x1p-64f : 1.0f);
-    const float r = 1.0f / (a * s);
-    uint32_t q[32];
-    if (s == 1.0f) {
-#pragma unroll
-      for (int e = 0; e < 32; ++e) q[e] = nearest_code<MODE, M>(widen<DT>(w, e) * r, qa, s_lut, s_thr);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 32; ++e) q[e] = nearest_code<MODE, M>((widen<DT>(w, e) * s) * r, qa, s_lut, s_thr);
-    }
-    if (nvalid < 32) {
-#pragma unroll
-      for (int e = 0; e < 32; ++e) q[e] = e < nvalid ? q[e] : 0u;  // zero pad nibble / unused codes
-    }
-
-    // Pack and store.
-    if constexpr (KB == 4) {
-      uint32_t o[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t v = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) v |= ((q[8 * i + 2 * b] << 4) | q[8 * i + 2 * b + 1]) << (8 * b);
-        o[i] = v;
-      }
-      const int64_t off = elem0 >> 1;
-      if (off + 16 <= packed_bytes) {
-        *reinterpret_cast<uint4*>(packed + off) = make_uint4(o[0], o[1], o[2], o[3]);
-      } else if (off < packed_bytes) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (off + i < packed_bytes) packed[off + i] = (uint8_t)(o[i >> 2] >> (8 * (i & 3)));
-      }
-    } else {
-      uint32_t o[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = q[4 * i] | (q[4 * i + 1] << 8) | (q[4 * i + 2] << 16) | (q[4 * i + 3] << 24);
-      const int64_t off = elem0;
-      if (off + 32 <= packed_bytes) {
-        uint4* dst = reinterpret_cast<uint4*>(packed + off);
-        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-      } else if (off < packed_bytes) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-          if (off + i < packed_bytes) packed[off + i] = (uint8_t)(o[i >> 2] >> (8 * (i & 3)));
-      }
-    }
+    quantize_chunk<DT, KB, MODE, M>(w, nvalid, elem0, n, log2g, t, absmax, packed, partials, qa, s_lut, s_thr, sh,
+                                    stage);
   }
+  if (partials != nullptr && tid == 0) partials[blockIdx.x] = sh.stack[log2tiles];
 }
 
 template <int DT, int KB, int MODE, int M>
-hipError_t launch4(const void* in, int64_t n, int log2g, float* absmax, uint8_t* packed, const QuantArgs& qa,
-                   hipStream_t stream) {
+hipError_t launch4(const void* in, int64_t n, int log2g, int log2tiles, float* absmax, uint8_t* packed,
+                   double* partials, const QuantArgs& qa, hipStream_t stream) {
   const int64_t tiles_total = (n + kTile - 1) / kTile;
-  const int tiles = 1;
-  const int64_t grid = (tiles_total + tiles - 1) / tiles;
+  const int64_t grid = (tiles_total + (1 << log2tiles) - 1) >> log2tiles;
   return launch_kernel(quantize_kernel<DT, KB, MODE, M>, dim3((unsigned)grid), dim3(kThreads), stream,
-                       static_cast<const uint8_t*>(in), n, log2g, tiles, absmax, packed, qa);
+                       static_cast<const uint8_t*>(in), n, log2g, log2tiles, absmax, packed, partials, qa);
 }
 
 template <int DT, int KB>
-hipError_t launch_mode(const void* in, int64_t n, int log2g, float* absmax, uint8_t* packed,
-                       const PreparedTable& t, hipStream_t s) {
+hipError_t launch_mode(const void* in, int64_t n, int log2g, int lt, float* absmax, uint8_t* packed,
+                       double* partials, const PreparedTable& t, hipStream_t s) {
   if (t.mode == LIN) {
-    if (t.M <= 1) return launch4<DT, KB, LIN, 1>(in, n, log2g, absmax, packed, t.qa, s);
-    if (t.M == 2) return launch4<DT, KB, LIN, 2>(in, n, log2g, absmax, packed, t.qa, s);
-    return launch4<DT, KB, LIN, 3>(in, n, log2g, absmax, packed, t.qa, s);
+    if (t.M <= 1) return launch4<DT, KB, LIN, 1>(in, n, log2g, lt, absmax, packed, partials, t.qa, s);
+    if (t.M == 2) return launch4<DT, KB, LIN, 2>(in, n, log2g, lt, absmax, packed, partials, t.qa, s);
+    return launch4<DT, KB, LIN, 3>(in, n, log2g, lt, absmax, packed, partials, t.qa, s);
   }
   if (t.mode == LOG) {
-    if (t.M <= 1) return launch4<DT, KB, LOG, 1>(in, n, log2g, absmax, packed, t.qa, s);
-    if (t.M == 2) return launch4<DT, KB, LOG, 2>(in, n, log2g, absmax, packed, t.qa, s);
-    return launch4<DT, KB, LOG, 3>(in, n, log2g, absmax, packed, t.qa, s);
+    if (t.M <= 1) return launch4<DT, KB, LOG, 1>(in, n, log2g, lt, absmax, packed, partials, t.qa, s);
+    if (t.M == 2) return launch4<DT, KB, LOG, 2>(in, n, log2g, lt, absmax, packed, partials, t.qa, s);
+    return launch4<DT, KB, LOG, 3>(in, n, log2g, lt, absmax, packed, partials, t.qa, s);
   }
-  return launch4<DT, KB, SEARCH, 1>(in, n, log2g, absmax, packed, t.qa, s);
+  return launch4<DT, KB, SEARCH, 1>(in, n, log2g, lt, absmax, packed, partials, t.qa, s);
 }
 
 template <int DT>
-hipError_t launch_dt(const void* in, int64_t n, int log2g, float* absmax, uint8_t* packed, const PreparedTable& t,
-                     hipStream_t s) {
-  return t.K == 16 ? launch_mode<DT, 4>(in, n, log2g, absmax, packed, t, s)
-                   : launch_mode<DT, 8>(in, n, log2g, absmax, packed, t, s);
+hipError_t launch_dt(const void* in, int64_t n, int log2g, int lt, float* absmax, uint8_t* packed,
+                     double* partials, const PreparedTable& t, hipStream_t s) {
+  return t.K == 16 ? launch_mode<DT, 4>(in, n, log2g, lt, absmax, packed, partials, t, s)
+                   : launch_mode<DT, 8>(in, n, log2g, lt, absmax, packed, partials, t, s);
 }
 
 }  // namespace
 
+int quantize_grid(int64_t n, int log2tiles) {
+  const int64_t tiles_total = (n + kTile - 1) / kTile;
+  return (int)((tiles_total + (1 << log2tiles) - 1) >> log2tiles);
+}
+
 int launch_quantize(const void* in, int dtype, int64_t n, int blocksize, const PreparedTable& t, float* absmax,
-                    uint8_t* packed, void* stream) {
+                    uint8_t* packed, double* partials, int log2tiles, void* stream) {
   int log2g = 0;
   while ((kEPT << log2g) < blocksize) ++log2g;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (dtype == F32) e = launch_dt<F32>(in, n, log2g, absmax, packed, t, s);
-  else if (dtype == F16) e = launch_dt<F16>(in, n, log2g, absmax, packed, t, s);
-  else e = launch_dt<BF16>(in, n, log2g, absmax, packed, t, s);
+  if (dtype == F32) e = launch_dt<F32>(in, n, log2g, log2tiles, absmax, packed, partials, t, s);
+  else if (dtype == F16) e = launch_dt<F16>(in, n, log2g, log2tiles, absmax, packed, partials, t, s);
+  else e = launch_dt<BF16>(in, n, log2g, log2tiles, absmax, packed, partials, t, s);
   return (int)e;
 }
 

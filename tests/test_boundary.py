@@ -140,10 +140,11 @@ def test_nested_validation():
 
 def test_workspace_bytes():
     assert bq.bq_nested_workspace_bytes(0, 64, 256) == 0
-    nb = -(-(2**29) // 64)
-    ws = bq.bq_nested_workspace_bytes(2**29, 64, 256)
-    assert ws >= nb * 4 + (-(-nb // 256)) * 8
-    assert ws < nb * 4 + (-(-nb // 256)) * 8 + 512
+    for n, B in ((2**29, 64), (1000, 32), (8192 * 3 + 1, 4096)):
+        nb = -(-n // B)
+        need = nb * 4 + (-(-n // 8192)) * 8  # fp32 block maxima + one fp64 partial sum per tile
+        ws = bq.bq_nested_workspace_bytes(n, B, 256)
+        assert need <= ws < need + 512
 
 
 def test_q32_validation():

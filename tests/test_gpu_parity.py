@@ -266,11 +266,13 @@ def test_nested_full_parity(dev, o, dtype, B, B2):
 
 
 def test_nested_mean_tree_shapes(dev, o):
-    """Block counts around powers of two and the 256-leaf partial-sum runs, with magnitudes
+    """Block counts around powers of two and the per-workgroup partial-sum runs, with magnitudes
     spread over many binades so that any other summation order would change the mean."""
     t16, t256 = synth.table16(), synth.table256()
     rng = np.random.default_rng(77)
-    for nb in (1, 2, 255, 256, 257, 1023, 1024, 1025, 65536 + 1, 262144 + 256 * 3 + 1):
+    # the last two give 2999 and 4121 per-workgroup partial sums: several ragged 2048-runs
+    for nb in (1, 2, 255, 256, 257, 1023, 1024, 1025, 65536 + 1, 262144 + 256 * 3 + 1, 2999 * 256 - 77,
+               2 * 4096 * 256 + 12345):
         heads = np.float32(np.abs(rng.normal(0, 1, nb)) * 2.0 ** rng.integers(-30, 30, nb))
         x = np.zeros(nb * 32, np.float32)
         x[::32] = heads
