@@ -7,10 +7,12 @@
 //
 // Work decomposition.  A unit is 8 consecutive elements: 4 bytes of 4-bit codes or 8 bytes of
 // 8-bit codes in, 16 bytes of bf16/fp16 (32 of fp32) out.  Lane `tid` of a 256-lane
-// workgroup handles units tile*1024 + u*256 + tid for u = 0..3, so every load and store
-// instruction of a wave touches one contiguous span (per-lane contiguous 64-byte writes
-// measured at half the bandwidth of this layout on MI355X).  The table lives in LDS; the
-// binary32 product is rounded once by the hardware conversion (round-to-nearest-even).
+// workgroup handles units tile*256*U + u*256 + tid for u < U (U = 4 for 4-bit codes, 2 for 8-bit), so
+// every load and store instruction of a wave touches one contiguous span (per-lane
+// contiguous 64-byte writes measured at half the bandwidth of this layout on MI355X).  The
+// lane's code loads are issued first; the tile's block scales are staged in LDS meanwhile.
+// The table lives in LDS; the binary32 product is rounded once by the hardware conversion
+// (round-to-nearest-even).
 #include <hip/hip_runtime.h>
 
 #include "bq_internal.h"
@@ -20,8 +22,14 @@ namespace bq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnits = 4;                          // units per lane per workgroup
-constexpr int kTileElems = kThreads * kUnits * 8;  // 8192
+// Units per lane: 4 for 4-bit codes (a 8192-element tile), 2 for 8-bit codes (4096), the
+// faster of 2, 4 and 8 for each on MI355X.
+template <int KB>
+struct Tile {
+  static constexpr int kUnits = KB == 4 ? 4 : 2;
+  static constexpr int kElems = kThreads * kUnits * 8;
+  static constexpr int kBlocks = kElems / 32;  // most blocks a tile can touch (B >= 32)
+};
 
 // Stores 8 binary32 values as `DT` at element offset e (full unit).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -70,40 +78,47 @@ __device__ __forceinline__ void store_tail(uint8_t* out, int64_t e, const float*
   }
 }
 
-// Codes of a unit starting at element e (e a multiple of 8).
+// Raw code bytes of the unit starting at element e (e a multiple of 8, e < n): 4 bytes of
+// nibbles (4-bit) or 8 code bytes (8-bit); bytes past the end of `packed` read as 0.
 template <int KB>
-__device__ __forceinline__ void load_codes(const uint8_t* packed, int64_t e, int64_t n, uint32_t* q) {
+__device__ __forceinline__ uint2 fetch_codes(const uint8_t* packed, int64_t e, int64_t n) {
+  uint2 p = make_uint2(0, 0);
   if constexpr (KB == 4) {
-    uint32_t p;
     if (e + 8 <= n) {
-      p = *reinterpret_cast<const uint32_t*>(packed + (e >> 1));
+      p.x = *reinterpret_cast<const uint32_t*>(packed + (e >> 1));
     } else {
-      p = 0;
       const int64_t nbytes = (n + 1) >> 1;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if ((e >> 1) + i < nbytes) p |= (uint32_t)packed[(e >> 1) + i] << (8 * i);
-    }
-    // byte b holds element 2b in its high nibble and element 2b+1 in its low nibble
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      q[2 * b] = (p >> (8 * b + 4)) & 15u;
-      q[2 * b + 1] = (p >> (8 * b)) & 15u;
+        if ((e >> 1) + i < nbytes) p.x |= (uint32_t)packed[(e >> 1) + i] << (8 * i);
     }
   } else {
-    uint2 p;
     if (e + 8 <= n) {
       p = *reinterpret_cast<const uint2*>(packed + e);
     } else {
-      p = make_uint2(0, 0);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if (e + i < n) {
-          uint32_t byte = packed[e + i];
+          const uint32_t byte = packed[e + i];
           if (i < 4) p.x |= byte << (8 * i);
           else p.y |= byte << (8 * (i - 4));
         }
     }
+  }
+  return p;
+}
+
+// The 8 codes of a unit from its raw bytes.
+template <int KB>
+__device__ __forceinline__ void decode_codes(uint2 p, uint32_t* q) {
+  if constexpr (KB == 4) {
+    // byte b holds element 2b in its high nibble and element 2b+1 in its low nibble
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      q[2 * b] = (p.x >> (8 * b + 4)) & 15u;
+      q[2 * b + 1] = (p.x >> (8 * b)) & 15u;
+    }
+  } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       q[i] = (p.x >> (8 * i)) & 255u;
@@ -112,31 +127,63 @@ __device__ __forceinline__ void load_codes(const uint8_t* packed, int64_t e, int
   }
 }
 
-// A lane takes its units one after another (load, scale, store).  Issuing all of a lane's
-// loads first measured slower on MI355X for the nested kernel (314 us against 273 us on
-// 2^29 bf16 outputs), and no faster for the plain one.
-template <int DT, int KB>
-__global__ __launch_bounds__(kThreads) void dequantize_kernel(const uint8_t* __restrict__ packed,
-                                                              const float* __restrict__ absmax, int64_t n,
-                                                              int log2b, uint8_t* __restrict__ out,
-                                                              DequantArgs da) {
-  __shared__ float s_c[256];
-  const int tid = threadIdx.x;
-  s_c[tid] = tid < da.K ? da.c[tid] : 0.0f;
-  __syncthreads();
+// Block scales of a tile are staged in LDS, each block's by one thread: one coalesced load
+// per block instead of one gather per unit.  With per-unit gathers of the nested statistics the kernel ran at 62% of HBM
+// peak on 2^29 bf16 outputs, against 90% without them.
+
+// Blocks of the tile starting at element e0: [e0 >> log2b, last element's block].
+template <int KB>
+__device__ __forceinline__ int tile_blocks(int64_t e0, int64_t n, int log2b) {
+  const int64_t e1 = min(e0 + (int64_t)Tile<KB>::kElems, n) - 1;
+  return (int)((e1 >> log2b) - (e0 >> log2b)) + 1;
+}
+
+// A lane's code loads, issued before the workgroup prologue so that they overlap it.
+template <int KB>
+__device__ __forceinline__ void fetch_tile(const uint8_t* __restrict__ packed, int64_t n, int64_t e0, uint2* raw) {
 #pragma unroll
-  for (int u = 0; u < kUnits; ++u) {
-    const int64_t e = (((int64_t)blockIdx.x * kUnits + u) * kThreads + tid) * 8;
+  for (int u = 0; u < Tile<KB>::kUnits; ++u) {
+    const int64_t e = e0 + (int64_t)(u * kThreads + threadIdx.x) * 8;
+    raw[u] = e < n ? fetch_codes<KB>(packed, e, n) : make_uint2(0, 0);
+  }
+}
+
+// Scales and stores the lane's units.
+template <int DT, int KB>
+__device__ __forceinline__ void emit_tile(const uint2* raw, int64_t n, int log2b, int64_t e0, const float* s_c,
+                                          const float* s_a, uint8_t* __restrict__ out) {
+  const int64_t b0 = e0 >> log2b;
+#pragma unroll
+  for (int u = 0; u < Tile<KB>::kUnits; ++u) {
+    const int64_t e = e0 + (int64_t)(u * kThreads + threadIdx.x) * 8;
     if (e >= n) break;
     uint32_t q[8];
-    load_codes<KB>(packed, e, n, q);
-    const float a = absmax[e >> log2b];
+    decode_codes<KB>(raw[u], q);
+    const float a = s_a[(int)((e >> log2b) - b0)];
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = s_c[q[i]] * a;
     if (e + 8 <= n) store8<DT>(out, e, v);
     else store_tail<DT>(out, e, v, (int)(n - e));
   }
+}
+
+template <int DT, int KB>
+__global__ __launch_bounds__(kThreads) void dequantize_kernel(const uint8_t* __restrict__ packed,
+                                                              const float* __restrict__ absmax, int64_t n,
+                                                              int log2b, uint8_t* __restrict__ out,
+                                                              DequantArgs da) {
+  __shared__ float s_c[256];
+  __shared__ float s_a[Tile<KB>::kBlocks];
+  const int tid = threadIdx.x;
+  const int64_t e0 = (int64_t)blockIdx.x * Tile<KB>::kElems;
+  uint2 raw[Tile<KB>::kUnits];
+  fetch_tile<KB>(packed, n, e0, raw);
+  s_c[tid] = tid < da.K ? da.c[tid] : 0.0f;
+  const int nblk = tile_blocks<KB>(e0, n, log2b);
+  for (int i = tid; i < nblk; i += kThreads) s_a[i] = absmax[(e0 >> log2b) + i];
+  __syncthreads();
+  emit_tile<DT, KB>(raw, n, log2b, e0, s_c, s_a, out);
 }
 
 template <int DT, int KB>
@@ -146,26 +193,40 @@ __global__ __launch_bounds__(kThreads) void dequantize_nested_kernel(
     NestedDequantArgs da) {
   __shared__ float s_c[256];
   __shared__ float s_c2[256];
+  constexpr int kPer = (Tile<KB>::kBlocks + kThreads - 1) / kThreads;  // blocks staged per thread
+  __shared__ float s_a[Tile<KB>::kBlocks];
   const int tid = threadIdx.x;
+  const int64_t e0 = (int64_t)blockIdx.x * Tile<KB>::kElems;
+  uint2 raw[Tile<KB>::kUnits];
+  fetch_tile<KB>(packed, n, e0, raw);
+  const int nblk = tile_blocks<KB>(e0, n, log2b);
+  uint32_t code2[kPer];
+  float a2[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = tid + k * kThreads;
+    code2[k] = 0;
+    a2[k] = 0.0f;
+    if (i < nblk) {
+      const int64_t b = (e0 >> log2b) + i;
+      code2[k] = q2[b];
+      a2[k] = absmax2[b >> log2b2];
+    }
+  }
   s_c[tid] = tid < da.K ? da.c[tid] : 0.0f;
   s_c2[tid] = da.c2[tid];
   const float m = *mean;
   __syncthreads();
 #pragma unroll
-  for (int u = 0; u < kUnits; ++u) {
-    const int64_t e = (((int64_t)blockIdx.x * kUnits + u) * kThreads + tid) * 8;
-    if (e >= n) break;
-    uint32_t q[8];
-    load_codes<KB>(packed, e, n, q);
-    const int64_t b = e >> log2b;
-    const float scaled = s_c2[q2[b]] * absmax2[b >> log2b2];
-    const float a = scaled + m;  // two roundings, no fused multiply-add
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = s_c[q[i]] * a;
-    if (e + 8 <= n) store8<DT>(out, e, v);
-    else store_tail<DT>(out, e, v, (int)(n - e));
+  for (int k = 0; k < kPer; ++k) {
+    const int i = tid + k * kThreads;
+    if (i < nblk) {
+      const float scaled = s_c2[code2[k]] * a2[k];
+      s_a[i] = scaled + m;  // two roundings, no fused multiply-add
+    }
   }
+  __syncthreads();
+  emit_tile<DT, KB>(raw, n, log2b, e0, s_c, s_a, out);
 }
 
 int ilog2(int v) {
@@ -177,7 +238,7 @@ int ilog2(int v) {
 template <int KB>
 hipError_t launch_dq(void* out, int dtype, int64_t n, int blocksize, const DequantArgs& a, const float* absmax,
                      const uint8_t* packed, hipStream_t s) {
-  const unsigned grid = (unsigned)((n + kTileElems - 1) / kTileElems);
+  const unsigned grid = (unsigned)((n + Tile<KB>::kElems - 1) / Tile<KB>::kElems);
   const int lb = ilog2(blocksize);
   uint8_t* o = static_cast<uint8_t*>(out);
   if (dtype == F32)
@@ -191,7 +252,7 @@ template <int KB>
 hipError_t launch_dqn(void* out, int dtype, int64_t n, int blocksize, int blocksize2, const NestedDequantArgs& a,
                       const uint8_t* q2, const float* absmax2, const float* mean, const uint8_t* packed,
                       hipStream_t s) {
-  const unsigned grid = (unsigned)((n + kTileElems - 1) / kTileElems);
+  const unsigned grid = (unsigned)((n + Tile<KB>::kElems - 1) / Tile<KB>::kElems);
   const int lb = ilog2(blocksize), lb2 = ilog2(blocksize2);
   uint8_t* o = static_cast<uint8_t*>(out);
   if (dtype == F32)
