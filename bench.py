@@ -111,22 +111,19 @@ STEP = ["quantize_nested", "dequantize_nested", "dequant_q32_q4", "dequant_q32_q
 
 
 def timed_step_loop(w: Workload, torch, steps: int):
-    """Runs `steps` steps with an event before and after every call; returns the elapsed ms
-    of the whole region and the per-call mean ms."""
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STEP) + 1)] for _ in range(steps)]
+    """Runs `steps` steps between two HIP events on the current stream (the stream every call
+    is enqueued on); returns the elapsed ms of the whole region and the host wall ms."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(steps):
-        evs[s][0].record()
-        for i, name in enumerate(STEP):
+    a.record()
+    for _ in range(steps):
+        for name in STEP:
             w.run(name)
-            evs[s][i + 1].record()
+    b.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
-    total = evs[0][0].elapsed_time(evs[-1][-1])
-    per = {name: sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)) / steps
-           for i, name in enumerate(STEP)}
-    return total, per, wall_ms
+    return a.elapsed_time(b), wall_ms
 
 
 def time_calls(fn, torch, reps: int) -> float:
@@ -274,8 +271,11 @@ def main():
     for _ in range(args.warmup):
         for name in STEP:
             w.run(name)
-    total_ms, per, wall_ms = timed_step_loop(w, torch, args.steps)
+    total_ms, wall_ms = timed_step_loop(w, torch, args.steps)
     ms_per_step = total_ms / args.steps
+    # Per-call breakdown: each call back to back between two events (an event between calls
+    # adds a few microseconds of its own).
+    per = {name: time_calls(lambda: w.run(name), torch, max(args.steps, 10)) for name in STEP}
     step_input = sum(w.calls[c]["inp"] for c in STEP)
     value = step_input / (ms_per_step / 1e3) / 1e9
     log("step %.3f ms (wall %.3f ms/step)" % (ms_per_step, wall_ms / args.steps))
@@ -288,7 +288,8 @@ def main():
                             rw_gbs=round(c["rw"] / ms / 1e6, 1), pct_hbm_peak=round(100 * c["rw"] / ms / 1e6 / PEAK_GBS, 1))
 
     # Roofline of the dominant kernel: the slower of the data quantize kernel (timed on its own,
-    # same launch as inside quantize_nested) and the nested dequantize kernel (one launch per call).
+    # same launch as inside quantize_nested) and the nested dequantize kernel (one launch per
+    # call), each as the mean over back-to-back launches between two HIP events.
     qk_ms = time_calls(lambda: w.run("quantize_kernel"), torch, max(args.steps, 10))
     n = w.N5
     q_bytes = 2 * n + n // 2 + 4 * w.nb

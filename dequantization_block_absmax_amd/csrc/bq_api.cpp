@@ -45,10 +45,14 @@ size_t ws_bytes(int64_t n, int64_t nb) {
   return ws_partials_offset(nb) + (size_t)((n + bq::kQuantTileElems - 1) / bq::kQuantTileElems) * 8;
 }
 
-// log2 of the 8192-element tiles each quantize workgroup processes: two tiles amortize the
-// LUT prologue once there are enough tiles to fill the GPU several times over (measured
-// best on MI355X for the 2^26 and 2^29 element workloads).
-int quantize_log2tiles(int64_t n) { return (n + bq::kQuantTileElems - 1) / bq::kQuantTileElems >= 4096 ? 1 : 0; }
+// log2 of the 8192-element tiles each quantize workgroup processes.  Two tiles amortize the
+// large LOG-mode LUT prologue once there are enough tiles to fill the GPU several times over;
+// with the small LIN and SEARCH prologues one tile per workgroup is faster (measured on
+// MI355X: 2^26 bf16 8-bit 44.6 against 45.8 us; 2^29 bf16 4-bit 231 against 249 us).
+int quantize_log2tiles(int64_t n, const bq::PreparedTable& t) {
+  const int64_t tiles = (n + bq::kQuantTileElems - 1) / bq::kQuantTileElems;
+  return t.mode == bq::LOG && tiles >= 4096 ? 1 : 0;
+}
 
 // Preparing a table (validation, thresholds, bucket LUT) costs more host time than a small
 // launch, so the last few prepared tables are kept, keyed by their entries.  This is a
@@ -138,7 +142,7 @@ bq_status bq_quantize_blockwise(const void* in, bq_dtype dtype, int64_t n, int32
   if (nblocks(n, blocksize) > INT32_MAX) return BQ_ERR_SIZE;
   if (!aligned(in, 16) || !aligned(packed, 16) || !aligned(absmax, 4)) return BQ_ERR_ALIGNMENT;
   return hip_status(bq::launch_quantize(in, dtype, n, blocksize, t.data, absmax, packed, nullptr,
-                                        quantize_log2tiles(n), stream));
+                                        quantize_log2tiles(n, t.data), stream));
 }
 
 bq_status bq_dequantize_blockwise(void* out, bq_dtype dtype, int64_t n, int32_t blocksize,
@@ -203,7 +207,7 @@ bq_status bq_quantize_nested(const void* in, bq_dtype dtype, int64_t n, int32_t 
   if (!aligned(in, 16) || !aligned(packed, 16)) return BQ_ERR_ALIGNMENT;
   float* ws_absmax = static_cast<float*>(stats->workspace);
   double* ws_partials = reinterpret_cast<double*>(static_cast<uint8_t*>(stats->workspace) + ws_partials_offset(nb));
-  const int lt = quantize_log2tiles(n);
+  const int lt = quantize_log2tiles(n, t.data);
   int e = bq::launch_quantize(in, dtype, n, blocksize, t.data, ws_absmax, packed, ws_partials, lt, stream);
   if (e != 0) return hip_status(e);
   e = bq::launch_nested_stats(ws_absmax, nb, stats->blocksize2, t.stats, ws_partials, bq::quantize_grid(n, lt),

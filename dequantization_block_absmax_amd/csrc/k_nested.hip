@@ -9,11 +9,13 @@
 //
 // The data quantize kernel already writes, per workgroup, the pairwise sum of its blocks'
 // maxima: an aligned subtree of 2^k leaves of the mean's tree (blocks past n hold +0, and
-// x + 0 = x, so padding never changes a sum).  Two kernels finish the statistics:
-//   run_sum_kernel, mean_kernel: continue the same tree over the per-workgroup partials;
-//   stats_kernel: one wave per 2048 or 4096 blocks (4 consecutive per lane per run of 256),
-//                 the same absmax / guard / LUT search as the data kernel, writing q2 and
-//                 the group maxima.
+// x + 0 = x, so padding never changes a sum).  Then:
+//   run_sum_kernel: sums runs of 2048 partials in place (more than 512 partials);
+//   mean_kernel:    finishes the tree (only when more than 512 run sums remain);
+//   stats_kernel:   finishes the tree itself otherwise (each workgroup, the same bits), then
+//                   one wave per 2048 or 4096 blocks (4 consecutive per lane per run of 256)
+//                   takes the same absmax / guard / LUT search as the data kernel and writes
+//                   q2 and the group maxima.
 #include <hip/hip_runtime.h>
 
 #include "bq_device.h"
@@ -57,6 +59,27 @@ __device__ __forceinline__ double wave_tree(const double* __restrict__ leaves, i
   for (int m = 1; m < 64; m <<= 1) s = s + __shfl_xor(s, m);
   return s;
 }
+
+// The same tree over at most 512 leaves leaves[i * stride] (lane l adds leaves [8l, 8l+8) as
+// a 3-level tree; the butterfly adds aligned runs of 8 .. 512), with a quarter of the registers.
+__device__ __forceinline__ double wave_tree512(const double* __restrict__ leaves, int64_t stride, int64_t count,
+                                               int lane) {
+  double v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t j = (int64_t)lane * 8 + i;
+    v[i] = j < count ? leaves[j * stride] : 0.0;
+  }
+#pragma unroll
+  for (int width = 8; width > 1; width >>= 1)
+#pragma unroll
+    for (int i = 0; i < width / 2; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+  double s = v[0];
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) s = s + __shfl_xor(s, m);
+  return s;
+}
+constexpr int64_t kFusedLeaves = 512;  // leaves the statistics kernel sums itself
 
 // First level over many per-workgroup partial sums: wave w replaces leaf 2048w by the sum of
 // leaves [2048w, 2048w + 2048), an aligned subtree of the same tree (it reads its whole run
@@ -121,12 +144,14 @@ __global__ __launch_bounds__(kMeanThreads) void mean_kernel(const double* __rest
 // wave's loads are issued before the LUT prologue.
 template <int MODE, int M, int KR>
 __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict__ absmax, int64_t nb,
-                                                         const float* __restrict__ mean, int log2b2,
+                                                         const double* __restrict__ leaves, int64_t stride,
+                                                         int64_t count, float* __restrict__ mean, int log2b2,
                                                          int64_t ngroups, uint8_t* __restrict__ q2,
                                                          float* __restrict__ absmax2, QuantArgs qa) {
   using E = typename Entry<M>::type;
   __shared__ float s_thr[260];
   __shared__ E s_lut[LutLayout<MODE, M>::kSize];
+  __shared__ float s_mean;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int B2 = 1 << log2b2;
@@ -148,9 +173,19 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
       if (b + 2 < nb) v[r].z = absmax[b + 2];
     }
   }
-  build_lut<MODE, M, kThreads>(qa, s_lut, s_thr, tid);
+  // With count > 0 every workgroup finishes the mean's tree itself (count <= 512 leaves, the
+  // same bits in every workgroup); workgroup 0 stores it.  With count == 0 the mean is read.
+  if (count > 0 && tid < 64) {
+    const double S = wave_tree512(leaves, stride, count, tid);
+    if (tid == 0) {
+      const float mv = (float)(S / (double)nb);
+      s_mean = mv;
+      if (blockIdx.x == 0) *mean = mv;
+    }
+  }
+  build_lut<MODE, M, kThreads>(qa, s_lut, s_thr, tid);  // ends with a barrier: s_mean is visible
   if (!active) return;  // whole waves
-  const float m = *mean;
+  const float m = count > 0 ? s_mean : *mean;
 
   // d = a - mean; blocks past nb contribute nothing to a group maximum.
   uint32_t key[KR];
@@ -206,16 +241,17 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
 }
 
 template <int MODE, int M>
-hipError_t launch_stats(const float* absmax, int64_t nb, const float* mean, int log2b2, int64_t ngroups,
-                        uint8_t* q2, float* absmax2, const QuantArgs& qa, hipStream_t s) {
+hipError_t launch_stats(const float* absmax, int64_t nb, const double* leaves, int64_t stride, int64_t count,
+                        float* mean, int log2b2, int64_t ngroups, uint8_t* q2, float* absmax2, const QuantArgs& qa,
+                        hipStream_t s) {
   if (log2b2 > 11) {
     const int64_t grid = (nb + 4 * 256 * 16 - 1) / (4 * 256 * 16);
-    return launch_kernel(stats_kernel<MODE, M, 16>, dim3((unsigned)grid), dim3(kThreads), s, absmax, nb, mean,
-                         log2b2, ngroups, q2, absmax2, qa);
+    return launch_kernel(stats_kernel<MODE, M, 16>, dim3((unsigned)grid), dim3(kThreads), s, absmax, nb, leaves,
+                         stride, count, mean, log2b2, ngroups, q2, absmax2, qa);
   }
   const int64_t grid = (nb + 4 * 256 * 8 - 1) / (4 * 256 * 8);
-  return launch_kernel(stats_kernel<MODE, M, 8>, dim3((unsigned)grid), dim3(kThreads), s, absmax, nb, mean,
-                       log2b2, ngroups, q2, absmax2, qa);
+  return launch_kernel(stats_kernel<MODE, M, 8>, dim3((unsigned)grid), dim3(kThreads), s, absmax, nb, leaves, stride,
+                       count, mean, log2b2, ngroups, q2, absmax2, qa);
 }
 
 }  // namespace
@@ -224,34 +260,41 @@ int launch_nested_stats(const float* absmax, int64_t nb, int blocksize2, const P
                         double* partials, int64_t npart, uint8_t* q2, float* absmax2, float* mean,
                         void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // One workgroup reading many partials is bound by a single CU's bandwidth; above one run,
-  // runs of 2048 are first summed in place by one wave each.
+  // Above 512 partial sums, runs of 2048 are first summed in place by one wave each (one
+  // workgroup reading them all would be bound by a single CU's bandwidth).  Up to 512 leaves
+  // remain, the statistics kernel finishes the tree itself; beyond, mean_kernel does.
   hipError_t e;
-  double* leaves = const_cast<double*>(partials);
+  double* leaves = partials;
   int64_t stride = 1, count = npart;
-  if (npart > kWaveLeaves) {
+  if (npart > kFusedLeaves) {
     const int64_t runs = (npart + kWaveLeaves - 1) / kWaveLeaves;
     e = launch_kernel(run_sum_kernel, dim3((unsigned)runs), dim3(64), s, leaves, npart);
     if (e != hipSuccess) return (int)e;
     stride = kWaveLeaves;
     count = runs;
   }
-  e = launch_kernel(mean_kernel, dim3(1), dim3(kMeanThreads), s, (const double*)leaves, stride, count, nb, mean);
-  if (e != hipSuccess) return (int)e;
+  if (count > kFusedLeaves) {
+    e = launch_kernel(mean_kernel, dim3(1), dim3(kMeanThreads), s, (const double*)leaves, stride, count, nb, mean);
+    if (e != hipSuccess) return (int)e;
+    count = 0;
+  }
   int log2b2 = 0;
   while ((1 << log2b2) < blocksize2) ++log2b2;
   const int64_t ngroups = (nb + blocksize2 - 1) / blocksize2;
   const QuantArgs& qa = t2.qa;
+  auto go = [&](auto kernel_launcher) {
+    return kernel_launcher(absmax, nb, leaves, stride, count, mean, log2b2, ngroups, q2, absmax2, qa, s);
+  };
   if (t2.mode == LIN) {
-    if (t2.M <= 1) e = launch_stats<LIN, 1>(absmax, nb, mean, log2b2, ngroups, q2, absmax2, qa, s);
-    else if (t2.M == 2) e = launch_stats<LIN, 2>(absmax, nb, mean, log2b2, ngroups, q2, absmax2, qa, s);
-    else e = launch_stats<LIN, 3>(absmax, nb, mean, log2b2, ngroups, q2, absmax2, qa, s);
+    if (t2.M <= 1) e = go(launch_stats<LIN, 1>);
+    else if (t2.M == 2) e = go(launch_stats<LIN, 2>);
+    else e = go(launch_stats<LIN, 3>);
   } else if (t2.mode == LOG) {
-    if (t2.M <= 1) e = launch_stats<LOG, 1>(absmax, nb, mean, log2b2, ngroups, q2, absmax2, qa, s);
-    else if (t2.M == 2) e = launch_stats<LOG, 2>(absmax, nb, mean, log2b2, ngroups, q2, absmax2, qa, s);
-    else e = launch_stats<LOG, 3>(absmax, nb, mean, log2b2, ngroups, q2, absmax2, qa, s);
+    if (t2.M <= 1) e = go(launch_stats<LOG, 1>);
+    else if (t2.M == 2) e = go(launch_stats<LOG, 2>);
+    else e = go(launch_stats<LOG, 3>);
   } else {
-    e = launch_stats<SEARCH, 1>(absmax, nb, mean, log2b2, ngroups, q2, absmax2, qa, s);
+    e = go(launch_stats<SEARCH, 1>);
   }
   return (int)e;
 }

@@ -282,6 +282,41 @@ def test_nested_mean_tree_shapes(dev, o):
         assert np.float32(r["mean"].item()).view(np.uint32) == np.float32(m_ref).view(np.uint32), nb
 
 
+def test_nested_mean_many_runs(dev, o):
+    """2^33 + 3 * 2^23 fp16 elements in blocks of 32: 1,051,648 per-workgroup partial sums, so
+    514 runs of 2048 remain and the separate mean kernel finishes the tree.  Only block heads
+    are nonzero, so the oracle needs just the 2^28 + 3 * 2^18 block maxima; sampled groups of
+    q2 / absmax2 are checked one by one."""
+    B, B2 = 32, 256
+    n = (1 << 33) + 3 * (1 << 23)
+    nb = n // B
+    rng = np.random.default_rng(5)
+    heads = (np.abs(rng.normal(0, 1, nb)) * 2.0 ** rng.integers(-12, 12, nb)).astype(np.float16)
+    heads_f32 = heads.astype(np.float32)
+    x = torch.zeros(n, dtype=torch.float16, device=dev)
+    x[::B] = torch.from_numpy(heads).to(dev)
+    t16, t256 = synth.table16(), synth.table256()
+    ng = nb // B2
+    ws_bytes = bq.bq_nested_workspace_bytes(n, B, B2)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    q2 = torch.empty(nb, dtype=torch.uint8, device=dev)
+    absmax2 = torch.empty(ng, dtype=torch.float32, device=dev)
+    mean = torch.full((1,), float("nan"), dtype=torch.float32, device=dev)
+    packed = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+    stats = bq.nested_stats(q2, absmax2, mean, t256, B2, ws, ws_bytes)
+    bq.check(bq.bq_quantize_nested(x, BQ_DT["float16"], n, B, t16, stats, packed), "quantize_nested")
+    del x, packed
+    m_ref = o.nested_mean(heads_f32)
+    assert np.float32(mean.item()).view(np.uint32) == np.float32(m_ref).view(np.uint32)
+    table = np.float32(t256)
+    for g in (0, 1, ng // 2, ng - 1):
+        d = (heads_f32[g * B2:(g + 1) * B2] - m_ref).astype(np.float32)
+        a2 = np.float32(np.abs(d).max())
+        assert np.float32(absmax2[g].item()).view(np.uint32) == a2.view(np.uint32), g
+        want = [o.nearest(o.normalize(v, a2), table) for v in d]
+        assert q2[g * B2:(g + 1) * B2].cpu().numpy().tolist() == want, g
+
+
 # ---- the five benchmark workloads ----------------------------------------------------------
 
 def test_c1_fp32_blocksize64(dev, o):
