@@ -41,8 +41,9 @@ int64_t nblocks(int64_t n, int32_t b) { return (n + b - 1) / b; }
 // workgroup (at most one per 8192-element tile).
 size_t ws_partials_offset(int64_t nb) { return ((size_t)nb * 4 + 255) & ~(size_t)255; }
 
+// absmax[nb] (fp32), padded to 256 bytes, then the quantize launch's partial sums (fp64).
 size_t ws_bytes(int64_t n, int64_t nb) {
-  return ws_partials_offset(nb) + (size_t)((n + bq::kQuantTileElems - 1) / bq::kQuantTileElems) * 8;
+  return ws_partials_offset(nb) + (size_t)bq::quantize_partials(n, bq::kMaxLog2Tiles, 32) * 8;
 }
 
 // log2 of the 8192-element tiles each quantize workgroup processes.  Two tiles amortize the
@@ -51,7 +52,7 @@ size_t ws_bytes(int64_t n, int64_t nb) {
 // MI355X: 2^26 bf16 8-bit 44.6 against 45.8 us; 2^29 bf16 4-bit 231 against 249 us).
 int quantize_log2tiles(int64_t n, const bq::PreparedTable& t) {
   const int64_t tiles = (n + bq::kQuantTileElems - 1) / bq::kQuantTileElems;
-  return t.mode == bq::LOG && tiles >= 4096 ? 1 : 0;
+  return t.mode == bq::LOG && tiles >= 4096 ? bq::kMaxLog2Tiles : 0;
 }
 
 // Preparing a table (validation, thresholds, bucket LUT) costs more host time than a small
@@ -210,7 +211,8 @@ bq_status bq_quantize_nested(const void* in, bq_dtype dtype, int64_t n, int32_t 
   const int lt = quantize_log2tiles(n, t.data);
   int e = bq::launch_quantize(in, dtype, n, blocksize, t.data, ws_absmax, packed, ws_partials, lt, stream);
   if (e != 0) return hip_status(e);
-  e = bq::launch_nested_stats(ws_absmax, nb, stats->blocksize2, t.stats, ws_partials, bq::quantize_grid(n, lt),
+  e = bq::launch_nested_stats(ws_absmax, nb, stats->blocksize2, t.stats, ws_partials,
+                              bq::quantize_partials(n, lt, blocksize),
                               stats->qabsmax, stats->absmax2, stats->mean, stream);
   return hip_status(e);
 }

@@ -7,8 +7,8 @@
 //   d_b   = fl32(a_b - mean);  per group of B2 blocks: a2_g = max |d_b|,
 //   q2_b  = nearest code of fl32(fl32(d_b * s) * fl32(1 / fl32(a2_g * s))) in the 256 table
 //
-// The data quantize kernel already writes, per workgroup, the pairwise sum of its blocks'
-// maxima: an aligned subtree of 2^k leaves of the mean's tree (blocks past n hold +0, and
+// The data quantize kernel already writes, per wave of 2048 elements, the pairwise sum of its
+// blocks' maxima: an aligned subtree of 2^k leaves of the mean's tree (blocks past n hold +0, and
 // x + 0 = x, so padding never changes a sum).  Then:
 //   run_sum_kernel: sums runs of 2048 partials in place (more than 512 partials);
 //   mean_kernel:    finishes the tree (only when more than 512 run sums remain);
@@ -24,7 +24,8 @@
 namespace bq {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // statistics workgroup
+constexpr int kWaves = kThreads / 64;
 constexpr int kMeanThreads = 1024;
 constexpr int kLeaves = 32;                 // sums per lane
 constexpr int kWaveLeaves = 64 * kLeaves;   // 2048: leaves per wave
@@ -81,7 +82,7 @@ __device__ __forceinline__ double wave_tree512(const double* __restrict__ leaves
 }
 constexpr int64_t kFusedLeaves = 512;  // leaves the statistics kernel sums itself
 
-// First level over many per-workgroup partial sums: wave w replaces leaf 2048w by the sum of
+// First level over many per-wave partial sums: wave w replaces leaf 2048w by the sum of
 // leaves [2048w, 2048w + 2048), an aligned subtree of the same tree (it reads its whole run
 // before lane 0 writes, and no other wave reads that run).
 __global__ __launch_bounds__(64) void run_sum_kernel(double* __restrict__ partials, int64_t npart) {
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(kMeanThreads) void mean_kernel(const double* __rest
 // One wave covers KR runs of 256 consecutive blocks (lane l holds blocks 4l..4l+3 of each run);
 // a group of B2 blocks is ceil(B2 / 256) whole runs, or B2 / 4 lanes of one run.  All of a
 // wave's loads are issued before the LUT prologue.
-template <int MODE, int M, int KR>
+template <int MODE, int M, int KR, bool kRoundwise>
 __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict__ absmax, int64_t nb,
                                                          const double* __restrict__ leaves, int64_t stride,
                                                          int64_t count, float* __restrict__ mean, int log2b2,
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
   const int B2 = 1 << log2b2;
   const int R = B2 > 256 ? B2 >> 8 : 1;       // runs per group
   const int lg = B2 >= 256 ? 64 : (B2 >> 2);  // lanes per group inside a run
-  const int64_t b0 = ((int64_t)blockIdx.x * (kThreads / 64) + (tid >> 6)) * 256 * KR + lane * 4;
+  const int64_t b0 = ((int64_t)blockIdx.x * kWaves + (tid >> 6)) * 256 * KR + lane * 4;
   const bool active = b0 - lane * 4 < nb;
 
   float4 v[KR];
@@ -187,43 +188,14 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
   if (!active) return;  // whole waves
   const float m = count > 0 ? s_mean : *mean;
 
-  // d = a - mean; blocks past nb contribute nothing to a group maximum.
-  uint32_t key[KR];
-#pragma unroll
-  for (int r = 0; r < KR; ++r) {
+  // Codes and q2 of run r, given the group maximum key of its blocks.
+  auto emit = [&](int r, uint32_t key, const float* d) {
     const int64_t b = b0 + r * 256;
-    float d[4] = {v[r].x - m, v[r].y - m, v[r].z - m, v[r].w - m};
-    key[r] = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (b + i < nb) key[r] = max(key[r], f32_bits(d[i]) & 0x7fffffffu);
-    v[r] = make_float4(d[0], d[1], d[2], d[3]);
-  }
-#pragma unroll
-  for (int r = 0; r < KR; ++r)
-    for (int k = 1; k < lg; k <<= 1) key[r] = max(key[r], (uint32_t)__shfl_xor((int)key[r], k));
-#pragma unroll
-  for (int st = 1; st < KR; st <<= 1)
-    if (st < R) {
-#pragma unroll
-      for (int r = 0; r < KR; ++r)
-        if ((r & st) == 0) {
-          const uint32_t k2 = max(key[r], key[r | st]);
-          key[r] = k2;
-          key[r | st] = k2;
-        }
-    }
-
-#pragma unroll
-  for (int r = 0; r < KR; ++r) {
-    const int64_t b = b0 + r * 256;
-    if (b >= nb) continue;
-    const float a2 = bits_f32(key[r]);
+    const float a2 = bits_f32(key);
     const int64_t g = b >> log2b2;
     if ((lane & (lg - 1)) == 0 && (r & (R - 1)) == 0 && g < ngroups) absmax2[g] = a2;
     const float s = a2 < 0x1p-64f ? 0x1p64f : (a2 > 0x1p64f ? 0x1p-64f : 1.0f);
     const float rc = 1.0f / (a2 * s);
-    const float d[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
     uint32_t w = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -237,6 +209,55 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
       for (int i = 0; i < 4; ++i)
         if (b + i < nb) q2[b + i] = (uint8_t)(w >> (8 * i));
     }
+  };
+
+  // d = a - mean; blocks past nb contribute nothing to a group maximum.
+  if constexpr (kRoundwise) {
+    // B2 <= 256: every group lies inside one run, so each run is finished as soon as its
+    // loads arrive, overlapping the codes of early runs with the loads of later ones.
+#pragma unroll
+    for (int r = 0; r < KR; ++r) {
+      const int64_t b = b0 + r * 256;
+      const float d[4] = {v[r].x - m, v[r].y - m, v[r].z - m, v[r].w - m};
+      uint32_t key = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (b + i < nb) key = max(key, f32_bits(d[i]) & 0x7fffffffu);
+      for (int k = 1; k < lg; k <<= 1) key = max(key, (uint32_t)__shfl_xor((int)key, k));
+      if (b < nb) emit(r, key, d);
+    }
+  } else {
+    uint32_t key[KR];
+#pragma unroll
+    for (int r = 0; r < KR; ++r) {
+      const int64_t b = b0 + r * 256;
+      float d[4] = {v[r].x - m, v[r].y - m, v[r].z - m, v[r].w - m};
+      key[r] = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (b + i < nb) key[r] = max(key[r], f32_bits(d[i]) & 0x7fffffffu);
+      v[r] = make_float4(d[0], d[1], d[2], d[3]);
+    }
+#pragma unroll
+    for (int r = 0; r < KR; ++r)
+      for (int k = 1; k < lg; k <<= 1) key[r] = max(key[r], (uint32_t)__shfl_xor((int)key[r], k));
+    // groups of R runs: an xor butterfly over run indices gives every run its group's maximum
+#pragma unroll
+    for (int st = 1; st < KR; st <<= 1)
+      if (st < R) {
+#pragma unroll
+        for (int r = 0; r < KR; ++r)
+          if ((r & st) == 0) {
+            const uint32_t k2 = max(key[r], key[r | st]);
+            key[r] = k2;
+            key[r | st] = k2;
+          }
+      }
+#pragma unroll
+    for (int r = 0; r < KR; ++r) {
+      const float d[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+      if (b0 + r * 256 < nb) emit(r, key[r], d);
+    }
   }
 }
 
@@ -244,14 +265,16 @@ template <int MODE, int M>
 hipError_t launch_stats(const float* absmax, int64_t nb, const double* leaves, int64_t stride, int64_t count,
                         float* mean, int log2b2, int64_t ngroups, uint8_t* q2, float* absmax2, const QuantArgs& qa,
                         hipStream_t s) {
-  if (log2b2 > 11) {
-    const int64_t grid = (nb + 4 * 256 * 16 - 1) / (4 * 256 * 16);
-    return launch_kernel(stats_kernel<MODE, M, 16>, dim3((unsigned)grid), dim3(kThreads), s, absmax, nb, leaves,
-                         stride, count, mean, log2b2, ngroups, q2, absmax2, qa);
-  }
-  const int64_t grid = (nb + 4 * 256 * 8 - 1) / (4 * 256 * 8);
-  return launch_kernel(stats_kernel<MODE, M, 8>, dim3((unsigned)grid), dim3(kThreads), s, absmax, nb, leaves, stride,
-                       count, mean, log2b2, ngroups, q2, absmax2, qa);
+  const int kr = log2b2 > 11 ? 16 : 8;  // runs per wave: a group (B2 / 256 runs) fits in a wave
+  const dim3 grid((unsigned)((nb + kWaves * 256 * kr - 1) / (kWaves * 256 * kr)));
+  if (log2b2 > 11)
+    return launch_kernel(stats_kernel<MODE, M, 16, false>, grid, dim3(kThreads), s, absmax, nb, leaves, stride,
+                         count, mean, log2b2, ngroups, q2, absmax2, qa);
+  if (log2b2 > 8)
+    return launch_kernel(stats_kernel<MODE, M, 8, false>, grid, dim3(kThreads), s, absmax, nb, leaves, stride,
+                         count, mean, log2b2, ngroups, q2, absmax2, qa);
+  return launch_kernel(stats_kernel<MODE, M, 8, true>, grid, dim3(kThreads), s, absmax, nb, leaves, stride, count,
+                       mean, log2b2, ngroups, q2, absmax2, qa);
 }
 
 }  // namespace

@@ -29,6 +29,15 @@ constexpr int kEPT = 32;
 constexpr int kTile = kThreads * kEPT;
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Non-temporal 16-byte store of the codes: they stream to memory without displacing the input
+// from the caches (2^29 bf16, 4-bit: 224 us against 234 us with ordinary stores on MI355X;
+// the same hint on the loads or the absmax stores measured slower).
+__device__ __forceinline__ void store16_nt(uint8_t* p, uint4 v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+}
 
 template <int DT>
 struct Traits {
@@ -70,6 +79,24 @@ __device__ __forceinline__ uint32_t chunk_key(const uint32_t* w) {
     }
     return max((uint32_t)acc.x, (uint32_t)acc.y);
   }
+}
+
+// Lane i receives lane i + M of its 16-lane row (M < 16; lanes past the row end get 0, and
+// their results are never used).
+template <int M>
+__device__ __forceinline__ double row_shl(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, 0x100 | M, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), 0x100 | M, 0xf, 0xf, true);
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// The value of lane `l` (wave-uniform).
+__device__ __forceinline__ double read_lane(double x, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
 // Block absmax (binary32) from the max key; +0 when the block has no finite element.
@@ -122,16 +149,14 @@ __device__ __forceinline__ int load_chunk(const uint8_t* __restrict__ in, int64_
 }
 
 struct QuantShared {
-  uint32_t red[kThreads / 64];
-  double wave[kThreads / 64];  // per-wave subtree sums of the nested mean
-  double stack[8];             // binary counter over the workgroup's tiles
+  uint32_t red[kThreads / 64];  // B = 4096: the two waves of a block exchange their keys
 };
 
-// Quantizes one lane chunk (tile t of the workgroup): block absmax, normalization, codes,
-// packing and stores; with `partials`, adds the tile's block maxima to the binary counter.
+// Quantizes one lane chunk: block absmax, normalization, codes, packing and stores; with
+// `partials`, also the pairwise sum of the block maxima of this wave's 2048 elements.
 template <int DT, int KB, int MODE, int M>
 __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, int64_t elem0, int64_t n, int log2g,
-                                               int t, float* __restrict__ absmax, uint8_t* __restrict__ packed,
+                                               float* __restrict__ absmax, uint8_t* __restrict__ packed,
                                                double* __restrict__ partials, const QuantArgs& qa,
                                                const typename Entry<M>::type* s_lut, const float* s_thr,
                                                QuantShared& sh, uint4* stage) {
@@ -154,22 +179,32 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, in
   if ((tid & (G - 1)) == 0 && blk < nb) absmax[blk] = a;
 
   if (partials != nullptr) {
-    // Pairwise sum of this tile's block maxima (an aligned subtree of the nested mean's tree;
-    // blocks past n hold +0).  Every lane of a block holds its absmax, so xor steps G, 2G,
-    // .., 32 add adjacent subtrees within the wave (commutative: both partners get the same
-    // bits); the four waves then combine as (w0 + w1) + (w2 + w3).
+    // Pairwise sum of the block maxima of this wave's 2048 elements: an aligned subtree of the
+    // nested mean's tree (blocks past n hold +0).  Lane i holds the sum of the subtree that
+    // starts at its block; each level adds the right neighbour subtree (lane i + m) to the left
+    // one, inside 16-lane rows by DPP row shifts, then across the four rows by lane reads.
+    // (Cross-lane shuffles through LDS made this chain long enough to slow the kernel by 4%.)
+    // Wave k of the grid writes partial k; with B = 4096 a block spans two waves and the
+    // first of the pair writes the block's absmax.
     double sum = (double)a;
-    for (int m = G; m < 64; m <<= 1) sum = sum + __shfl_xor(sum, m);
-    if (lane == 0) sh.wave[tid >> 6] = sum;
-    __syncthreads();
-    if (tid == 0) {
-      double tsum = G <= 64 ? (sh.wave[0] + sh.wave[1]) + (sh.wave[2] + sh.wave[3])
-                            : sh.wave[0] + sh.wave[2];  // B = 4096: waves 0-1 and 2-3 hold one block each
-      int lvl = 0;
-      for (int k = t; k & 1; k >>= 1, ++lvl) tsum = sh.stack[lvl] + tsum;
-      sh.stack[lvl] = tsum;
+    if (G <= 1) sum = sum + row_shl<1>(sum);
+    if (G <= 2) sum = sum + row_shl<2>(sum);
+    if (G <= 4) sum = sum + row_shl<4>(sum);
+    if (G <= 8) sum = sum + row_shl<8>(sum);
+    const double r0 = read_lane(sum, 0);
+    double wsum = r0;
+    if (G <= 32) {
+      const double r32 = read_lane(sum, 32);
+      if (G <= 16) {
+        const double r16 = read_lane(sum, 16), r48 = read_lane(sum, 48);
+        wsum = (r0 + r16) + (r32 + r48);
+      } else {
+        wsum = r0 + r32;
+      }
     }
-    __syncthreads();
+    const int64_t gw = elem0 >> 11;  // global wave index: 2048 elements per wave
+    const int per = G > 64 ? G >> 6 : 1;
+    if (lane == 0 && (gw & (per - 1)) == 0) partials[gw / per] = wsum;
   }
 
   // Normalize with the power-of-two guard; codes are packed into their output word as soon
@@ -228,16 +263,15 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, in
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    uint4* dst = reinterpret_cast<uint4*>(packed + wave_off);
-    dst[lane] = stage[lane];
-    dst[64 + lane] = stage[64 + lane];
+    uint8_t* dst = packed + wave_off;
+    store16_nt(dst + 16 * lane, stage[lane]);
+    store16_nt(dst + 16 * (64 + lane), stage[64 + lane]);
     __builtin_amdgcn_wave_barrier();  // the next tile's writes come after these reads
   } else if (KB == 4 && off + kBytes <= packed_bytes) {
-    *reinterpret_cast<uint4*>(packed + off) = make_uint4(o[0], o[1], o[2], o[3]);
+    store16_nt(packed + off, make_uint4(o[0], o[1], o[2], o[3]));
   } else if (KB == 8 && off + kBytes <= packed_bytes) {
-    uint4* dst = reinterpret_cast<uint4*>(packed + off);
-    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_uint4(o[4 % kOut], o[5 % kOut], o[6 % kOut], o[7 % kOut]);
+    store16_nt(packed + off, make_uint4(o[0], o[1], o[2], o[3]));
+    store16_nt(packed + off + 16, make_uint4(o[4 % kOut], o[5 % kOut], o[6 % kOut], o[7 % kOut]));
   } else if (off < packed_bytes) {
 #pragma unroll
     for (int i = 0; i < kBytes; ++i)
@@ -272,10 +306,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __res
       elem0 = ((tile0 + t) * kThreads + tid) * kEPT;
       nvalid = load_chunk<DT>(in, n, elem0, w);
     }
-    quantize_chunk<DT, KB, MODE, M>(w, nvalid, elem0, n, log2g, t, absmax, packed, partials, qa, s_lut, s_thr, sh,
+    quantize_chunk<DT, KB, MODE, M>(w, nvalid, elem0, n, log2g, absmax, packed, partials, qa, s_lut, s_thr, sh,
                                     stage);
   }
-  if (partials != nullptr && tid == 0) partials[blockIdx.x] = sh.stack[log2tiles];
 }
 
 template <int DT, int KB, int MODE, int M>
@@ -315,6 +348,11 @@ hipError_t launch_dt(const void* in, int64_t n, int log2g, int lt, float* absmax
 int quantize_grid(int64_t n, int log2tiles) {
   const int64_t tiles_total = (n + kTile - 1) / kTile;
   return (int)((tiles_total + (1 << log2tiles) - 1) >> log2tiles);
+}
+
+int64_t quantize_partials(int64_t n, int log2tiles, int blocksize) {
+  const int64_t waves = ((int64_t)quantize_grid(n, log2tiles) << log2tiles) * (kThreads / 64);
+  return blocksize == 4096 ? waves / 2 : waves;
 }
 
 int launch_quantize(const void* in, int dtype, int64_t n, int blocksize, const PreparedTable& t, float* absmax,

@@ -142,7 +142,7 @@ def test_workspace_bytes():
     assert bq.bq_nested_workspace_bytes(0, 64, 256) == 0
     for n, B in ((2**29, 64), (1000, 32), (8192 * 3 + 1, 4096)):
         nb = -(-n // B)
-        need = nb * 4 + (-(-n // 8192)) * 8  # fp32 block maxima + one fp64 partial sum per tile
+        need = nb * 4 + (-(-n // 2048)) * 8  # fp32 block maxima + one fp64 partial sum per wave
         ws = bq.bq_nested_workspace_bytes(n, B, 256)
         assert need <= ws < need + 512
 

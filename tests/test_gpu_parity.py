@@ -246,7 +246,8 @@ def gpu_nested(x: torch.Tensor, dtype: str, B: int, t16, t256, B2=256, out_dtype
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("B,B2", [(64, 256), (32, 32), (128, 64), (4096, 256), (256, 4096)])
+@pytest.mark.parametrize("B,B2", [(64, 256), (32, 32), (128, 64), (4096, 256), (256, 4096), (512, 32), (1024, 64),
+                                  (2048, 128)])
 def test_nested_full_parity(dev, o, dtype, B, B2):
     t16, t256 = synth.table16(), synth.table256()
     for n in (B * B2 * 3 + B * 7 + 5, 777, B * B2):
@@ -266,11 +267,11 @@ def test_nested_full_parity(dev, o, dtype, B, B2):
 
 
 def test_nested_mean_tree_shapes(dev, o):
-    """Block counts around powers of two and the per-workgroup partial-sum runs, with magnitudes
+    """Block counts around powers of two and the per-wave partial-sum runs, with magnitudes
     spread over many binades so that any other summation order would change the mean."""
     t16, t256 = synth.table16(), synth.table256()
     rng = np.random.default_rng(77)
-    # the last two give 2999 and 4121 per-workgroup partial sums: several ragged 2048-runs
+    # the last two give 11,995 and 32,961 per-wave partial sums: several ragged 2048-runs
     for nb in (1, 2, 255, 256, 257, 1023, 1024, 1025, 65536 + 1, 262144 + 256 * 3 + 1, 2999 * 256 - 77,
                2 * 4096 * 256 + 12345):
         heads = np.float32(np.abs(rng.normal(0, 1, nb)) * 2.0 ** rng.integers(-30, 30, nb))
@@ -283,8 +284,8 @@ def test_nested_mean_tree_shapes(dev, o):
 
 
 def test_nested_mean_many_runs(dev, o):
-    """2^33 + 3 * 2^23 fp16 elements in blocks of 32: 1,051,648 per-workgroup partial sums, so
-    514 runs of 2048 remain and the separate mean kernel finishes the tree.  Only block heads
+    """2^33 + 3 * 2^23 fp16 elements in blocks of 32: 4,206,592 per-wave partial sums, so 2054
+    runs of 2048 remain and the separate mean kernel finishes the tree.  Only block heads
     are nonzero, so the oracle needs just the 2^28 + 3 * 2^18 block maxima; sampled groups of
     q2 / absmax2 are checked one by one."""
     B, B2 = 32, 256
