@@ -46,13 +46,13 @@ size_t ws_bytes(int64_t n, int64_t nb) {
   return ws_partials_offset(nb) + (size_t)bq::quantize_partials(n, bq::kMaxLog2Tiles, 32) * 8;
 }
 
-// log2 of the 8192-element tiles each quantize workgroup processes.  Two tiles amortize the
-// large LOG-mode LUT prologue once there are enough tiles to fill the GPU several times over;
-// with the small LIN and SEARCH prologues one tile per workgroup is faster (measured on
-// MI355X: 2^26 bf16 8-bit 44.6 against 45.8 us; 2^29 bf16 4-bit 231 against 249 us).
+// log2 of the 8192-element tiles each quantize workgroup processes: two tiles amortize the
+// table prologue once there are enough tiles to fill the GPU several times over (measured on
+// MI355X: 2^29 bf16 4-bit 220 against 230 us; 2^26 bf16 8-bit 43.4 against 45.1 us).
 int quantize_log2tiles(int64_t n, const bq::PreparedTable& t) {
+  (void)t;
   const int64_t tiles = (n + bq::kQuantTileElems - 1) / bq::kQuantTileElems;
-  return t.mode == bq::LOG && tiles >= 4096 ? bq::kMaxLog2Tiles : 0;
+  return tiles >= 4096 ? bq::kMaxLog2Tiles : 0;
 }
 
 // Preparing a table (validation, thresholds, bucket LUT) costs more host time than a small

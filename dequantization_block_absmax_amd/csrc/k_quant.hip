@@ -148,6 +148,40 @@ __device__ __forceinline__ int load_chunk(const uint8_t* __restrict__ in, int64_
   return nvalid;
 }
 
+// The lane's 32 elements of a full wave, loaded through LDS: the wave reads its 2048 elements
+// as C rows of 64 x 16 bytes (one contiguous KiB per instruction, non-temporal: the input is
+// read once), stores the 16-byte chunks in element order and each lane reads back its own C
+// consecutive chunks.  Chunk q sits in slot q + q / C, which keeps the 16 lanes of every LDS
+// access phase on distinct banks for both the writes and the reads.  With per-lane
+// contiguous 16-byte loads straight from memory the kernel ran 7% slower on MI355X.
+template <int DT>
+__device__ __forceinline__ void load_chunk_lds(const uint8_t* __restrict__ in, int64_t wave0, int lane,
+                                               uint4* tr, uint32_t* w) {
+  constexpr int C = DT == F32 ? 8 : 4;  // 16-byte chunks per lane
+  const u32x4* src = reinterpret_cast<const u32x4*>(in + wave0 * (DT == F32 ? 4 : 2)) + lane;
+  u32x4 t[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) t[c] = __builtin_nontemporal_load(src + c * 64);
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int q = c * 64 + lane;
+    tr[q + q / C] = make_uint4(t[c].x, t[c].y, t[c].z, t[c].w);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    const int q = lane * C + i;
+    const uint4 x = tr[q + q / C];
+    w[4 * i] = x.x;
+    w[4 * i + 1] = x.y;
+    w[4 * i + 2] = x.z;
+    w[4 * i + 3] = x.w;
+  }
+  __builtin_amdgcn_wave_barrier();  // the next tile's writes come after these reads
+}
+
 struct QuantShared {
   uint32_t red[kThreads / 64];  // B = 4096: the two waves of a block exchange their keys
 };
@@ -296,15 +330,29 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __res
   const int tiles = 1 << log2tiles;
   const int64_t tile0 = (int64_t)blockIdx.x << log2tiles;
   // The first tile's loads are issued before the table prologue, so the two overlap.
+  // 4-bit codes load through LDS (see load_chunk_lds); 8-bit codes, whose LUT fills most of
+  // the LDS, load directly.
+  constexpr bool kViaLds = KB == 4;
+  constexpr int kTrChunks = DT == F32 ? 576 : 320;  // padded chunk slots per wave
+  __shared__ uint4 s_tr[kViaLds ? kThreads / 64 * kTrChunks : 1];
+  uint4* tr = s_tr + (kViaLds ? (tid >> 6) * kTrChunks : 0);
+  auto load = [&](int64_t e0, uint32_t* w) -> int {
+    const int64_t wave0 = e0 - (int64_t)(tid & 63) * kEPT;
+    if (kViaLds && wave0 + 64 * kEPT <= n) {  // uniform: the whole wave is in range
+      load_chunk_lds<DT>(in, wave0, tid & 63, tr, w);
+      return kEPT;
+    }
+    return load_chunk<DT>(in, n, e0, w);
+  };
   int64_t elem0 = (tile0 * kThreads + tid) * kEPT;
   uint32_t w[Tr::kWords];
-  int nvalid = load_chunk<DT>(in, n, elem0, w);
+  int nvalid = load(elem0, w);
   build_lut<MODE, M, kThreads>(qa, s_lut, s_thr, tid);
   uint4* stage = s_stage + (KB == 8 ? (tid >> 6) * 128 : 0);
   for (int t = 0; t < tiles; ++t) {
     if (t > 0) {
       elem0 = ((tile0 + t) * kThreads + tid) * kEPT;
-      nvalid = load_chunk<DT>(in, n, elem0, w);
+      nvalid = load(elem0, w);
     }
     quantize_chunk<DT, KB, MODE, M>(w, nvalid, elem0, n, log2g, absmax, packed, partials, qa, s_lut, s_thr, sh,
                                     stage);
