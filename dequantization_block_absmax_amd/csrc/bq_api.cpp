@@ -250,7 +250,7 @@ bq_status bq_dequant_q32(const void* blocks, bq_dtype dtype, int64_t n, int32_t 
   if (n == 0) return BQ_OK;
   if (blocks == nullptr || out == nullptr) return BQ_ERR_NULL;
   if (n / 32 > INT32_MAX) return BQ_ERR_SIZE;
-  if (!aligned(blocks, 16) || !aligned(out, 16)) return BQ_ERR_ALIGNMENT;
+  if (!aligned(blocks, 2) || !aligned(out, 16)) return BQ_ERR_ALIGNMENT;
   return hip_status(bq::launch_q32(blocks, dtype, n, (int)format, out, stream));
 }
 

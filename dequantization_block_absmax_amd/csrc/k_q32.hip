@@ -11,8 +11,8 @@
 //
 // Work decomposition: a unit is a quarter block (8 elements, 16 output bytes for bf16).
 // Lane `tid` of a 256-lane workgroup handles units tile*1024 + u*256 + tid, u = 0..3, so the
-// output stores of a wave are contiguous.  Blocks are only 2-byte aligned (18 and 34 bytes),
-// so the 8 payload bytes of a unit are read as 16-bit loads.
+// output stores of a wave are contiguous.  Blocks are only 2-byte aligned (18 and 34 bytes);
+// a tile's bytes are staged through LDS with 16-byte loads.
 #include <hip/hip_runtime.h>
 
 #include "bq_internal.h"
@@ -57,49 +57,90 @@ __device__ __forceinline__ void store8(uint8_t* out, int64_t e, const float* v) 
   }
 }
 
+// The 8 values of a unit (quarter block k) from its fp16 scale bits and 8 payload bytes.
+template <int FMT>
+__device__ __forceinline__ void unit_values(uint16_t dbits, uint32_t lo, uint32_t hi, int k, float* v) {
+  const float d = (float)__builtin_bit_cast(_Float16, dbits);
+  if constexpr (FMT == 0) {
+    const int sh = (k & 2) ? 4 : 0;  // units 0,1: low nibbles; units 2,3: high nibbles
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = (float)((int)((lo >> (8 * i + sh)) & 15u) - 8) * d;
+      v[4 + i] = (float)((int)((hi >> (8 * i + sh)) & 15u) - 8) * d;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = (float)(int)(int8_t)(lo >> (8 * i)) * d;
+      v[4 + i] = (float)(int)(int8_t)(hi >> (8 * i)) * d;
+    }
+  }
+}
+
+// Payload byte offset of unit k inside its block (after the 2-byte scale).
+template <int FMT>
+__device__ __forceinline__ int unit_offset(int k) {
+  return 2 + (FMT == 0 ? 8 * (k & 1) : 8 * k);
+}
+
+// A workgroup expands 256 blocks (8192 values).  When the tile is whole and the blocks are
+// 16-byte aligned, the tile's 4608 (Q4) or 8704 (Q8) bytes are read as contiguous 16-byte
+// chunks (non-temporal) into LDS, and every unit reads its scale and payload there: one
+// global load per 16 bytes instead of five 2-byte loads per unit (the records are only 2-byte
+// aligned).  Otherwise each unit reads its bytes from memory with 2-byte loads.
 template <int DT, int FMT>
 __global__ __launch_bounds__(kThreads) void q32_kernel(const uint8_t* __restrict__ blocks, int64_t n,
                                                        uint8_t* __restrict__ out) {
   constexpr int BS = FMT == 0 ? 18 : 34;
+  constexpr int kTileBlocks = kThreads * kUnits / 4;
+  constexpr int kChunks = kTileBlocks * BS / 16;
+  constexpr int kPer = (kChunks + kThreads - 1) / kThreads;
+  __shared__ uint4 s_raw[kChunks];
   const int tid = threadIdx.x;
-  // All loads of the lane's units first (n is a multiple of 32: units are whole).
-  int64_t unit[kUnits];
-  uint16_t dbits[kUnits];
-  uint32_t lo[kUnits], hi[kUnits];
+  const int64_t blk0 = (int64_t)blockIdx.x * kTileBlocks;
+  const bool staged = blk0 + kTileBlocks <= n / 32 && (reinterpret_cast<uintptr_t>(blocks) & 15) == 0;
+  if (staged) {  // uniform
+    const u32x4* src = reinterpret_cast<const u32x4*>(blocks + blk0 * BS);
+    u32x4 t[kPer];
 #pragma unroll
-  for (int u = 0; u < kUnits; ++u) {
-    unit[u] = ((int64_t)blockIdx.x * kUnits + u) * kThreads + tid;
-    if (unit[u] * 8 < n) {
-      const int k = (int)(unit[u] & 3);
-      const uint8_t* bp = blocks + (unit[u] >> 2) * BS;
-      dbits[u] = *reinterpret_cast<const uint16_t*>(bp);
-      const uint16_t* pay = reinterpret_cast<const uint16_t*>(bp + 2 + (FMT == 0 ? 8 * (k & 1) : 8 * k));
-      lo[u] = (uint32_t)pay[0] | ((uint32_t)pay[1] << 16);
-      hi[u] = (uint32_t)pay[2] | ((uint32_t)pay[3] << 16);
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + i * kThreads;
+      if (c < kChunks) t[i] = __builtin_nontemporal_load(src + c);
     }
-  }
 #pragma unroll
-  for (int u = 0; u < kUnits; ++u) {
-    if (unit[u] * 8 < n) {
-      const int k = (int)(unit[u] & 3);
-      const float d = (float)__builtin_bit_cast(_Float16, dbits[u]);
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + i * kThreads;
+      if (c < kChunks) s_raw[c] = make_uint4(t[i].x, t[i].y, t[i].z, t[i].w);
+    }
+    __syncthreads();
+    const uint16_t* raw = reinterpret_cast<const uint16_t*>(s_raw);
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      const int uu = u * kThreads + tid;  // unit in the tile
+      const int k = uu & 3;
+      const int h = (uu >> 2) * (BS / 2);  // the block's first halfword
+      const int p = h + unit_offset<FMT>(k) / 2;
+      const uint32_t lo = (uint32_t)raw[p] | ((uint32_t)raw[p + 1] << 16);
+      const uint32_t hi = (uint32_t)raw[p + 2] | ((uint32_t)raw[p + 3] << 16);
       float v[8];
-      if constexpr (FMT == 0) {
-        const int sh = (k & 2) ? 4 : 0;  // units 0,1: low nibbles; units 2,3: high nibbles
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[i] = (float)((int)((lo[u] >> (8 * i + sh)) & 15u) - 8) * d;
-          v[4 + i] = (float)((int)((hi[u] >> (8 * i + sh)) & 15u) - 8) * d;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[i] = (float)(int)(int8_t)(lo[u] >> (8 * i)) * d;
-          v[4 + i] = (float)(int)(int8_t)(hi[u] >> (8 * i)) * d;
-        }
-      }
-      store8<DT>(out, unit[u] * 8, v);
+      unit_values<FMT>(raw[h], lo, hi, k, v);
+      store8<DT>(out, ((int64_t)blockIdx.x * kUnits * kThreads + uu) * 8, v);
     }
+    return;
+  }
+  // n is a multiple of 32: units are whole.
+#pragma unroll
+  for (int u = 0; u < kUnits; ++u) {
+    const int64_t unit = ((int64_t)blockIdx.x * kUnits + u) * kThreads + tid;
+    if (unit * 8 >= n) break;
+    const int k = (int)(unit & 3);
+    const uint8_t* bp = blocks + (unit >> 2) * BS;
+    const uint16_t* pay = reinterpret_cast<const uint16_t*>(bp + unit_offset<FMT>(k));
+    const uint32_t lo = (uint32_t)pay[0] | ((uint32_t)pay[1] << 16);
+    const uint32_t hi = (uint32_t)pay[2] | ((uint32_t)pay[3] << 16);
+    float v[8];
+    unit_values<FMT>(*reinterpret_cast<const uint16_t*>(bp), lo, hi, k, v);
+    store8<DT>(out, unit * 8, v);
   }
 }
 

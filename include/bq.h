@@ -141,7 +141,8 @@ typedef enum { BQ_Q32_Q4 = 0, BQ_Q32_Q8 = 1 } bq_q32_format;
 /* Dequantizes n / 32 consecutive blocks (row-major rows of row_len elements; row_len a
  * multiple of 32 dividing n, so no block straddles a row: the per-row alignment check of
  * "[OMNIML-5899] Add CUDA kernels for IQ packing").
- *   blocks  [device] (n / 32) * 18 or * 34 bytes, 16-byte aligned.
+ *   blocks  [device] (n / 32) * 18 or * 34 bytes, 2-byte aligned (the records themselves are;
+ *           a slice starting at any block is accepted; 16-byte aligned arrays are read faster).
  *   out     [device] out: n elements of `dtype`. */
 bq_status bq_dequant_q32(const void* blocks, bq_dtype dtype, int64_t n, int32_t row_len,
                          bq_q32_format format, void* out, hipStream_t stream);

@@ -163,7 +163,7 @@ def test_q32_validation():
     assert call(n=0) == bq.BQ_OK
     assert call(blocks=None) == bq.BQ_ERR_NULL
     assert call(out=None) == bq.BQ_ERR_NULL
-    assert call(blocks=FAKE + 2) == bq.BQ_ERR_ALIGNMENT
+    assert call(blocks=FAKE + 1) == bq.BQ_ERR_ALIGNMENT  # records are 2-byte aligned
 
 
 # ---- host table preparation vs the oracle ------------------------------------------------

@@ -374,6 +374,26 @@ def test_c3_bf16_8bit_blocksize4096(dev, o):
 
 
 @pytest.mark.parametrize("fmt", ["q4", "q8"])
+def test_q32_partial_tile_and_offset(dev, o, fmt):
+    """Whole 256-block tiles go through LDS with 16-byte loads; a partial last tile and a block
+    array that is not 16-byte aligned (it starts one 18- or 34-byte block into a buffer) take
+    the 2-byte-load path.  Both must give the same values."""
+    bs = 18 if fmt == "q4" else 34
+    f = bq.BQ_Q32_Q4 if fmt == "q4" else bq.BQ_Q32_Q8
+    of = oracle.Q4 if fmt == "q4" else oracle.Q8
+    nblk = 256 * 5 + 77
+    buf = synth.q32_blocks(nblk + 1, fmt, seed=9, device=dev)
+    for start in (0, 1):  # in blocks: the second view is only 2-byte aligned
+        blocks = buf[start * bs:(start + nblk) * bs]
+        n = nblk * 32
+        for odt in ("bfloat16", "float32"):
+            out = torch.empty(n, dtype=TORCH_DT[odt], device=dev)
+            bq.check(bq.bq_dequant_q32(blocks, BQ_DT[odt], n, 32, f, out))
+            ref = o.dequant_q32(blocks.cpu().numpy(), n, 32, of, ORACLE_DT[odt])
+            assert_out_equal(out, ref, n, odt, "q32 %s start=%d %s" % (fmt, start, odt))
+
+
+@pytest.mark.parametrize("fmt", ["q4", "q8"])
 def test_c4_gguf_4096x14336(dev, o, fmt):
     rows, cols = 4096, 14336
     n = rows * cols
