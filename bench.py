@@ -233,8 +233,8 @@ def cpu_baseline(w: Workload, torch):
 
     import oracle
     o = oracle.Oracle()
-    n5 = 1 << 26
-    rows = 1024
+    n5 = 1 << 27
+    rows = 2048
     xs = w.x[:n5].cpu().view(torch.int16).numpy().view(np.uint16)
     m4 = rows * w.COLS
     b4 = w.q4[: m4 // 32 * 18].cpu().numpy()
@@ -249,8 +249,8 @@ def cpu_baseline(w: Workload, torch):
     nb = n5 // w.B5
     inp = 2 * n5 + (n5 // 2 + nb + 4 * (-(-nb // w.B2)) + 4) + b4.size + b8.size
     return dict(value=round(inp / dt / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                sample="first 2^26 elements of the 2^29 bf16 tensor (nested quantize + dequantize) and the first "
-                       "1024 of 4096 rows of both GGUF matrices; %.1f s single-threaded" % dt)
+                sample="first 2^27 elements of the 2^29 bf16 tensor (nested quantize + dequantize) and the first "
+                       "2048 of 4096 rows of both GGUF matrices; %.1f s single-threaded" % dt)
 
 
 def main():
