@@ -184,7 +184,10 @@ def detail_configs(bq, synth, torch, dev, peak):
     out = {}
     t16, t256 = bq.code_table(synth.table16()), bq.code_table(synth.table256())
 
-    def rotate(make, footprint, fn, reps):
+    def rotate(make, footprint, fn, reps, graph=False):
+        """Mean ms per call over buffer sets rotated past the last-level cache; with graph,
+        also the mean ms per call when the k calls are captured once as a HIP graph and
+        replayed (no per-call launch cost from the host)."""
         k = max(1, min(64, -(-(1 << 30) // footprint)))
         sets = [make() for _ in range(k)]
         i = [0]
@@ -192,11 +195,31 @@ def detail_configs(bq, synth, torch, dev, peak):
         def call():
             fn(sets[i[0] % k])
             i[0] += 1
-        return time_calls(call, torch, reps)
+        ms = time_calls(call, torch, reps)
+        if not graph:
+            return ms, None
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for st in sets:
+                fn(st)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for st in sets:
+                fn(st)
+        replays = max(1, reps // k)
+        gms = time_calls(g.replay, torch, replays) / k
+        del g
+        return ms, gms
 
-    def rec(name, ms, inp, rw):
+    def rec(name, ms, inp, rw, graph_ms=None):
         out[name] = dict(us=round(ms * 1e3, 2), input_gbs=round(inp / ms / 1e6, 1), rw_gbs=round(rw / ms / 1e6, 1),
                          pct_hbm_peak=round(100 * rw / ms / 1e6 / peak, 1))
+        if graph_ms is not None:  # the same calls replayed from a HIP graph
+            out[name].update(us_graph=round(graph_ms * 1e3, 2),
+                             pct_hbm_peak_graph=round(100 * rw / graph_ms / 1e6 / peak, 1))
 
     def blockwise(tag, n, dtype, B, table, seed, std, p_out=0.0, p_nf=0.0, reps=50):
         es = {"float32": 4, "float16": 2, "bfloat16": 2}[dtype]
@@ -211,14 +234,18 @@ def detail_configs(bq, synth, torch, dev, peak):
             return dict(x=x0.clone(), a=torch.empty(nb, dtype=torch.float32, device=dev),
                         p=torch.empty(pb + 16, dtype=torch.uint8, device=dev), o=torch.empty(n, dtype=tdt, device=dev))
         foot = n * es * 2 + pb + nb * 4
-        qms = rotate(make, foot, lambda s: bq.check(bq.bq_quantize_blockwise(s["x"], code, n, B, table, s["a"], s["p"])), reps)
+        small = n * es < (64 << 20)  # launch-bound sizes: also time them replayed from a graph
+        qms, qg = rotate(make, foot, lambda s: bq.check(bq.bq_quantize_blockwise(s["x"], code, n, B, table, s["a"],
+                                                                                 s["p"])), reps, small)
         sets_once = make()
         bq.check(bq.bq_quantize_blockwise(sets_once["x"], code, n, B, table, sets_once["a"], sets_once["p"]))
-        dms = rotate(lambda: dict(a=sets_once["a"].clone(), p=sets_once["p"].clone(), o=torch.empty(n, dtype=tdt, device=dev)),
-                     foot, lambda s: bq.check(bq.bq_dequantize_blockwise(s["o"], code, n, B, table, s["a"], s["p"])), reps)
+        dms, dg = rotate(lambda: dict(a=sets_once["a"].clone(), p=sets_once["p"].clone(),
+                                      o=torch.empty(n, dtype=tdt, device=dev)),
+                         foot, lambda s: bq.check(bq.bq_dequantize_blockwise(s["o"], code, n, B, table, s["a"],
+                                                                             s["p"])), reps, small)
         rw = n * es + pb + nb * 4
-        rec(tag + " quantize", qms, n * es, rw)
-        rec(tag + " dequantize", dms, pb + nb * 4, rw)
+        rec(tag + " quantize", qms, n * es, rw, qg)
+        rec(tag + " dequantize", dms, pb + nb * 4, rw, dg)
 
     blockwise("C1 fp32 n=524288 B=64", 524288, "float32", 64, t16, 1, 1.0, reps=200)
     for B in (32, 64, 128, 256, 512, 1024, 2048, 4096):
