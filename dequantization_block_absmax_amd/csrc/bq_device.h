@@ -31,17 +31,26 @@ __device__ __forceinline__ uint32_t nearest_code(float y, const QuantArgs& qa,
     for (int step = qa.K >> 1; step >= 1; step >>= 1) q += (y >= s_thr[q + step - 1]) ? step : 0;
     return (uint32_t)q;
   } else {
-    uint32_t idx;
+    typename Entry<M>::type e;
     if constexpr (MODE == LIN) {
       float zz = __builtin_fmaf(y, kLinAlpha, kLinBeta);
       zz = fminf(fmaxf(zz, 0.0f), 1.0f);
-      idx = __builtin_amdgcn_ubfe(f32_bits(zz), (uint32_t)qa.sh, (uint32_t)(24 - qa.sh));
+      e = lut[__builtin_amdgcn_ubfe(f32_bits(zz), (uint32_t)qa.sh, (uint32_t)(24 - qa.sh))];
     } else {
-      uint32_t u = f32_bits(y);
-      uint32_t a = min(max(u & 0x7fffffffu, qa.lo), qa.hi);
-      idx = ((a - qa.lo) >> qa.sh) + ((u >> 31) ? (uint32_t)qa.nj : 0u);
+      // The same j as min(max(a, LO), HI) - LO >> SH, computed straight as a byte offset: LO
+      // and HI are multiples of 2^SH, so clearing the low SH bits of a first changes neither
+      // the clamp nor j, and (t - LO) >> (SH - log2 sizeof(entry)) is j * sizeof(entry).
+      constexpr int kLog2E = M == 1 ? 3 : 4;
+      const uint32_t u = f32_bits(y);
+      const uint32_t m = u & qa.log_mask;  // sign and the low SH bits cleared
+      uint32_t t;
+      asm("v_med3_u32 %0, %1, %2, %3" : "=v"(t) : "v"(m), "v"(qa.lo), "v"(qa.hi));
+      const int sh = qa.sh - kLog2E;
+      const uint32_t neg = (uint32_t)((int32_t)u >> 31) & ((uint32_t)qa.nj << kLog2E);
+      const uint32_t bias = 0u - (qa.lo >> sh);  // (t - LO) >> sh = (t >> sh) - (LO >> sh): LO is a multiple of 2^SH
+      const uint32_t off = (t >> sh) + neg + bias;
+      e = *reinterpret_cast<const typename Entry<M>::type*>(reinterpret_cast<const char*>(lut) + off);
     }
-    typename Entry<M>::type e = lut[idx];
     uint32_t q = e.x + (y >= bits_f32(e.y) ? 1u : 0u);
     if constexpr (M >= 2) q += (y >= bits_f32(e.z) ? 1u : 0u);
     if constexpr (M >= 3) q += (y >= bits_f32(e.w) ? 1u : 0u);

@@ -46,6 +46,7 @@ struct QuantArgs {
   // Bucket parameters.
   int32_t sh;               // LIN and LOG shift
   uint32_t lo, hi;          // LOG clamp bounds (bit patterns of |y|)
+  uint32_t log_mask;        // LOG: 0x7fffffff with the low SH bits cleared
   int32_t nj;               // LOG buckets per sign
 };
 

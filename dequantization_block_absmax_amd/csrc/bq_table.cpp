@@ -157,6 +157,7 @@ bool prepare_table(const float* entries, int size, PreparedTable* out) {
     qa.lo = best.lp.lo;
     qa.hi = best.lp.hi;
     qa.nj = best.lp.nj;
+    qa.log_mask = 0x7fffffffu & ~((1u << best.lp.sh) - 1u);
     qa.nbuckets = 2 * best.lp.nj;
     qa.special0 = best.lp.nj - 1;
     qa.special1 = 2 * best.lp.nj - 1;
