@@ -69,13 +69,23 @@ __device__ __forceinline__ uint32_t chunk_key(const uint32_t* w) {
     for (int i = 0; i < 32; ++i) k = max(k, (w[i] << 1) + 0x01000000u);
     return k;
   } else {
+    // Common case first: the max of 2|h| (the shift drops the sign), two packed operations per
+    // pair.  Only when that max is Inf/NaN (exponent all ones) is the key recomputed with the
+    // wrap that excludes non-finite elements; for finite elements both give 2|h| + off.
     constexpr unsigned short off = DT == BF16 ? 0x0100 : 0x0800;
+    constexpr uint32_t kNonFinite = DT == BF16 ? 0xff00u : 0xf800u;  // 2 * (bits of +Inf)
     u16x2 acc = {0, 0};
 #pragma unroll
+    for (int i = 0; i < 16; ++i)
+      acc = __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2, w[i]) << (u16x2){1, 1});
+    const uint32_t m = max((uint32_t)acc.x, (uint32_t)acc.y);
+    // wave-uniform, so the rare path is a branch the common case skips
+    if (__builtin_expect(__all(m < kNonFinite), 1)) return m + off;
+    acc = (u16x2){0, 0};
+#pragma unroll
     for (int i = 0; i < 16; ++i) {
-      u16x2 h = __builtin_bit_cast(u16x2, w[i]);
-      u16x2 k = h * (u16x2){2, 2} + (u16x2){off, off};  // one packed multiply-add per pair
-      acc = __builtin_elementwise_max(acc, k);
+      const u16x2 h = __builtin_bit_cast(u16x2, w[i]);
+      acc = __builtin_elementwise_max(acc, (h << (u16x2){1, 1}) + (u16x2){off, off});
     }
     return max((uint32_t)acc.x, (uint32_t)acc.y);
   }
@@ -271,7 +281,9 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, in
       o[i] = v;
     }
   }
-  if (nvalid < 32) {  // codes of elements past n are 0 (the pad nibble of an odd n)
+  // codes of elements past n are 0 (the pad nibble of an odd n); wave-uniform test, so full
+  // waves skip the masks instead of computing them
+  if (__builtin_expect(!__all(nvalid >= 32), 0)) {
 #pragma unroll
     for (int i = 0; i < kOut; ++i) {
       const int c = min(max(nvalid - i * kPer, 0), kPer);
@@ -329,7 +341,6 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __res
   const int tid = threadIdx.x;
   const int tiles = 1 << log2tiles;
   const int64_t tile0 = (int64_t)blockIdx.x << log2tiles;
-  // The first tile's loads are issued before the table prologue, so the two overlap.
   // 4-bit codes load through LDS (see load_chunk_lds); 8-bit codes, whose LUT fills most of
   // the LDS, load directly.
   constexpr bool kViaLds = KB == 4;
@@ -344,16 +355,21 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __res
     }
     return load_chunk<DT>(in, n, e0, w);
   };
-  int64_t elem0 = (tile0 * kThreads + tid) * kEPT;
-  uint32_t w[Tr::kWords];
-  int nvalid = load(elem0, w);
-  build_lut<MODE, M, kThreads>(qa, s_lut, s_thr, tid);
   uint4* stage = s_stage + (KB == 8 ? (tid >> 6) * 128 : 0);
-  for (int t = 0; t < tiles; ++t) {
-    if (t > 0) {
-      elem0 = ((tile0 + t) * kThreads + tid) * kEPT;
-      nvalid = load(elem0, w);
-    }
+  {
+    // The first tile apart from the others: its chunk is loaded before the table prologue,
+    // and giving each tile its own registers avoids copying them between loop iterations.
+    const int64_t elem0 = (tile0 * kThreads + tid) * kEPT;
+    uint32_t w[Tr::kWords];
+    const int nvalid = load(elem0, w);
+    build_lut<MODE, M, kThreads>(qa, s_lut, s_thr, tid);
+    quantize_chunk<DT, KB, MODE, M>(w, nvalid, elem0, n, log2g, absmax, packed, partials, qa, s_lut, s_thr, sh,
+                                    stage);
+  }
+  for (int t = 1; t < tiles; ++t) {
+    const int64_t elem0 = ((tile0 + t) * kThreads + tid) * kEPT;
+    uint32_t w[Tr::kWords];
+    const int nvalid = load(elem0, w);
     quantize_chunk<DT, KB, MODE, M>(w, nvalid, elem0, n, log2g, absmax, packed, partials, qa, s_lut, s_thr, sh,
                                     stage);
   }
