@@ -37,18 +37,16 @@ __device__ __forceinline__ uint32_t nearest_code(float y, const QuantArgs& qa,
       zz = fminf(fmaxf(zz, 0.0f), 1.0f);
       e = lut[__builtin_amdgcn_ubfe(f32_bits(zz), (uint32_t)qa.sh, (uint32_t)(24 - qa.sh))];
     } else {
-      // The same j as min(max(a, LO), HI) - LO >> SH, computed straight as a byte offset: LO
-      // and HI are multiples of 2^SH, so clearing the low SH bits of a first changes neither
-      // the clamp nor j, and (t - LO) >> (SH - log2 sizeof(entry)) is j * sizeof(entry).
+      // Byte offset of the entry, in five operations: LO and HI are multiples of 2^SH, so
+      // clamping |y| bits >> SH to [LO >> SH, HI >> SH] gives j + (LO >> SH); the sign picks the
+      // bias that removes LO >> SH and, for negative y, adds the NJ buckets of the positive side.
       constexpr int kLog2E = M == 1 ? 3 : 4;
       const uint32_t u = f32_bits(y);
-      const uint32_t m = u & qa.log_mask;  // sign and the low SH bits cleared
-      uint32_t t;
-      asm("v_med3_u32 %0, %1, %2, %3" : "=v"(t) : "v"(m), "v"(qa.lo), "v"(qa.hi));
-      const int sh = qa.sh - kLog2E;
-      const uint32_t neg = (uint32_t)((int32_t)u >> 31) & ((uint32_t)qa.nj << kLog2E);
-      const uint32_t bias = 0u - (qa.lo >> sh);  // (t - LO) >> sh = (t >> sh) - (LO >> sh): LO is a multiple of 2^SH
-      const uint32_t off = (t >> sh) + neg + bias;
+      uint32_t j = __builtin_amdgcn_ubfe(u, (uint32_t)qa.sh, (uint32_t)(31 - qa.sh));
+      asm("v_med3_u32 %0, %1, %2, %3" : "=v"(j) : "v"(j), "v"(qa.jlo), "v"(qa.jhi));
+      const uint32_t neg = (uint32_t)((int32_t)u >> 31);
+      const uint32_t bias = (neg & qa.log_nbias) | (~neg & qa.log_bias);
+      const uint32_t off = (j << kLog2E) + bias;
       e = *reinterpret_cast<const typename Entry<M>::type*>(reinterpret_cast<const char*>(lut) + off);
     }
     uint32_t q = e.x + (y >= bits_f32(e.y) ? 1u : 0u);

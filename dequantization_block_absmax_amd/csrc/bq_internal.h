@@ -46,8 +46,12 @@ struct QuantArgs {
   // Bucket parameters.
   int32_t sh;               // LIN and LOG shift
   uint32_t lo, hi;          // LOG clamp bounds (bit patterns of |y|)
-  uint32_t log_mask;        // LOG: 0x7fffffff with the low SH bits cleared
   int32_t nj;               // LOG buckets per sign
+  // LOG, as the kernels evaluate it: LUT byte offset = (clamp(|y| bits >> SH, jlo, jhi) << log2
+  // of the entry size) + (y negative ? log_nbias : log_bias), in modulo-2^32 arithmetic.
+  uint32_t jlo, jhi;        // LO >> SH, HI >> SH
+  uint32_t log_bias;        // -(jlo * entry size)
+  uint32_t log_nbias;       // log_bias + NJ * entry size
 };
 
 struct DequantArgs {

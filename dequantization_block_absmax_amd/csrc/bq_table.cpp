@@ -157,7 +157,11 @@ bool prepare_table(const float* entries, int size, PreparedTable* out) {
     qa.lo = best.lp.lo;
     qa.hi = best.lp.hi;
     qa.nj = best.lp.nj;
-    qa.log_mask = 0x7fffffffu & ~((1u << best.lp.sh) - 1u);
+    const int e = best.M == 1 ? 3 : 4;  // log2 of the LUT entry size (uint2 or uint4)
+    qa.jlo = qa.lo >> qa.sh;
+    qa.jhi = qa.hi >> qa.sh;
+    qa.log_bias = 0u - (qa.jlo << e);
+    qa.log_nbias = qa.log_bias + ((uint32_t)qa.nj << e);
     qa.nbuckets = 2 * best.lp.nj;
     qa.special0 = best.lp.nj - 1;
     qa.special1 = 2 * best.lp.nj - 1;
@@ -195,6 +199,11 @@ uint32_t host_nearest(const bq::PreparedTable& t, float y) {
     uint32_t u = f32_bits(y);
     uint32_t a = std::min(std::max(u & 0x7fffffffu, qa.lo), qa.hi);
     idx = ((a - qa.lo) >> qa.sh) + ((u >> 31) ? (uint32_t)qa.nj : 0u);
+    // The kernels' form of the same bucket: the LUT entry's byte offset.  A mismatch returns an
+    // impossible code, so the table tests fail.
+    const int e = t.M == 1 ? 3 : 4;
+    const uint32_t j = std::min(std::max((u & 0x7fffffffu) >> qa.sh, qa.jlo), qa.jhi);
+    if ((j << e) + ((u >> 31) ? qa.log_nbias : qa.log_bias) != idx << e) return 0xffffffffu;
   }
   if ((int)idx == qa.special0 || (int)idx == qa.special1) return (uint32_t)qa.z;
   uint32_t b = qa.base[idx];

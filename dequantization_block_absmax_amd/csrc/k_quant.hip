@@ -196,6 +196,19 @@ struct QuantShared {
   uint32_t red[kThreads / 64];  // B = 4096: the two waves of a block exchange their keys
 };
 
+// One output word from its codes, in byte order: eight 4-bit codes (the first element of a
+// pair in the high nibble) or four 8-bit codes.  The bytes are joined with byte permutes, one
+// operation per byte pair, where a chain of shifts and ORs is compiled into more operations.
+template <int KB>
+__device__ __forceinline__ uint32_t pack_word(const uint32_t* q) {
+  uint32_t b[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) b[k] = KB == 4 ? (q[2 * k] << 4) | q[2 * k + 1] : q[k];
+  const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);  // b0 | b1 << 8
+  const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);  // b2 | b3 << 8
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);                    // lo | hi << 16
+}
+
 // Quantizes one lane chunk: block absmax, normalization, codes, packing and stores; with
 // `partials`, also the pairwise sum of the block maxima of this wave's 2048 elements.
 template <int DT, int KB, int MODE, int M>
@@ -247,8 +260,8 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, in
       }
     }
     const int64_t gw = elem0 >> 11;  // global wave index: 2048 elements per wave
-    const int per = G > 64 ? G >> 6 : 1;
-    if (lane == 0 && (gw & (per - 1)) == 0) partials[gw / per] = wsum;
+    const int lper = log2g > 6 ? log2g - 6 : 0;  // log2 of the waves per block
+    if (lane == 0 && (gw & ((1 << lper) - 1)) == 0) partials[gw >> lper] = wsum;
   }
 
   // Normalize with the power-of-two guard; codes are packed into their output word as soon
@@ -261,24 +274,20 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, in
   if (s == 1.0f) {
 #pragma unroll
     for (int i = 0; i < kOut; ++i) {
-      uint32_t v = 0;
+      uint32_t q[kPer];
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const uint32_t q = nearest_code<MODE, M>(widen<DT>(w, i * kPer + j) * r, qa, s_lut, s_thr);
-        v |= KB == 4 ? q << (8 * (j >> 1) + 4 * (1 - (j & 1))) : q << (8 * j);
-      }
-      o[i] = v;
+      for (int j = 0; j < kPer; ++j)
+        q[j] = nearest_code<MODE, M>(widen<DT>(w, i * kPer + j) * r, qa, s_lut, s_thr);
+      o[i] = pack_word<KB>(q);
     }
   } else {
 #pragma unroll
     for (int i = 0; i < kOut; ++i) {
-      uint32_t v = 0;
+      uint32_t q[kPer];
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const uint32_t q = nearest_code<MODE, M>((widen<DT>(w, i * kPer + j) * s) * r, qa, s_lut, s_thr);
-        v |= KB == 4 ? q << (8 * (j >> 1) + 4 * (1 - (j & 1))) : q << (8 * j);
-      }
-      o[i] = v;
+      for (int j = 0; j < kPer; ++j)
+        q[j] = nearest_code<MODE, M>((widen<DT>(w, i * kPer + j) * s) * r, qa, s_lut, s_thr);
+      o[i] = pack_word<KB>(q);
     }
   }
   // codes of elements past n are 0 (the pad nibble of an odd n); wave-uniform test, so full
