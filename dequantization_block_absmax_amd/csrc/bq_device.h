@@ -56,40 +56,54 @@ __device__ __forceinline__ uint32_t nearest_code(float y, const QuantArgs& qa,
   }
 }
 
-// Copies the thresholds into LDS and expands the per-bucket bases of the kernel arguments
-// into LDS entries (base, T[base], T[base+1], T[base+2]); special buckets get (z, NaN, ...).
+// The table words one thread copies into LDS: thresholds and per-bucket bases, read from the
+// kernel arguments in one batch with fixed trip counts, so the prologue waits for memory once.
+// A kernel issues these loads before its first data loads: loads return in issue order, so the
+// LUT fill need not wait behind the data.
+template <int MODE, int M, int NT>
+struct LutWords {
+  static constexpr int kThrIt = (260 + NT - 1) / NT;
+  static constexpr int kLutIt = MODE == SEARCH ? 0 : (LutLayout<MODE, M>::kSize + NT - 1) / NT;
+  float th[kThrIt];
+  uint32_t bs[kLutIt > 0 ? kLutIt : 1];
+};
+
+template <int MODE, int M, int NT>
+__device__ __forceinline__ LutWords<MODE, M, NT> lut_fetch(const QuantArgs& qa, int tid) {
+  using L = LutWords<MODE, M, NT>;
+  L l;
+#pragma unroll
+  for (int k = 0; k < L::kThrIt; ++k) {
+    const int i = tid + k * NT;
+    l.th[k] = i < 260 ? qa.thr[i] : 0.0f;
+  }
+#pragma unroll
+  for (int k = 0; k < L::kLutIt; ++k) {
+    const int i = tid + k * NT;
+    l.bs[k] = i < qa.nbuckets ? qa.base[i] : 0u;
+  }
+  return l;
+}
+
+// Writes the thresholds into LDS and expands the per-bucket bases into LDS entries
+// (base, T[base], T[base+1], T[base+2]); special buckets get (z, NaN, ...).
 // s_lut holds LutLayout<MODE, M>::kSize entries.
 // Must be called by every thread of the workgroup; ends with a barrier.
 template <int MODE, int M, int NT>
-__device__ __forceinline__ void build_lut(const QuantArgs& qa, typename Entry<M>::type* s_lut, float* s_thr,
-                                          int tid) {
+__device__ __forceinline__ void lut_fill(const QuantArgs& qa, const LutWords<MODE, M, NT>& l,
+                                         typename Entry<M>::type* s_lut, float* s_thr, int tid) {
   using E = typename Entry<M>::type;
-  // Every argument word a thread needs is loaded in one batch (fixed trip counts), so the
-  // prologue waits for memory once rather than once per loop iteration.
-  constexpr int kThrIt = (260 + NT - 1) / NT;
-  constexpr int kLutIt = MODE == SEARCH ? 0 : (LutLayout<MODE, M>::kSize + NT - 1) / NT;
-  float th[kThrIt];
-  uint32_t bs[kLutIt > 0 ? kLutIt : 1];
+  using L = LutWords<MODE, M, NT>;
 #pragma unroll
-  for (int k = 0; k < kThrIt; ++k) {
-    const int i = tid + k * NT;
-    th[k] = i < 260 ? qa.thr[i] : 0.0f;
-  }
-#pragma unroll
-  for (int k = 0; k < kLutIt; ++k) {
-    const int i = tid + k * NT;
-    bs[k] = i < qa.nbuckets ? qa.base[i] : 0u;
-  }
-#pragma unroll
-  for (int k = 0; k < kThrIt; ++k)
-    if (tid + k * NT < 260) s_thr[tid + k * NT] = th[k];
+  for (int k = 0; k < L::kThrIt; ++k)
+    if (tid + k * NT < 260) s_thr[tid + k * NT] = l.th[k];
   __syncthreads();
   if constexpr (MODE != SEARCH) {
 #pragma unroll
-    for (int k = 0; k < kLutIt; ++k) {
+    for (int k = 0; k < L::kLutIt; ++k) {
       const int i = tid + k * NT;
       if (i < qa.nbuckets) {
-        const uint32_t b = bs[k];
+        const uint32_t b = l.bs[k];
         const bool sp = (i == qa.special0) || (i == qa.special1);
         const uint32_t nan = 0x7fc00000u;
         E e;

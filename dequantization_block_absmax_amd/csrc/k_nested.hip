@@ -161,6 +161,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
   const int64_t b0 = ((int64_t)blockIdx.x * kWaves + (tid >> 6)) * 256 * KR + lane * 4;
   const bool active = b0 - lane * 4 < nb;
 
+  const auto lw = lut_fetch<MODE, M, kThreads>(qa, tid);  // table loads ahead of the data loads
   float4 v[KR];
 #pragma unroll
   for (int r = 0; r < KR; ++r) {
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
       if (blockIdx.x == 0) *mean = mv;
     }
   }
-  build_lut<MODE, M, kThreads>(qa, s_lut, s_thr, tid);  // ends with a barrier: s_mean is visible
+  lut_fill<MODE, M, kThreads>(qa, lw, s_lut, s_thr, tid);  // ends with a barrier: s_mean is visible
   if (!active) return;  // whole waves
   const float m = count > 0 ? s_mean : *mean;
 

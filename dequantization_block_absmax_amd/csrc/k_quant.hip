@@ -366,12 +366,14 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __res
   };
   uint4* stage = s_stage + (KB == 8 ? (tid >> 6) * 128 : 0);
   {
-    // The first tile apart from the others: its chunk is loaded before the table prologue,
-    // and giving each tile its own registers avoids copying them between loop iterations.
+    // The first tile apart from the others: the table words are loaded first, then the tile's
+    // chunk, then the LUT is filled while the chunk is in flight.  Giving each tile its own
+    // registers avoids copying them between loop iterations.
+    const auto lw = lut_fetch<MODE, M, kThreads>(qa, tid);
     const int64_t elem0 = (tile0 * kThreads + tid) * kEPT;
     uint32_t w[Tr::kWords];
     const int nvalid = load(elem0, w);
-    build_lut<MODE, M, kThreads>(qa, s_lut, s_thr, tid);
+    lut_fill<MODE, M, kThreads>(qa, lw, s_lut, s_thr, tid);
     quantize_chunk<DT, KB, MODE, M>(w, nvalid, elem0, n, log2g, absmax, packed, partials, qa, s_lut, s_thr, sh,
                                     stage);
   }
