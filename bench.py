@@ -24,6 +24,7 @@ import gc
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -81,6 +82,7 @@ class Workload:
         self.q4 = synth.q32_blocks(self.n4 // 32, "q4", seed=4, device=dev)
         self.q8 = synth.q32_blocks(self.n4 // 32, "q8", seed=4, device=dev)
         self.out4 = torch.empty(self.n4, dtype=torch.bfloat16, device=dev)
+        self.q32_sets = {}  # rotated GGUF buffer sets of the per-call timing
         e = 2 ** 29
         # input bytes and algorithmic read+write bytes of each call
         self.calls = {
@@ -95,17 +97,17 @@ class Workload:
         bq, torch = self.bq, self.torch
         src = self.q4 if name == "dequant_q32_q4" else self.q8
         fmt = bq.BQ_Q32_Q4 if name == "dequant_q32_q4" else bq.BQ_Q32_Q8
-        k = -(-(1 << 30) // (src.numel() + 2 * self.n4))
-        sets = [(src.clone(), torch.empty_like(self.out4)) for _ in range(k)]
+        if name not in self.q32_sets:  # made once, kept for the later rounds
+            k = -(-(1 << 30) // (src.numel() + 2 * self.n4))
+            self.q32_sets[name] = [(src.clone(), torch.empty_like(self.out4)) for _ in range(k)]
+        sets = self.q32_sets[name]
         i = [0]
 
         def call():
-            blocks, out = sets[i[0] % k]
+            blocks, out = sets[i[0] % len(sets)]
             i[0] += 1
             bq.check(bq.bq_dequant_q32(blocks, bq.BQ_BF16, self.n4, self.COLS, fmt, out), name)
-        ms = time_calls(call, torch, reps)
-        del sets
-        return ms
+        return time_calls(call, torch, reps)
 
     def run(self, name):
         bq = self.bq
@@ -125,6 +127,7 @@ class Workload:
 
 
 STEP = ["quantize_nested", "dequantize_nested", "dequant_q32_q4", "dequant_q32_q8"]
+ROUNDS, REPS = 7, 10  # per-call breakdown: interleaved rounds of back-to-back calls
 
 
 def timed_step_loop(w: Workload, torch, steps: int):
@@ -185,9 +188,10 @@ def detail_configs(bq, synth, torch, dev, peak):
     t16, t256 = bq.code_table(synth.table16()), bq.code_table(synth.table256())
 
     def rotate(make, footprint, fn, reps, graph=False):
-        """Mean ms per call over buffer sets rotated past the last-level cache; with graph,
-        also the mean ms per call when the k calls are captured once as a HIP graph and
-        replayed (no per-call launch cost from the host)."""
+        """Ms per call over buffer sets rotated past the last-level cache (the median of
+        ROUNDS batches of reps back-to-back calls); with graph, also the ms per call when the k
+        calls are captured once as a HIP graph and replayed (no per-call launch cost from the
+        host)."""
         k = max(1, min(64, -(-(1 << 30) // footprint)))
         sets = [make() for _ in range(k)]
         i = [0]
@@ -195,7 +199,7 @@ def detail_configs(bq, synth, torch, dev, peak):
         def call():
             fn(sets[i[0] % k])
             i[0] += 1
-        ms = time_calls(call, torch, reps)
+        ms = statistics.median(time_calls(call, torch, reps) for _ in range(ROUNDS))
         if not graph:
             return ms, None
         g = torch.cuda.CUDAGraph()
@@ -210,7 +214,7 @@ def detail_configs(bq, synth, torch, dev, peak):
             for st in sets:
                 fn(st)
         replays = max(1, reps // k)
-        gms = time_calls(g.replay, torch, replays) / k
+        gms = statistics.median(time_calls(g.replay, torch, replays) for _ in range(ROUNDS)) / k
         del g
         return ms, gms
 
@@ -318,15 +322,21 @@ def main():
     total_ms, wall_ms = timed_step_loop(w, torch, args.steps)
     ms_per_step = total_ms / args.steps
     # Per-call breakdown: each call back to back between two events (an event between calls
-    # adds a few microseconds of its own).  The GGUF calls rotate over buffer sets of more than
-    # 1 GiB in total, so that back-to-back calls do not find their data in the 256 MB
-    # last-level cache (inside the step, the 1 GiB calls between them evict it anyway).
-    per = {}
-    for name in STEP:
-        if name.startswith("dequant_q32"):
-            per[name] = w.time_q32_rotated(name, time_calls, max(args.steps, 10))
-        else:
-            per[name] = time_calls(lambda: w.run(name), torch, max(args.steps, 10))
+    # adds a few microseconds of its own), REPS calls per round.  The GGUF calls rotate over
+    # buffer sets of more than 1 GiB in total, so that back-to-back calls do not find their data
+    # in the 256 MB last-level cache (inside the step, the 1 GiB calls between them evict it
+    # anyway).
+    # The call types take turns over several rounds and each reports its median round: clocks
+    # drift under sustained load, and a fixed order would hand the drift to whichever call is
+    # timed at the wrong moment.
+    rounds = {name: [] for name in STEP + ["quantize_kernel"]}
+    for _ in range(ROUNDS):
+        for name in rounds:
+            if name.startswith("dequant_q32"):
+                rounds[name].append(w.time_q32_rotated(name, time_calls, REPS))
+            else:
+                rounds[name].append(time_calls(lambda: w.run(name), torch, REPS))
+    per = {name: statistics.median(v) for name, v in rounds.items()}
     step_input = sum(w.calls[c]["inp"] for c in STEP)
     value = step_input / (ms_per_step / 1e3) / 1e9
     log("step %.3f ms (wall %.3f ms/step)" % (ms_per_step, wall_ms / args.steps))
@@ -340,8 +350,8 @@ def main():
 
     # Roofline of the dominant kernel: the slower of the data quantize kernel (timed on its own,
     # same launch as inside quantize_nested) and the nested dequantize kernel (one launch per
-    # call), each as the mean over back-to-back launches between two HIP events.
-    qk_ms = time_calls(lambda: w.run("quantize_kernel"), torch, max(args.steps, 10))
+    # call), each as the median round of back-to-back launches between two HIP events.
+    qk_ms = per["quantize_kernel"]
     n = w.N5
     q_bytes = 2 * n + n // 2 + 4 * w.nb
     dq_bytes = w.calls["dequantize_nested"]["rw"]

@@ -56,6 +56,19 @@ __device__ __forceinline__ uint32_t nearest_code(float y, const QuantArgs& qa,
   }
 }
 
+// One output word from its codes, in byte order: eight 4-bit codes (the first element of a
+// pair in the high nibble) or four 8-bit codes.  The bytes are joined with byte permutes, one
+// operation per byte pair, where a chain of shifts and ORs is compiled into more operations.
+template <int KB>
+__device__ __forceinline__ uint32_t pack_word(const uint32_t* q) {
+  uint32_t b[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) b[k] = KB == 4 ? (q[2 * k] << 4) | q[2 * k + 1] : q[k];
+  const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);  // b0 | b1 << 8
+  const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);  // b2 | b3 << 8
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);                    // lo | hi << 16
+}
+
 // The table words one thread copies into LDS: thresholds and per-bucket bases, read from the
 // kernel arguments in one batch with fixed trip counts, so the prologue waits for memory once.
 // A kernel issues these loads before its first data loads: loads return in issue order, so the

@@ -197,12 +197,17 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
     if ((lane & (lg - 1)) == 0 && (r & (R - 1)) == 0 && g < ngroups) absmax2[g] = a2;
     const float s = a2 < 0x1p-64f ? 0x1p64f : (a2 > 0x1p64f ? 0x1p-64f : 1.0f);
     const float rc = 1.0f / (a2 * s);
-    uint32_t w = 0;
+    // (d * s) * rc is d * rc when s = 1; a wave-uniform test lets the common case skip the
+    // scaling instead of computing both and selecting.
+    uint32_t q[4];
+    if (__builtin_expect(__all(s == 1.0f), 1)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float y = (s == 1.0f) ? d[i] * rc : (d[i] * s) * rc;
-      w |= nearest_code<MODE, M>(y, qa, s_lut, s_thr) << (8 * i);
+      for (int i = 0; i < 4; ++i) q[i] = nearest_code<MODE, M>(d[i] * rc, qa, s_lut, s_thr);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = nearest_code<MODE, M>((d[i] * s) * rc, qa, s_lut, s_thr);
     }
+    const uint32_t w = pack_word<8>(q);
     if (b + 4 <= nb) {
       *reinterpret_cast<uint32_t*>(q2 + b) = w;
     } else {

@@ -196,19 +196,6 @@ struct QuantShared {
   uint32_t red[kThreads / 64];  // B = 4096: the two waves of a block exchange their keys
 };
 
-// One output word from its codes, in byte order: eight 4-bit codes (the first element of a
-// pair in the high nibble) or four 8-bit codes.  The bytes are joined with byte permutes, one
-// operation per byte pair, where a chain of shifts and ORs is compiled into more operations.
-template <int KB>
-__device__ __forceinline__ uint32_t pack_word(const uint32_t* q) {
-  uint32_t b[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) b[k] = KB == 4 ? (q[2 * k] << 4) | q[2 * k + 1] : q[k];
-  const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);  // b0 | b1 << 8
-  const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);  // b2 | b3 << 8
-  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);                    // lo | hi << 16
-}
-
 // Quantizes one lane chunk: block absmax, normalization, codes, packing and stores; with
 // `partials`, also the pairwise sum of the block maxima of this wave's 2048 elements.
 template <int DT, int KB, int MODE, int M>
@@ -306,22 +293,29 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, in
   }
 
   // Store.  4-bit: each lane's 16 bytes follow its left neighbour's.  8-bit: a lane holds 32
-  // bytes, so a wave's 2 KB goes through its LDS region and leaves as two 1 KB stores with
-  // consecutive lanes writing consecutive 16 bytes (lane l writes half l & 1 of lane 32k + l/2).
+  // bytes, so a wave's 2 KB goes through its 1 KB LDS region in two halves and leaves as two
+  // 1 KB stores with consecutive lanes writing consecutive 16 bytes (in half h, lane l writes
+  // half l & 1 of lane 32h + l/2).
   const int64_t packed_bytes = KB == 4 ? (n + 1) / 2 : n;
   constexpr int kBytes = kOut * 4;
   const int64_t off = KB == 4 ? elem0 >> 1 : elem0;
   const int64_t wave_off = off - (int64_t)lane * kBytes;
   if (KB == 8 && wave_off + 64 * kBytes <= packed_bytes) {  // whole wave in range (uniform)
-    stage[2 * lane] = make_uint4(o[0], o[1], o[2], o[3]);
-    stage[2 * lane + 1] = make_uint4(o[4 % kOut], o[5 % kOut], o[6 % kOut], o[7 % kOut]);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // Two rounds through a 1 KB region: lanes 0-31, then 32-63, stage their bytes and the
+    // whole wave stores them.
     uint8_t* dst = packed + wave_off;
-    store16_nt(dst + 16 * lane, stage[lane]);
-    store16_nt(dst + 16 * (64 + lane), stage[64 + lane]);
-    __builtin_amdgcn_wave_barrier();  // the next tile's writes come after these reads
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if ((lane >> 5) == h) {
+        stage[2 * (lane & 31)] = make_uint4(o[0], o[1], o[2], o[3]);
+        stage[2 * (lane & 31) + 1] = make_uint4(o[4 % kOut], o[5 % kOut], o[6 % kOut], o[7 % kOut]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      store16_nt(dst + 1024 * h + 16 * lane, stage[lane]);
+      __builtin_amdgcn_wave_barrier();  // the next round's writes come after these reads
+    }
   } else if (KB == 4 && off + kBytes <= packed_bytes) {
     store16_nt(packed + off, make_uint4(o[0], o[1], o[2], o[3]));
   } else if (KB == 8 && off + kBytes <= packed_bytes) {
@@ -344,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __res
   using E = typename Entry<M>::type;
   __shared__ float s_thr[260];
   __shared__ E s_lut[LutLayout<MODE, M>::kSize];
-  __shared__ uint4 s_stage[KB == 8 ? kThreads * 2 : 1];  // 8-bit codes: store exchange
+  __shared__ uint4 s_stage[KB == 8 ? kThreads : 1];  // 8-bit codes: store exchange, 1 KB per wave
   __shared__ QuantShared sh;
 
   const int tid = threadIdx.x;
@@ -364,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __res
     }
     return load_chunk<DT>(in, n, e0, w);
   };
-  uint4* stage = s_stage + (KB == 8 ? (tid >> 6) * 128 : 0);
+  uint4* stage = s_stage + (KB == 8 ? (tid >> 6) * 64 : 0);
   {
     // The first tile apart from the others: the table words are loaded first, then the tile's
     // chunk, then the LUT is filled while the chunk is in flight.  Giving each tile its own
