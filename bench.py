@@ -304,6 +304,16 @@ def main():
         for name in STEP + ["quantize_kernel"]:
             for _ in range(3):
                 w.run(name)
+        # the bf16 2^26 8-bit B=4096 workload's two calls, for their own counter summaries
+        n3 = 1 << 26
+        x3 = synth.blockwise_input(n3, "bfloat16", 3, std=0.02, device=dev)
+        a3 = torch.empty(n3 // 4096, dtype=torch.float32, device=dev)
+        p3 = torch.empty(n3, dtype=torch.uint8, device=dev)
+        o3 = torch.empty_like(x3)
+        for _ in range(3):
+            bq.check(bq.bq_quantize_blockwise(x3, bq.BQ_BF16, n3, 4096, w.t256, a3, p3), "C3 quantize")
+        for _ in range(3):
+            bq.check(bq.bq_dequantize_blockwise(o3, bq.BQ_BF16, n3, 4096, w.t256, a3, p3), "C3 dequantize")
         src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
