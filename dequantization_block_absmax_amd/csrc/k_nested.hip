@@ -24,7 +24,7 @@
 namespace bq {
 namespace {
 
-constexpr int kThreads = 256;  // statistics workgroup
+constexpr int kThreads = 512;  // statistics workgroup: eight waves share one LUT
 constexpr int kWaves = kThreads / 64;
 constexpr int kMeanThreads = 1024;
 constexpr int kLeaves = 32;                 // sums per lane
