@@ -116,19 +116,25 @@ __device__ __forceinline__ void lut_fill(const QuantArgs& qa, const LutWords<MOD
     for (int k = 0; k < L::kLutIt; ++k) {
       const int i = tid + k * NT;
       if (i < qa.nbuckets) {
-        const uint32_t b = l.bs[k];
-        const bool sp = (i == qa.special0) || (i == qa.special1);
-        const uint32_t nan = 0x7fc00000u;
+        const uint32_t b = l.bs[k];  // <= 255, so b + 2 stays inside the 260 thresholds
         E e;
-        e.x = sp ? (uint32_t)qa.z : b;
-        e.y = sp ? nan : f32_bits(s_thr[b]);
+        e.x = b;
+        e.y = f32_bits(s_thr[b]);
         if constexpr (M >= 2) {
-          e.z = sp ? nan : f32_bits(s_thr[b + 1]);
-          e.w = sp ? nan : f32_bits(s_thr[b + 2]);
+          e.z = f32_bits(s_thr[b + 1]);
+          e.w = f32_bits(s_thr[b + 2]);
         }
         s_lut[i] = e;
       }
     }
+    // The two special buckets are rewritten by the threads that wrote them above, so program
+    // order puts these writes last: code z, and NaN thresholds that no compare passes.
+    E sp;
+    sp.x = (uint32_t)qa.z;
+    sp.y = 0x7fc00000u;
+    if constexpr (M >= 2) sp.z = sp.w = 0x7fc00000u;
+    if (tid == (qa.special0 & (NT - 1))) s_lut[qa.special0] = sp;
+    if (tid == (qa.special1 & (NT - 1))) s_lut[qa.special1] = sp;
     __syncthreads();
   }
 }
