@@ -80,6 +80,14 @@ __device__ __forceinline__ void store_tail(uint8_t* out, int64_t e, const float*
 
 // Raw code bytes of the unit starting at element e (e a multiple of 8, e < n): 4 bytes of
 // nibbles (4-bit) or 8 code bytes (8-bit); bytes past the end of `packed` read as 0.
+// In the tail unit each byte is loaded into its own register and the words are joined after
+// by byte permutes, so the loads are in flight together (merging each byte into its word as it
+// arrives made every load wait for the previous one).
+__device__ __forceinline__ uint32_t join_bytes(const uint32_t* b) {
+  return __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u),
+                               __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u), 0x05040100u);
+}
+
 template <int KB>
 __device__ __forceinline__ uint2 fetch_codes(const uint8_t* packed, int64_t e, int64_t n) {
   uint2 p = make_uint2(0, 0);
@@ -88,21 +96,20 @@ __device__ __forceinline__ uint2 fetch_codes(const uint8_t* packed, int64_t e, i
       p.x = *reinterpret_cast<const uint32_t*>(packed + (e >> 1));
     } else {
       const int64_t nbytes = (n + 1) >> 1;
+      uint32_t b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if ((e >> 1) + i < nbytes) p.x |= (uint32_t)packed[(e >> 1) + i] << (8 * i);
+      for (int i = 0; i < 4; ++i) b[i] = (e >> 1) + i < nbytes ? (uint32_t)packed[(e >> 1) + i] : 0u;
+      p.x = join_bytes(b);
     }
   } else {
     if (e + 8 <= n) {
       p = *reinterpret_cast<const uint2*>(packed + e);
     } else {
+      uint32_t b[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (e + i < n) {
-          const uint32_t byte = packed[e + i];
-          if (i < 4) p.x |= byte << (8 * i);
-          else p.y |= byte << (8 * (i - 4));
-        }
+      for (int i = 0; i < 8; ++i) b[i] = e + i < n ? (uint32_t)packed[e + i] : 0u;
+      p.x = join_bytes(b);
+      p.y = join_bytes(b + 4);
     }
   }
   return p;

@@ -149,11 +149,15 @@ __device__ __forceinline__ int load_chunk(const uint8_t* __restrict__ in, int64_
     for (int e = 0; e < 32; ++e)
       if (e < nvalid) w[e] = src[e];
   } else {
+    // Every element is loaded into its own register first and the words are joined after by
+    // byte permutes: merging each load into its word as it arrives (or shifting it in the
+    // load's branch) made every load wait for the previous one.
     const unsigned short* src = reinterpret_cast<const unsigned short*>(in) + elem0;
+    uint32_t h[32];
 #pragma unroll
-    for (int e = 0; e < 32; ++e)
-      if (e < nvalid)
-        w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0xffffu) | ((uint32_t)src[e] << 16)) : ((w[e >> 1] & 0xffff0000u) | src[e]);
+    for (int e = 0; e < 32; ++e) h[e] = e < nvalid ? (uint32_t)src[e] : (Tr::kNaNWord & 0xffffu);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = __builtin_amdgcn_perm(h[2 * i + 1], h[2 * i], 0x05040100u);
   }
   return nvalid;
 }
