@@ -10,7 +10,7 @@
 // output is rounded exactly once, by the conversion to the output type.
 //
 // Work decomposition: a unit is a quarter block (8 elements, 16 output bytes for bf16).
-// Lane `tid` of a 256-lane workgroup handles units tile*1024 + u*256 + tid, u = 0..3, so the
+// Lane `tid` of a 256-lane workgroup handles units tile*512 + u*256 + tid, u = 0..1, so the
 // output stores of a wave are contiguous.  Blocks are only 2-byte aligned (18 and 34 bytes);
 // a tile's bytes are staged through LDS with 16-byte loads.
 #include <hip/hip_runtime.h>
@@ -22,7 +22,7 @@ namespace bq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnits = 4;
+constexpr int kUnits = 2;  // 128 blocks per workgroup: 2.5% faster than 256, far faster than 64
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -83,8 +83,8 @@ __device__ __forceinline__ int unit_offset(int k) {
   return 2 + (FMT == 0 ? 8 * (k & 1) : 8 * k);
 }
 
-// A workgroup expands 256 blocks (8192 values).  When the tile is whole and the blocks are
-// 16-byte aligned, the tile's 4608 (Q4) or 8704 (Q8) bytes are read as contiguous 16-byte
+// A workgroup expands 128 blocks (4096 values).  When the tile is whole and the blocks are
+// 16-byte aligned, the tile's 2304 (Q4) or 4352 (Q8) bytes are read as contiguous 16-byte
 // chunks (non-temporal) into LDS, and every unit reads its scale and payload there: one
 // global load per 16 bytes instead of five 2-byte loads per unit (the records are only 2-byte
 // aligned).  Otherwise each unit reads its bytes from memory with 2-byte loads.

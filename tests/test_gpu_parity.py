@@ -375,7 +375,7 @@ def test_c3_bf16_8bit_blocksize4096(dev, o):
 
 @pytest.mark.parametrize("fmt", ["q4", "q8"])
 def test_q32_partial_tile_and_offset(dev, o, fmt):
-    """Whole 256-block tiles go through LDS with 16-byte loads; a partial last tile and a block
+    """Whole tiles (128 blocks) go through LDS with 16-byte loads; a partial last tile and a block
     array that is not 16-byte aligned (it starts one 18- or 34-byte block into a buffer) take
     the 2-byte-load path.  Both must give the same values."""
     bs = 18 if fmt == "q4" else 34
