@@ -255,7 +255,55 @@ def detail_configs(bq, synth, torch, dev, peak):
     for B in (32, 64, 128, 256, 512, 1024, 2048, 4096):
         blockwise("C2 fp16 n=8388609 B=%d" % B, 8388609, "float16", B, t16, 2, 1.0, 1e-3, 1e-4, reps=100)
     blockwise("C3 bf16 n=2^26 8-bit B=4096", 1 << 26, "bfloat16", 4096, t256, 3, 0.02, reps=50)
+    out.update(loading_pipeline(bq, synth, torch, dev, t16))
     return out
+
+
+def loading_pipeline(bq, synth, torch, dev, table, chunks=8, chunk=1 << 25, B=64):
+    """The loading path: bf16 weights in pinned host memory reach the device in chunks on one
+    stream while a second stream quantizes each chunk as it lands (double-buffered).  Reports
+    the rate of the whole pipeline next to the host-to-device copies alone: the library's
+    calls take device pointers, so PCIe is outside the boundary and never part of `value`."""
+    x = synth.blockwise_input(chunks * chunk, "bfloat16", 8, std=0.02, device=dev)
+    host = torch.empty(chunks * chunk, dtype=torch.bfloat16, pin_memory=True)
+    host.copy_(x)
+    del x
+    bufs = [torch.empty(chunk, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    nb = chunk // B
+    absmax = torch.empty(chunks, nb, dtype=torch.float32, device=dev)
+    packed = torch.empty(chunks, chunk // 2, dtype=torch.uint8, device=dev)
+    copy_s, work_s = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def run(quantize):
+        copied = [torch.cuda.Event() for _ in range(chunks)]
+        used = [torch.cuda.Event() for _ in range(chunks)]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(copy_s)
+        for c in range(chunks):
+            buf = bufs[c % 2]
+            if c >= 2:
+                copy_s.wait_event(used[c - 2])
+            with torch.cuda.stream(copy_s):
+                buf.copy_(host[c * chunk:(c + 1) * chunk], non_blocking=True)
+                copied[c].record(copy_s)
+            work_s.wait_event(copied[c])
+            if quantize:
+                bq.check(bq.bq_quantize_blockwise(buf, bq.BQ_BF16, chunk, B, table, absmax[c], packed[c], work_s))
+            used[c].record(work_s)
+        copy_s.wait_event(used[chunks - 1])
+        b.record(copy_s)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    run(True)
+    copy_ms = statistics.median(run(False) for _ in range(3))
+    pipe_ms = statistics.median(run(True) for _ in range(3))
+    byts = chunks * chunk * 2
+    return {"loading pipeline bf16 2^28 in 8 chunks: pinned H2D + 4-bit B=64 quantize": dict(
+        us=round(pipe_ms * 1e3, 1), input_gbs=round(byts / pipe_ms / 1e6, 1),
+        h2d_only_us=round(copy_ms * 1e3, 1), h2d_only_gbs=round(byts / copy_ms / 1e6, 1),
+        quantize_hidden=round(copy_ms / pipe_ms, 3))}
 
 
 def cpu_baseline(w: Workload, torch):
