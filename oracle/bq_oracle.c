@@ -256,6 +256,29 @@ int bqo_dequantize_blockwise(void* out, int dtype, int64_t n, int32_t B, const f
   return 0;
 }
 
+/* Fused dequantize + linear, the consumer of A6 (y = x . deq(W)^T): W is the N x K row-major
+ * weight tensor quantized blockwise over its flat index (element (n, k) is flat element
+ * n*K + k), w = fl32(c[q] * a_b) its binary32 dequantized value (A6 with a binary32 output),
+ * and y[m][n] = sum over k of x[m][k] * w[n][k], accumulated in binary64 in ascending k.
+ * x is M x K row-major in `dtype`; y is M x N row-major binary64. */
+int bqo_linear_blockwise(const void* x, int dtype, int64_t M, int64_t K, int64_t N, int32_t B,
+                         const float* c, int Kc, const float* absmax, const uint8_t* packed,
+                         double* y) {
+  if (M < 0 || K < 0 || N < 0 || !valid_args(dtype, M * K, B, Kc)) return -1;
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      double s = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const int64_t flat = n * K + k;
+        const float scale = absmax[flat / B];
+        const float w = c[unpack_code(packed, flat, Kc)] * scale;
+        s += (double)load_elem(x, dtype, m * K + k) * (double)w;
+      }
+      y[m * N + n] = s;
+    }
+  return 0;
+}
+
 /* ------------------------------------------------------------------------------------ */
 /* Nested statistics (nested General8 / compressed-statistics NF4).                     */
 /* ------------------------------------------------------------------------------------ */

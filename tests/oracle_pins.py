@@ -556,4 +556,66 @@ def pin_q32_closed_form(o):
         assert np.array_equal(_bits32(out32), _bits32(prod)), name
 
 
+# ------------------------------------------------------------------------------------------
+# Fused dequantize + linear (y = x . deq(W)^T)
+# ------------------------------------------------------------------------------------------
+
+def _codes_high_first(packed: np.ndarray, n: int, K: int) -> np.ndarray:
+    """Codes read back from packed bytes without the oracle: 8-bit codes one per byte; 4-bit
+    codes two per byte, the first element of a pair in the high nibble."""
+    p = np.asarray(packed, np.uint8).astype(np.int64)
+    if K == 256:
+        return p[:n]
+    q = np.empty(2 * p.size, np.int64)
+    q[0::2] = p >> 4
+    q[1::2] = p & 15
+    return q[:n]
+
+
+def pin_linear_dyadic_closed_form(o):
+    """Every product and sum exact: the hand-worked table (multiples of 1/8), power-of-two
+    block scales and small integer activations.  The N x K codes are written into the packed
+    bytes here (first element of a pair high), not by the oracle's quantizer, so y must equal
+    the exact rational value of sum_k x[m][k] * c[q[n][k]] * a[(n*K + k) // B]."""
+    table = _hand_table()
+    M, N, K, B = 3, 5, 128, 32
+    q = (np.arange(N)[:, None] * 5 + np.arange(K)[None, :] * 3) % 16
+    flat = q.reshape(-1)
+    packed = ((flat[0::2] << 4) | flat[1::2]).astype(np.uint8)
+    nb = N * K // B
+    absmax = np.ldexp(np.float32(1), (np.arange(nb) % 7) - 3).astype(np.float32)
+    x = ((np.arange(M * K).reshape(M, K) * 7) % 11 - 5).astype(np.float32)
+    y = o.linear_blockwise(x, oracle.F32, M, K, N, B, table, absmax, packed)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(Fraction(float(x[m, k])) * Fraction(float(table[q[n, k]])) *
+                        Fraction(float(absmax[(n * K + k) // B])) for k in range(K))
+            assert y[m, n] == exact, (m, n, y[m, n], float(exact))
+
+
+def pin_linear_exact_rational(o):
+    """Random bf16 activations and weights quantized to 4 and 8 bits: y must be within the
+    binary64 summation bound (K * 2^-53 of sum |x w|) of the exact rational sum, with each
+    weight w = fl32(c[q] * a) formed by numpy's IEEE binary32 product and the codes read back
+    from the packed bytes here."""
+    rng = _rng(61)
+    for K, table, B in ((16, synth.table16(), 64), (256, synth.table256(), 32)):
+        M, N, Kd = 2, 3, 192
+        xb = synth.to_bits16(torch.from_numpy(rng.standard_normal((M, Kd)).astype(np.float32))
+                             .to(torch.bfloat16)).reshape(M, Kd)
+        xf = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).view(torch.bfloat16).float().numpy()
+        w_in = (rng.standard_normal(N * Kd) * 0.02).astype(np.float32)
+        absmax, packed = o.quantize_blockwise(w_in, oracle.F32, B, table)
+        y = o.linear_blockwise(xb, oracle.BF16, M, Kd, N, B, table, absmax, packed)
+        codes = _codes_high_first(packed, N * Kd, K).reshape(N, Kd)
+        t32 = np.float32(table)
+        for m in range(M):
+            for n in range(N):
+                terms = [Fraction(float(xf[m, k])) *
+                         Fraction(float(t32[codes[n, k]] * absmax[(n * Kd + k) // B])) for k in range(Kd)]
+                exact = sum(terms)
+                bound = Fraction(Kd, 2 ** 53) * sum(abs(t) for t in terms) * Fraction(1 + 2 ** -40)
+                assert abs(Fraction(float(y[m, n])) - exact) <= bound, (K, m, n, float(y[m, n]), float(exact))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -37,6 +37,12 @@ MUTANTS = {
     "q32_offset_7": ("(float)(lo - 8) * d", "(float)(lo - 7) * d"),
     "q8_unsigned_codes": ("int q = (int8_t)blk[2 + j];", "int q = (uint8_t)blk[2 + j];"),
     "dequant_wrong_block": ("* absmax[i / B];", "* absmax[(i + 1) / B];"),
+    "linear_transposed_weight": ("const int64_t flat = n * K + k;", "const int64_t flat = k * N + n;"),
+    "linear_wrong_block": ("const float scale = absmax[flat / B];", "const float scale = absmax[flat / B / 2];"),
+    "linear_drops_last_term": ("s += (double)load_elem(x, dtype, m * K + k) * (double)w;",
+                               "if (k + 1 < K) s += (double)load_elem(x, dtype, m * K + k) * (double)w;"),
+    "linear_binary32_sum": ("      double s = 0.0;\n      for (int64_t k = 0; k < K; ++k) {\n        const int64_t flat",
+                            "      float s = 0.0f;\n      for (int64_t k = 0; k < K; ++k) {\n        const int64_t flat"),
 }
 
 
