@@ -101,6 +101,10 @@ BQ_HD float bits_f32(uint32_t u) {
 
 // Launchers (k_*.hip).  Each returns the hipError_t of its launches as an int.
 namespace bq {
+// Fused dequantize + linear for M <= 4 (k_linear.hip): y (M x N, binary32) = x . deq(W)^T.
+int launch_linear(const void* x, int dtype, int64_t M, int64_t K, int64_t N, int blocksize, const DequantArgs& da,
+                  const float* absmax, const uint8_t* packed, float* y, void* stream);
+
 int launch_quantize(const void* in, int dtype, int64_t n, int blocksize, const PreparedTable& t,
                     float* absmax, uint8_t* packed, double* partials, int log2tiles, void* stream);
 // Workgroups of a quantize launch over n elements.

@@ -147,6 +147,28 @@ typedef enum { BQ_Q32_Q4 = 0, BQ_Q32_Q8 = 1 } bq_q32_format;
 bq_status bq_dequant_q32(const void* blocks, bq_dtype dtype, int64_t n, int32_t row_len,
                          bq_q32_format format, void* out, hipStream_t stream);
 
+/* Fused dequantize + linear for small batches (decoding): y = x . deq(W)^T, with the
+ * dequantized weights formed in registers and never written out (weights used without
+ * expanding the full tensor, as in the mixed-input GEMMs of "stable-diffusion.cpp PR 2278",
+ * Summary; here for the blockwise codes of bq_quantize_blockwise).
+ *   x          [device] M x K row-major activations of `dtype`, 16-byte aligned.
+ *   M, K, N    1 <= M <= 4; K > 0 and a multiple of 16; N >= 0 (N = 0: nothing enqueued).
+ *   blocksize, code_table
+ *              the block size and table W was quantized with.
+ *   absmax     [device] ceil(N*K / blocksize) binary32 block maxima of W.
+ *   packed     [device] W's codes, 16-byte aligned, as bq_quantize_blockwise writes them for
+ *              the N*K-element weight tensor stored row-major (element (n, k) of W is flat
+ *              element n*K + k; blocks run over the flat index).
+ *   y          [device] out: M x N row-major binary32.
+ * y[m][n] approximates sum_k x[m][k] * w[n][k], w = fl32(c[q] * a) the binary32 dequantized
+ * weight (never rounded to 16 bits), accumulated in binary32 in an unspecified order: its
+ * error is at most (K/1024 + 64) * 2^-24 * sum_k |x[m][k] w[n][k]|.
+ * Errors: BQ_ERR_SIZE for M outside [1, 4], K not a positive multiple of 16, N < 0, or more
+ * than INT32_MAX blocks; otherwise as bq_dequantize_blockwise. */
+bq_status bq_linear_blockwise(const void* x, bq_dtype dtype, int64_t M, int64_t K, int64_t N, int32_t blocksize,
+                              const bq_code_table* code_table, const float* absmax, const uint8_t* packed,
+                              float* y, hipStream_t stream);
+
 /* The hipError_t (as int) of the most recent launch that failed on the calling thread with
  * BQ_ERR_HIP, or 0 if none has. */
 int bq_last_hip_error(void);
