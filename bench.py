@@ -256,6 +256,49 @@ def detail_configs(bq, synth, torch, dev, peak):
         blockwise("C2 fp16 n=8388609 B=%d" % B, 8388609, "float16", B, t16, 2, 1.0, 1e-3, 1e-4, reps=100)
     blockwise("C3 bf16 n=2^26 8-bit B=4096", 1 << 26, "bfloat16", 4096, t256, 3, 0.02, reps=50)
     out.update(loading_pipeline(bq, synth, torch, dev, t16))
+    out.update(fused_linear(bq, synth, torch, dev, t16, t256, peak))
+    return out
+
+
+def fused_linear(bq, synth, torch, dev, t16, t256, peak, N=14336, K=4096, B=64, sets=24):
+    """bq_linear_blockwise at a decode shape (a 14336 x 4096 weight, bf16 activations) for M = 1
+    and 4, 4- and 8-bit codes, with the weights rotated over enough sets to miss the 256 MB
+    last-level cache.  Beside it, the unfused path: dequantize to bf16 with this library, then
+    torch's matmul."""
+    out = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    for KB, table in ((4, t16), (8, t256)):
+        per = N * K // 2 if KB == 4 else N * K
+        ws = [(torch.randint(0, 256, (per,), dtype=torch.uint8, device=dev, generator=g),
+               (0.02 * torch.exp(torch.randn(N * K // B, device=dev, generator=g))).float()) for _ in range(sets)]
+        wbf = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
+        for M in (1, 4):
+            x = torch.randn(M, K, device=dev, generator=g).to(torch.bfloat16)
+            y = torch.empty(M, N, device=dev)
+            i = [0]
+
+            def fused():
+                p, a = ws[i[0] % sets]
+                i[0] += 1
+                bq.check(bq.bq_linear_blockwise(x, bq.BQ_BF16, M, K, N, B, table, a, p, y))
+
+            def unfused():
+                p, a = ws[i[0] % sets]
+                i[0] += 1
+                bq.check(bq.bq_dequantize_blockwise(wbf, bq.BQ_BF16, N * K, B, table, a, p))
+                torch.matmul(x, wbf.t())
+            fused()
+            unfused()
+            torch.cuda.synchronize()
+            f_ms = statistics.median(time_calls(fused, torch, 48) for _ in range(ROUNDS))
+            u_ms = statistics.median(time_calls(unfused, torch, 24) for _ in range(ROUNDS))
+            byts = per + 4 * (N * K // B) + 2 * M * K + 4 * M * N
+            out["linear %dx%d %d-bit B=%d M=%d bf16" % (N, K, KB, B, M)] = dict(
+                us=round(f_ms * 1e3, 2), rw_gbs=round(byts / f_ms / 1e6, 1),
+                pct_hbm_peak=round(100 * byts / f_ms / 1e6 / peak, 1),
+                unfused_us=round(u_ms * 1e3, 2), speedup_vs_unfused=round(u_ms / f_ms, 2))
+        del ws, wbf
     return out
 
 
