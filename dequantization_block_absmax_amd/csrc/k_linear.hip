@@ -31,7 +31,7 @@ constexpr int kWaves = kThreads / 64;
 // with 4 rows).
 template <int MT>
 constexpr int rows_per_group() { return MT > 2 ? 4 : 8; }
-constexpr int kLaneK = 16;              // consecutive k per lane and chunk
+constexpr int kLaneK = 16;  // consecutive k per lane and chunk (32 left half the waves idle at K = 4096: slower)
 constexpr int kChunk = 64 * kLaneK;     // k per wave and chunk
 
 // A lane's 16 activations of one row: the raw 16-byte words (loaded first, for every row,

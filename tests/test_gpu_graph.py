@@ -32,6 +32,12 @@ def test_graph_replay_matches_eager(dev):
     rows, cols = 64, 14336
     m = rows * cols
     q4 = synth.q32_blocks(m // 32, "q4", seed=42, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(43)
+    Ml, Kl, Nl = 3, 4096, 1000  # fused linear: seeded codes and block maxima of a 1000 x 4096 weight
+    wpk = torch.randint(0, 256, (Nl * Kl // 2,), dtype=torch.uint8, device=dev, generator=gen)
+    wam = 0.01 + 0.02 * torch.rand(Nl * Kl // B, device=dev, generator=gen)
+    xl = torch.randn(Ml, Kl, device=dev, generator=gen).to(torch.bfloat16)
 
     def buffers():
         ws_bytes = bq.bq_nested_workspace_bytes(n, B, B2)
@@ -41,7 +47,8 @@ def test_graph_replay_matches_eager(dev):
                     mean=torch.zeros(1, dtype=torch.float32, device=dev),
                     ws=torch.zeros(ws_bytes, dtype=torch.uint8, device=dev),
                     out=torch.zeros(n, dtype=torch.bfloat16, device=dev),
-                    out4=torch.zeros(m, dtype=torch.bfloat16, device=dev))
+                    out4=torch.zeros(m, dtype=torch.bfloat16, device=dev),
+                    y=torch.zeros(Ml, Nl, dtype=torch.float32, device=dev))
 
     def run(b, stream=None):
         st = bq.nested_stats(b["q2"], b["a2"], b["mean"], t256, B2, b["ws"])
@@ -49,11 +56,12 @@ def test_graph_replay_matches_eager(dev):
         bq.check(bq.bq_dequantize_nested(b["out"], bq.BQ_BF16, n, B, t16, st, b["packed"], stream),
                  "dequantize_nested")
         bq.check(bq.bq_dequant_q32(q4, bq.BQ_BF16, m, cols, bq.BQ_Q32_Q4, b["out4"], stream), "dequant_q32")
+        bq.check(bq.bq_linear_blockwise(xl, bq.BQ_BF16, Ml, Kl, Nl, B, t16, wam, wpk, b["y"], stream), "linear")
 
     eager = buffers()
     run(eager)
     torch.cuda.synchronize()
-    keys = ("packed", "q2", "a2", "mean", "out", "out4")
+    keys = ("packed", "q2", "a2", "mean", "out", "out4", "y")
     want = {k: eager[k].clone() for k in keys}
 
     g = buffers()
