@@ -55,7 +55,7 @@ def parse_args():
 
 
 class Workload:
-    """C5 (1 GiB bf16, nested 4-bit) and C4 (GGUF 4096 x 14336) buffers, resident on the device."""
+    """The 1 GiB bf16 nested 4-bit workload and the GGUF 4096 x 14336 blocks, resident on the device."""
 
     N5, B5, B2 = 1 << 29, 64, 256
     ROWS, COLS = 4096, 14336
@@ -182,8 +182,8 @@ def traffic_for(kernel: str):
 
 
 def detail_configs(bq, synth, torch, dev, peak):
-    """C1, C2 (every block size), C3 and C4/C5 calls on their own, with buffer sets rotated
-    so that each call's data is not resident in the 256 MB last-level cache."""
+    """fp32 2^19, fp16 2^23 + 1 (every block size) and bf16 2^26 8-bit calls on their own, with
+    buffer sets rotated so that each call's data is not resident in the 256 MB last-level cache."""
     out = {}
     t16, t256 = bq.code_table(synth.table16()), bq.code_table(synth.table256())
 
@@ -251,10 +251,10 @@ def detail_configs(bq, synth, torch, dev, peak):
         rec(tag + " quantize", qms, n * es, rw, qg)
         rec(tag + " dequantize", dms, pb + nb * 4, rw, dg)
 
-    blockwise("C1 fp32 n=524288 B=64", 524288, "float32", 64, t16, 1, 1.0, reps=200)
+    blockwise("fp32 n=2^19 4-bit B=64", 524288, "float32", 64, t16, 1, 1.0, reps=200)
     for B in (32, 64, 128, 256, 512, 1024, 2048, 4096):
-        blockwise("C2 fp16 n=8388609 B=%d" % B, 8388609, "float16", B, t16, 2, 1.0, 1e-3, 1e-4, reps=100)
-    blockwise("C3 bf16 n=2^26 8-bit B=4096", 1 << 26, "bfloat16", 4096, t256, 3, 0.02, reps=50)
+        blockwise("fp16 n=2^23+1 4-bit B=%d" % B, 8388609, "float16", B, t16, 2, 1.0, 1e-3, 1e-4, reps=100)
+    blockwise("bf16 n=2^26 8-bit B=4096", 1 << 26, "bfloat16", 4096, t256, 3, 0.02, reps=50)
     out.update(loading_pipeline(bq, synth, torch, dev, t16))
     out.update(fused_linear(bq, synth, torch, dev, t16, t256, peak))
     return out
@@ -402,9 +402,9 @@ def main():
         p3 = torch.empty(n3, dtype=torch.uint8, device=dev)
         o3 = torch.empty_like(x3)
         for _ in range(3):
-            bq.check(bq.bq_quantize_blockwise(x3, bq.BQ_BF16, n3, 4096, w.t256, a3, p3), "C3 quantize")
+            bq.check(bq.bq_quantize_blockwise(x3, bq.BQ_BF16, n3, 4096, w.t256, a3, p3), "bf16 2^26 8-bit quantize")
         for _ in range(3):
-            bq.check(bq.bq_dequantize_blockwise(o3, bq.BQ_BF16, n3, 4096, w.t256, a3, p3), "C3 dequantize")
+            bq.check(bq.bq_dequantize_blockwise(o3, bq.BQ_BF16, n3, 4096, w.t256, a3, p3), "bf16 2^26 8-bit dequantize")
         src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):

@@ -320,15 +320,15 @@ def test_nested_mean_many_runs(dev, o):
 
 # ---- the five benchmark workloads ----------------------------------------------------------
 
-def test_c1_fp32_blocksize64(dev, o):
+def test_fp32_2pow19_4bit_blocksize64(dev, o):
     x = synth.blockwise_input(524288, "float32", 1, std=1.0, device=dev)
-    check_blockwise(o, x, "float32", 64, synth.table16(), "C1")
+    check_blockwise(o, x, "float32", 64, synth.table16(), "fp32 2^19 B=64")
 
 
-def test_c2_fp16_all_blocksizes(dev, o):
+def test_fp16_2pow23plus1_4bit_all_blocksizes(dev, o):
     x = synth.blockwise_input(8388609, "float16", 2, std=1.0, p_out=1e-3, p_nf=1e-4, device=dev)
     for B in BLOCKSIZES:
-        check_blockwise(o, x, "float16", B, synth.table16(), "C2 B=%d" % B)
+        check_blockwise(o, x, "float16", B, synth.table16(), "fp16 2^23+1 B=%d" % B)
 
 
 def _finite_absmax_np(xbits: np.ndarray, dtype: str, B: int) -> np.ndarray:
@@ -353,7 +353,7 @@ def _sample_blocks(nb: int, count: int, seed: int) -> np.ndarray:
     return np.unique(np.concatenate([[0, nb - 1], rng.integers(0, nb, count)]))
 
 
-def test_c3_bf16_8bit_blocksize4096(dev, o):
+def test_bf16_2pow26_8bit_blocksize4096(dev, o):
     n, B = 67108864, 4096
     t256 = synth.table256()
     x = synth.blockwise_input(n, "bfloat16", 3, std=0.02, device=dev)
@@ -361,16 +361,16 @@ def test_c3_bf16_8bit_blocksize4096(dev, o):
     out = gpu_dequantize(packed, absmax, n, "bfloat16", B, t256)
     xb = host_bits(x)
     a_gpu = absmax.cpu().numpy()
-    assert_f32_bits_equal(a_gpu, _finite_absmax_np(xb, "bfloat16", B), "C3 absmax (all blocks)")
+    assert_f32_bits_equal(a_gpu, _finite_absmax_np(xb, "bfloat16", B), "bf16 2^26 8-bit absmax (all blocks)")
     p_gpu = packed.cpu().numpy()
     o_gpu = host_bits(out)
     for b in _sample_blocks(n // B, 30, 3):
         sl = slice(b * B, (b + 1) * B)
         oa, op = o.quantize_blockwise(xb[sl], oracle.BF16, B, t256)
-        assert_f32_bits_equal(a_gpu[b:b + 1], oa, "C3 absmax block %d" % b)
-        assert_bytes_equal(p_gpu[sl], op, "C3 codes block %d" % b)
+        assert_f32_bits_equal(a_gpu[b:b + 1], oa, "bf16 2^26 8-bit absmax block %d" % b)
+        assert_bytes_equal(p_gpu[sl], op, "bf16 2^26 8-bit codes block %d" % b)
         ref = o.dequantize_blockwise(op, oa, B, oracle.BF16, B, t256)
-        assert_bytes_equal(o_gpu[sl], ref, "C3 dequant block %d" % b)
+        assert_bytes_equal(o_gpu[sl], ref, "bf16 2^26 8-bit dequant block %d" % b)
 
 
 @pytest.mark.parametrize("fmt", ["q4", "q8"])
@@ -394,7 +394,7 @@ def test_q32_partial_tile_and_offset(dev, o, fmt):
 
 
 @pytest.mark.parametrize("fmt", ["q4", "q8"])
-def test_c4_gguf_4096x14336(dev, o, fmt):
+def test_gguf_4096x14336(dev, o, fmt):
     rows, cols = 4096, 14336
     n = rows * cols
     blocks = synth.q32_blocks(n // 32, fmt, seed=4, device=dev)
@@ -402,17 +402,17 @@ def test_c4_gguf_4096x14336(dev, o, fmt):
     f = bq.BQ_Q32_Q4 if fmt == "q4" else bq.BQ_Q32_Q8
     bq.check(bq.bq_dequant_q32(blocks, bq.BQ_BF16, n, cols, f, out))
     ref = o.dequant_q32(blocks.cpu().numpy(), n, cols, oracle.Q4 if fmt == "q4" else oracle.Q8, oracle.BF16)
-    assert_bytes_equal(host_bits(out), ref, "C4 " + fmt)
+    assert_bytes_equal(host_bits(out), ref, "gguf 4096x14336 " + fmt)
     for odt in ("float32", "float16"):  # other output types on a slice of rows
         m = 64 * cols
         out2 = torch.empty(m, dtype=TORCH_DT[odt], device=dev)
         bq.check(bq.bq_dequant_q32(blocks, BQ_DT[odt], m, cols, f, out2))
         ref2 = o.dequant_q32(blocks[:m // 32 * (18 if fmt == "q4" else 34)].cpu().numpy(), m, cols,
                              oracle.Q4 if fmt == "q4" else oracle.Q8, ORACLE_DT[odt])
-        assert_out_equal(out2, ref2, m, odt, "C4 %s -> %s" % (fmt, odt))
+        assert_out_equal(out2, ref2, m, odt, "gguf 4096x14336 %s -> %s" % (fmt, odt))
 
 
-def test_c5_bf16_nested_1gib(dev, o):
+def test_bf16_2pow29_4bit_nested(dev, o):
     n, B, B2 = 536870912, 64, 256
     t16, t256 = synth.table16(), synth.table256()
     x = synth.blockwise_input(n, "bfloat16", 5, std=0.02, device=dev)
@@ -421,9 +421,9 @@ def test_c5_bf16_nested_1gib(dev, o):
     nb = n // B
     xb = host_bits(x)
     a_gpu = r["absmax"].cpu().numpy()
-    assert_f32_bits_equal(a_gpu, _finite_absmax_np(xb, "bfloat16", B), "C5 absmax (all blocks)")
+    assert_f32_bits_equal(a_gpu, _finite_absmax_np(xb, "bfloat16", B), "bf16 2^29 nested absmax (all blocks)")
     m_ref = o.nested_mean(a_gpu)
-    assert np.float32(r["mean"].item()).view(np.uint32) == np.float32(m_ref).view(np.uint32), "C5 mean"
+    assert np.float32(r["mean"].item()).view(np.uint32) == np.float32(m_ref).view(np.uint32), "bf16 2^29 nested mean"
     q2 = r["q2"].cpu().numpy()
     a2 = r["absmax2"].cpu().numpy()
     p_gpu = r["packed"].cpu().numpy()
@@ -432,10 +432,10 @@ def test_c5_bf16_nested_1gib(dev, o):
     for g in _sample_blocks(nb // B2, 6, 5):
         gs = slice(g * B2, (g + 1) * B2)
         ra2, rq2 = o.quantize_blockwise(d[gs], oracle.F32, B2, t256)
-        assert_f32_bits_equal(a2[g:g + 1], ra2, "C5 absmax2 group %d" % g)
-        assert_bytes_equal(q2[gs], rq2, "C5 q2 group %d" % g)
+        assert_f32_bits_equal(a2[g:g + 1], ra2, "bf16 2^29 nested absmax2 group %d" % g)
+        assert_bytes_equal(q2[gs], rq2, "bf16 2^29 nested q2 group %d" % g)
         es = slice(g * B2 * B, (g + 1) * B2 * B)
         oa, op = o.quantize_blockwise(xb[es], oracle.BF16, B, t16)
-        assert_bytes_equal(p_gpu[g * B2 * B // 2:(g + 1) * B2 * B // 2], op, "C5 codes group %d" % g)
+        assert_bytes_equal(p_gpu[g * B2 * B // 2:(g + 1) * B2 * B // 2], op, "bf16 2^29 nested codes group %d" % g)
         ref = o.dequantize_nested(op, rq2, ra2, m_ref, B2 * B, oracle.BF16, B, t16, t256, B2)
-        assert_bytes_equal(o_gpu[es], ref, "C5 dequant group %d" % g)
+        assert_bytes_equal(o_gpu[es], ref, "bf16 2^29 nested dequant group %d" % g)
