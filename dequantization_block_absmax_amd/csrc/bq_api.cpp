@@ -46,13 +46,16 @@ size_t ws_bytes(int64_t n, int64_t nb) {
   return ws_partials_offset(nb) + (size_t)bq::quantize_partials(n, bq::kMaxLog2Tiles, 32) * 8;
 }
 
-// log2 of the 8192-element tiles each quantize workgroup processes: two tiles amortize the
-// table prologue once there are enough tiles to fill the GPU several times over (measured on
-// MI355X: 2^29 bf16 4-bit 220 against 230 us; 2^26 bf16 8-bit 43.4 against 45.1 us).
+// log2 of the 8192-element tiles each quantize workgroup processes.  One tile per workgroup:
+// since the table loads are issued ahead of the data and the LUT fill overlaps them, a second
+// tile no longer pays for its longer workgroups (measured on MI355X, interleaved rounds:
+// bf16 2^29 4-bit 212.4 against 218.4 us, 2^26 8-bit B=4096 37.9 against 39.2 us, and equal or
+// better at every size from 2^26 to 2^28 for both code widths).  The kernels still take the
+// parameter, and the nested workspace is sized for up to 2^kMaxLog2Tiles tiles.
 int quantize_log2tiles(int64_t n, const bq::PreparedTable& t) {
+  (void)n;
   (void)t;
-  const int64_t tiles = (n + bq::kQuantTileElems - 1) / bq::kQuantTileElems;
-  return tiles >= 4096 ? bq::kMaxLog2Tiles : 0;
+  return 0;
 }
 
 // Preparing a table (validation, thresholds, bucket LUT) costs more host time than a small
