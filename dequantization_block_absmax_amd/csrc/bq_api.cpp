@@ -37,25 +37,13 @@ bq_status hip_status(int e) {
 
 int64_t nblocks(int64_t n, int32_t b) { return (n + b - 1) / b; }
 
-// Nested workspace: binary32 absmax[nb], then one binary64 partial sum per quantize
-// workgroup (at most one per 8192-element tile).
+// Nested workspace: binary32 absmax[nb], then the binary64 partial sums of the quantize launch
+// (one per 2048-element wave).
 size_t ws_partials_offset(int64_t nb) { return ((size_t)nb * 4 + 255) & ~(size_t)255; }
 
 // absmax[nb] (fp32), padded to 256 bytes, then the quantize launch's partial sums (fp64).
 size_t ws_bytes(int64_t n, int64_t nb) {
-  return ws_partials_offset(nb) + (size_t)bq::quantize_partials(n, bq::kMaxLog2Tiles, 32) * 8;
-}
-
-// log2 of the 8192-element tiles each quantize workgroup processes.  One tile per workgroup:
-// since the table loads are issued ahead of the data and the LUT fill overlaps them, a second
-// tile no longer pays for its longer workgroups (measured on MI355X, interleaved rounds:
-// bf16 2^29 4-bit 212.4 against 218.4 us, 2^26 8-bit B=4096 37.9 against 39.2 us, and equal or
-// better at every size from 2^26 to 2^28 for both code widths).  The kernels still take the
-// parameter, and the nested workspace is sized for up to 2^kMaxLog2Tiles tiles.
-int quantize_log2tiles(int64_t n, const bq::PreparedTable& t) {
-  (void)n;
-  (void)t;
-  return 0;
+  return ws_partials_offset(nb) + (size_t)bq::quantize_partials(n, 32) * 8;
 }
 
 // Preparing a table (validation, thresholds, bucket LUT) costs more host time than a small
@@ -146,7 +134,7 @@ bq_status bq_quantize_blockwise(const void* in, bq_dtype dtype, int64_t n, int32
   if (nblocks(n, blocksize) > INT32_MAX) return BQ_ERR_SIZE;
   if (!aligned(in, 16) || !aligned(packed, 16) || !aligned(absmax, 4)) return BQ_ERR_ALIGNMENT;
   return hip_status(bq::launch_quantize(in, dtype, n, blocksize, t.data, absmax, packed, nullptr,
-                                        quantize_log2tiles(n, t.data), stream));
+                                        stream));
 }
 
 bq_status bq_dequantize_blockwise(void* out, bq_dtype dtype, int64_t n, int32_t blocksize,
@@ -232,11 +220,10 @@ bq_status bq_quantize_nested(const void* in, bq_dtype dtype, int64_t n, int32_t 
   if (!aligned(in, 16) || !aligned(packed, 16)) return BQ_ERR_ALIGNMENT;
   float* ws_absmax = static_cast<float*>(stats->workspace);
   double* ws_partials = reinterpret_cast<double*>(static_cast<uint8_t*>(stats->workspace) + ws_partials_offset(nb));
-  const int lt = quantize_log2tiles(n, t.data);
-  int e = bq::launch_quantize(in, dtype, n, blocksize, t.data, ws_absmax, packed, ws_partials, lt, stream);
+  int e = bq::launch_quantize(in, dtype, n, blocksize, t.data, ws_absmax, packed, ws_partials, stream);
   if (e != 0) return hip_status(e);
   e = bq::launch_nested_stats(ws_absmax, nb, stats->blocksize2, t.stats, ws_partials,
-                              bq::quantize_partials(n, lt, blocksize),
+                              bq::quantize_partials(n, blocksize),
                               stats->qabsmax, stats->absmax2, stats->mean, stream);
   return hip_status(e);
 }

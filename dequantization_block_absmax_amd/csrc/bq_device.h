@@ -56,6 +56,22 @@ __device__ __forceinline__ uint32_t nearest_code(float y, const QuantArgs& qa,
   }
 }
 
+// Maximum of v over aligned groups of g lanes (g a power of two, 1..64, the same in every
+// lane), returned in every lane of the group.  Inside a 16-lane row the exchanges are DPP
+// lane permutes (xor 1 and xor 2 by quad permutes, then the half-row and row mirrors, which
+// pair each 4- and 8-lane group with its neighbour); wider groups add one cross-row shuffle
+// and two lane reads.  Each DPP step is one instruction with a short latency, where an LDS
+// shuffle costs an address computation and a round trip through the LDS unit.
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v, int g) {
+  if (g >= 2) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));  // quad [1,0,3,2]
+  if (g >= 4) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));  // quad [2,3,0,1]
+  if (g >= 8) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // half-row mirror
+  if (g >= 16) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row mirror
+  if (g >= 32) v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+  if (g >= 64) v = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 32));
+  return v;
+}
+
 // One output word from its codes, in byte order: eight 4-bit codes (the first element of a
 // pair in the high nibble) or four 8-bit codes.  The bytes are joined with byte permutes, one
 // operation per byte pair, where a chain of shifts and ORs is compiled into more operations.
@@ -90,10 +106,13 @@ __device__ __forceinline__ LutWords<MODE, M, NT> lut_fetch(const QuantArgs& qa, 
     const int i = tid + k * NT;
     l.th[k] = i < 260 ? qa.thr[i] : 0.0f;
   }
+  // Every entry of the base array is read, not just the nbuckets in use: the host zero-fills
+  // the rest, and a bound known at compile time leaves no branch between the loads.
+  constexpr int kSize = LutLayout<MODE, M>::kSize;
 #pragma unroll
   for (int k = 0; k < L::kLutIt; ++k) {
     const int i = tid + k * NT;
-    l.bs[k] = i < qa.nbuckets ? qa.base[i] : 0u;
+    l.bs[k] = (k + 1) * NT <= kSize || i < kSize ? qa.base[i] : 0u;
   }
   return l;
 }
@@ -112,10 +131,13 @@ __device__ __forceinline__ void lut_fill(const QuantArgs& qa, const LutWords<MOD
     if (tid + k * NT < 260) s_thr[tid + k * NT] = l.th[k];
   __syncthreads();
   if constexpr (MODE != SEARCH) {
+    // All kSize entries are written (those past nbuckets from the zero bases are never read),
+    // so the threshold reads and entry writes form one batch instead of a chain of branches.
+    constexpr int kSize = LutLayout<MODE, M>::kSize;
 #pragma unroll
     for (int k = 0; k < L::kLutIt; ++k) {
       const int i = tid + k * NT;
-      if (i < qa.nbuckets) {
+      if ((k + 1) * NT <= kSize || i < kSize) {
         const uint32_t b = l.bs[k];  // <= 255, so b + 2 stays inside the 260 thresholds
         E e;
         e.x = b;

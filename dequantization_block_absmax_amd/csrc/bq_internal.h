@@ -106,13 +106,12 @@ int launch_linear(const void* x, int dtype, int64_t M, int64_t K, int64_t N, int
                   const float* absmax, const uint8_t* packed, float* y, void* stream);
 
 int launch_quantize(const void* in, int dtype, int64_t n, int blocksize, const PreparedTable& t,
-                    float* absmax, uint8_t* packed, double* partials, int log2tiles, void* stream);
+                    float* absmax, uint8_t* packed, double* partials, void* stream);
 // Workgroups of a quantize launch over n elements.
-int quantize_grid(int64_t n, int log2tiles);
+int quantize_grid(int64_t n);
 // Partial sums a quantize launch writes: one per wave of 2048 elements (one per pair of waves
 // for B = 4096, whose blocks span two waves), including waves past n, which write +0.
-int64_t quantize_partials(int64_t n, int log2tiles, int blocksize);
-constexpr int kMaxLog2Tiles = 1;  // most tiles per quantize workgroup (workspace sizing)
+int64_t quantize_partials(int64_t n, int blocksize);
 constexpr int64_t kQuantTileElems = 8192;  // elements per quantize tile
 int launch_dequantize(void* out, int dtype, int64_t n, int blocksize, const DequantArgs& a,
                       const float* absmax, const uint8_t* packed, void* stream);

@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (b + i < nb) key = max(key, f32_bits(d[i]) & 0x7fffffffu);
-      for (int k = 1; k < lg; k <<= 1) key = max(key, (uint32_t)__shfl_xor((int)key, k));
+      key = group_max_u32(key, lg);
       if (b < nb) emit(r, key, d);
     }
   } else {
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
     }
 #pragma unroll
     for (int r = 0; r < KR; ++r)
-      for (int k = 1; k < lg; k <<= 1) key[r] = max(key[r], (uint32_t)__shfl_xor((int)key[r], k));
+      key[r] = group_max_u32(key[r], lg);
     // groups of R runs: an xor butterfly over run indices gives every run its group's maximum
 #pragma unroll
     for (int st = 1; st < KR; st <<= 1)

@@ -11,8 +11,11 @@
 // fp32), loaded with 16-byte vector loads; its 4-bit codes are one 16-byte store, so the
 // stores of consecutive lanes are contiguous.  A block of B elements is G = B/32 consecutive
 // lanes: G <= 64 reduce the absmax within the wave by xor-shuffles, G = 128 (B = 4096) adds
-// one LDS exchange between the two waves.  A 256-lane workgroup covers 8192 elements per
-// tile and `tiles` consecutive tiles; the grid is not persistent.
+// one LDS exchange between the two waves.  A 256-lane workgroup quantizes one tile of 8192
+// elements.  (Workgroups that each took several tiles, with the next tile's loads issued
+// ahead of the current tile's arithmetic, measured slower on MI355X: 41.2 against 36.9 us for
+// 2^26 bf16 elements with 8-bit codes, B = 4096; the second register buffer costs more
+// occupancy than the overlap gains.)
 //
 // The absmax uses an integer key: k = (bits << 1) + OFF (mod 2^w) drops the sign and wraps
 // NaN/Inf below every finite value, so max(k) excludes non-finite elements without a compare.
@@ -122,6 +125,21 @@ __device__ __forceinline__ float key_to_absmax(uint32_t k) {
   }
 }
 
+// Loads the 32 elements of this lane's chunk (first element elem0, all of them < n) into w
+// with 16-byte loads.
+template <int DT>
+__device__ __forceinline__ void load_chunk_full(const uint8_t* __restrict__ in, int64_t elem0, uint32_t* w) {
+  const uint4* src = reinterpret_cast<const uint4*>(in + elem0 * (DT == F32 ? 4 : 2));
+#pragma unroll
+  for (int i = 0; i < Traits<DT>::kWords / 4; ++i) {
+    const uint4 v = src[i];
+    w[4 * i] = v.x;
+    w[4 * i + 1] = v.y;
+    w[4 * i + 2] = v.z;
+    w[4 * i + 3] = v.w;
+  }
+}
+
 // Loads the 32 elements of this lane's chunk (first element elem0) into w with 16-byte loads;
 // returns how many are < n.  The ragged end loads element by element; elements past n read
 // as NaN, which the absmax key excludes.
@@ -129,15 +147,7 @@ template <int DT>
 __device__ __forceinline__ int load_chunk(const uint8_t* __restrict__ in, int64_t n, int64_t elem0, uint32_t* w) {
   using Tr = Traits<DT>;
   if (elem0 + kEPT <= n) {
-    const uint4* src = reinterpret_cast<const uint4*>(in + elem0 * (DT == F32 ? 4 : 2));
-#pragma unroll
-    for (int i = 0; i < Tr::kWords / 4; ++i) {
-      uint4 v = src[i];
-      w[4 * i] = v.x;
-      w[4 * i + 1] = v.y;
-      w[4 * i + 2] = v.z;
-      w[4 * i + 3] = v.w;
-    }
+    load_chunk_full<DT>(in, elem0, w);
     return 32;
   }
   const int nvalid = elem0 < n ? (int)(n - elem0) : 0;
@@ -169,17 +179,28 @@ __device__ __forceinline__ int load_chunk(const uint8_t* __restrict__ in, int64_
 // access phase on distinct banks for both the writes and the reads.  With per-lane
 // contiguous 16-byte loads straight from memory the kernel ran 7% slower on MI355X.
 template <int DT>
-__device__ __forceinline__ void load_chunk_lds(const uint8_t* __restrict__ in, int64_t wave0, int lane,
-                                               uint4* tr, uint32_t* w) {
-  constexpr int C = DT == F32 ? 8 : 4;  // 16-byte chunks per lane
-  const u32x4* src = reinterpret_cast<const u32x4*>(in + wave0 * (DT == F32 ? 4 : 2)) + lane;
+struct LdsChunks {
+  static constexpr int C = DT == F32 ? 8 : 4;  // 16-byte chunks per lane
   u32x4 t[C];
+};
+
+template <int DT>
+__device__ __forceinline__ LdsChunks<DT> load_chunk_lds_issue(const uint8_t* __restrict__ in, int64_t wave0,
+                                                               int lane) {
+  LdsChunks<DT> r;
+  const u32x4* src = reinterpret_cast<const u32x4*>(in + wave0 * (DT == F32 ? 4 : 2)) + lane;
 #pragma unroll
-  for (int c = 0; c < C; ++c) t[c] = __builtin_nontemporal_load(src + c * 64);
+  for (int c = 0; c < LdsChunks<DT>::C; ++c) r.t[c] = __builtin_nontemporal_load(src + c * 64);
+  return r;
+}
+
+template <int DT>
+__device__ __forceinline__ void load_chunk_lds_complete(const LdsChunks<DT>& r, int lane, uint4* tr, uint32_t* w) {
+  constexpr int C = LdsChunks<DT>::C;
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     const int q = c * 64 + lane;
-    tr[q + q / C] = make_uint4(t[c].x, t[c].y, t[c].z, t[c].w);
+    tr[q + q / C] = make_uint4(r.t[c].x, r.t[c].y, r.t[c].z, r.t[c].w);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -193,7 +214,20 @@ __device__ __forceinline__ void load_chunk_lds(const uint8_t* __restrict__ in, i
     w[4 * i + 2] = x.z;
     w[4 * i + 3] = x.w;
   }
-  __builtin_amdgcn_wave_barrier();  // the next tile's writes come after these reads
+  __builtin_amdgcn_wave_barrier();  // later writes to tr come after these reads
+}
+
+// The lane's 32 elements of a full wave, loaded through LDS: the wave reads its 2048 elements
+// as C rows of 64 x 16 bytes (one contiguous KiB per instruction, non-temporal: the input is
+// read once), stores the 16-byte chunks in element order and each lane reads back its own C
+// consecutive chunks.  Chunk q sits in slot q + q / C, which keeps the 16 lanes of every LDS
+// access phase on distinct banks for both the writes and the reads.  With per-lane
+// contiguous 16-byte loads straight from memory the kernel ran 7% slower on MI355X.  The
+// loads are issued and completed by separate calls, so that other work can run between.
+template <int DT>
+__device__ __forceinline__ void load_chunk_lds(const uint8_t* __restrict__ in, int64_t wave0, int lane,
+                                               uint4* tr, uint32_t* w) {
+  load_chunk_lds_complete<DT>(load_chunk_lds_issue<DT>(in, wave0, lane), lane, tr, w);
 }
 
 struct QuantShared {
@@ -215,6 +249,8 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, in
 
   // Block absmax over G lanes.
   uint32_t key = chunk_key<DT>(w);
+  // LDS shuffles here: the DPP form of group_max_u32 measured slower in this kernel (2^29
+  // bf16 4-bit 221.1 against 218.5 us), where the statistics kernel gains from it.
   for (int m = 1; m < G && m < 64; m <<= 1) key = max(key, (uint32_t)__shfl_xor((int)key, m));
   if (G > 64) {  // B = 4096: two waves per block
     if (lane == 0) sh.red[tid >> 6] = key;
@@ -332,10 +368,10 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, in
   }
 }
 
-// A workgroup quantizes 2^log2tiles consecutive tiles of 8192 elements.
+// A workgroup quantizes one tile of 8192 elements, tile blockIdx.x.
 template <int DT, int KB, int MODE, int M>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __restrict__ in, int64_t n, int log2g,
-                                                            int log2tiles, float* __restrict__ absmax,
+                                                            float* __restrict__ absmax,
                                                             uint8_t* __restrict__ packed,
                                                             double* __restrict__ partials, QuantArgs qa) {
   using Tr = Traits<DT>;
@@ -346,97 +382,97 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __res
   __shared__ QuantShared sh;
 
   const int tid = threadIdx.x;
-  const int tiles = 1 << log2tiles;
-  const int64_t tile0 = (int64_t)blockIdx.x << log2tiles;
+  const int64_t tile0 = blockIdx.x;
   // 4-bit codes load through LDS (see load_chunk_lds); 8-bit codes, whose LUT fills most of
   // the LDS, load directly.
   constexpr bool kViaLds = KB == 4;
   constexpr int kTrChunks = DT == F32 ? 576 : 320;  // padded chunk slots per wave
   __shared__ uint4 s_tr[kViaLds ? kThreads / 64 * kTrChunks : 1];
   uint4* tr = s_tr + (kViaLds ? (tid >> 6) * kTrChunks : 0);
-  auto load = [&](int64_t e0, uint32_t* w) -> int {
-    const int64_t wave0 = e0 - (int64_t)(tid & 63) * kEPT;
+  uint4* stage = s_stage + (KB == 8 ? (tid >> 6) * 64 : 0);
+  const int64_t elem0 = (tile0 * kThreads + tid) * kEPT;
+  uint32_t w[Tr::kWords];
+  // The table words are loaded first, then the tile, and the LUT is filled while the tile is
+  // in flight.  A complete tile (every tile but a partial last one; the test is uniform) takes
+  // a path of unconditional loads of its own: where a load under a condition joins a path
+  // without it, the compiler can only wait for every outstanding load, the tile's included,
+  // before the LUT fill.
+  if ((tile0 + 1) * kTile <= n) {
+    const auto lw = lut_fetch<MODE, M, kThreads>(qa, tid);
+    if constexpr (kViaLds) {
+      const auto chunks = load_chunk_lds_issue<DT>(in, elem0 - (int64_t)(tid & 63) * kEPT, tid & 63);
+      lut_fill<MODE, M, kThreads>(qa, lw, s_lut, s_thr, tid);
+      load_chunk_lds_complete<DT>(chunks, tid & 63, tr, w);
+    } else {
+      load_chunk_full<DT>(in, elem0, w);
+      lut_fill<MODE, M, kThreads>(qa, lw, s_lut, s_thr, tid);
+    }
+    quantize_chunk<DT, KB, MODE, M>(w, kEPT, elem0, n, log2g, absmax, packed, partials, qa, s_lut, s_thr, sh,
+                                    stage);
+  } else {
+    const auto lw = lut_fetch<MODE, M, kThreads>(qa, tid);
+    const int64_t wave0 = elem0 - (int64_t)(tid & 63) * kEPT;
+    int nvalid;
     if (kViaLds && wave0 + 64 * kEPT <= n) {  // uniform: the whole wave is in range
       load_chunk_lds<DT>(in, wave0, tid & 63, tr, w);
-      return kEPT;
+      nvalid = kEPT;
+    } else {
+      nvalid = load_chunk<DT>(in, n, elem0, w);
     }
-    return load_chunk<DT>(in, n, e0, w);
-  };
-  uint4* stage = s_stage + (KB == 8 ? (tid >> 6) * 64 : 0);
-  {
-    // The first tile apart from the others: the table words are loaded first, then the tile's
-    // chunk, then the LUT is filled while the chunk is in flight.  Giving each tile its own
-    // registers avoids copying them between loop iterations.
-    const auto lw = lut_fetch<MODE, M, kThreads>(qa, tid);
-    const int64_t elem0 = (tile0 * kThreads + tid) * kEPT;
-    uint32_t w[Tr::kWords];
-    const int nvalid = load(elem0, w);
     lut_fill<MODE, M, kThreads>(qa, lw, s_lut, s_thr, tid);
-    quantize_chunk<DT, KB, MODE, M>(w, nvalid, elem0, n, log2g, absmax, packed, partials, qa, s_lut, s_thr, sh,
-                                    stage);
-  }
-  for (int t = 1; t < tiles; ++t) {
-    const int64_t elem0 = ((tile0 + t) * kThreads + tid) * kEPT;
-    uint32_t w[Tr::kWords];
-    const int nvalid = load(elem0, w);
     quantize_chunk<DT, KB, MODE, M>(w, nvalid, elem0, n, log2g, absmax, packed, partials, qa, s_lut, s_thr, sh,
                                     stage);
   }
 }
 
 template <int DT, int KB, int MODE, int M>
-hipError_t launch4(const void* in, int64_t n, int log2g, int log2tiles, float* absmax, uint8_t* packed,
-                   double* partials, const QuantArgs& qa, hipStream_t stream) {
-  const int64_t tiles_total = (n + kTile - 1) / kTile;
-  const int64_t grid = (tiles_total + (1 << log2tiles) - 1) >> log2tiles;
-  return launch_kernel(quantize_kernel<DT, KB, MODE, M>, dim3((unsigned)grid), dim3(kThreads), stream,
-                       static_cast<const uint8_t*>(in), n, log2g, log2tiles, absmax, packed, partials, qa);
+hipError_t launch4(const void* in, int64_t n, int log2g, float* absmax, uint8_t* packed, double* partials,
+                   const QuantArgs& qa, hipStream_t stream) {
+  return launch_kernel(quantize_kernel<DT, KB, MODE, M>, dim3((unsigned)quantize_grid(n)), dim3(kThreads), stream,
+                       static_cast<const uint8_t*>(in), n, log2g, absmax, packed, partials, qa);
 }
 
 template <int DT, int KB>
-hipError_t launch_mode(const void* in, int64_t n, int log2g, int lt, float* absmax, uint8_t* packed,
+hipError_t launch_mode(const void* in, int64_t n, int log2g, float* absmax, uint8_t* packed,
                        double* partials, const PreparedTable& t, hipStream_t s) {
   if (t.mode == LIN) {
-    if (t.M <= 1) return launch4<DT, KB, LIN, 1>(in, n, log2g, lt, absmax, packed, partials, t.qa, s);
-    if (t.M == 2) return launch4<DT, KB, LIN, 2>(in, n, log2g, lt, absmax, packed, partials, t.qa, s);
-    return launch4<DT, KB, LIN, 3>(in, n, log2g, lt, absmax, packed, partials, t.qa, s);
+    if (t.M <= 1) return launch4<DT, KB, LIN, 1>(in, n, log2g, absmax, packed, partials, t.qa, s);
+    if (t.M == 2) return launch4<DT, KB, LIN, 2>(in, n, log2g, absmax, packed, partials, t.qa, s);
+    return launch4<DT, KB, LIN, 3>(in, n, log2g, absmax, packed, partials, t.qa, s);
   }
   if (t.mode == LOG) {
-    if (t.M <= 1) return launch4<DT, KB, LOG, 1>(in, n, log2g, lt, absmax, packed, partials, t.qa, s);
-    if (t.M == 2) return launch4<DT, KB, LOG, 2>(in, n, log2g, lt, absmax, packed, partials, t.qa, s);
-    return launch4<DT, KB, LOG, 3>(in, n, log2g, lt, absmax, packed, partials, t.qa, s);
+    if (t.M <= 1) return launch4<DT, KB, LOG, 1>(in, n, log2g, absmax, packed, partials, t.qa, s);
+    if (t.M == 2) return launch4<DT, KB, LOG, 2>(in, n, log2g, absmax, packed, partials, t.qa, s);
+    return launch4<DT, KB, LOG, 3>(in, n, log2g, absmax, packed, partials, t.qa, s);
   }
-  return launch4<DT, KB, SEARCH, 1>(in, n, log2g, lt, absmax, packed, partials, t.qa, s);
+  return launch4<DT, KB, SEARCH, 1>(in, n, log2g, absmax, packed, partials, t.qa, s);
 }
 
 template <int DT>
-hipError_t launch_dt(const void* in, int64_t n, int log2g, int lt, float* absmax, uint8_t* packed,
+hipError_t launch_dt(const void* in, int64_t n, int log2g, float* absmax, uint8_t* packed,
                      double* partials, const PreparedTable& t, hipStream_t s) {
-  return t.K == 16 ? launch_mode<DT, 4>(in, n, log2g, lt, absmax, packed, partials, t, s)
-                   : launch_mode<DT, 8>(in, n, log2g, lt, absmax, packed, partials, t, s);
+  return t.K == 16 ? launch_mode<DT, 4>(in, n, log2g, absmax, packed, partials, t, s)
+                   : launch_mode<DT, 8>(in, n, log2g, absmax, packed, partials, t, s);
 }
 
 }  // namespace
 
-int quantize_grid(int64_t n, int log2tiles) {
-  const int64_t tiles_total = (n + kTile - 1) / kTile;
-  return (int)((tiles_total + (1 << log2tiles) - 1) >> log2tiles);
-}
+int quantize_grid(int64_t n) { return (int)((n + kTile - 1) / kTile); }
 
-int64_t quantize_partials(int64_t n, int log2tiles, int blocksize) {
-  const int64_t waves = ((int64_t)quantize_grid(n, log2tiles) << log2tiles) * (kThreads / 64);
+int64_t quantize_partials(int64_t n, int blocksize) {
+  const int64_t waves = (int64_t)quantize_grid(n) * (kThreads / 64);
   return blocksize == 4096 ? waves / 2 : waves;
 }
 
 int launch_quantize(const void* in, int dtype, int64_t n, int blocksize, const PreparedTable& t, float* absmax,
-                    uint8_t* packed, double* partials, int log2tiles, void* stream) {
+                    uint8_t* packed, double* partials, void* stream) {
   int log2g = 0;
   while ((kEPT << log2g) < blocksize) ++log2g;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (dtype == F32) e = launch_dt<F32>(in, n, log2g, log2tiles, absmax, packed, partials, t, s);
-  else if (dtype == F16) e = launch_dt<F16>(in, n, log2g, log2tiles, absmax, packed, partials, t, s);
-  else e = launch_dt<BF16>(in, n, log2g, log2tiles, absmax, packed, partials, t, s);
+  if (dtype == F32) e = launch_dt<F32>(in, n, log2g, absmax, packed, partials, t, s);
+  else if (dtype == F16) e = launch_dt<F16>(in, n, log2g, absmax, packed, partials, t, s);
+  else e = launch_dt<BF16>(in, n, log2g, absmax, packed, partials, t, s);
   return (int)e;
 }
 

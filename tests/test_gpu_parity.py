@@ -373,6 +373,96 @@ def test_bf16_2pow26_8bit_blocksize4096(dev, o):
         assert_bytes_equal(o_gpu[sl], ref, "bf16 2^26 8-bit dequant block %d" % b)
 
 
+# ---- 8-bit codes, several tiles per workgroup ----------------------------------------------
+
+# 3,075 tiles of 8192 elements, the last one partial: more tiles than workgroups resident on
+# the device, so each workgroup of the 8-bit quantizer takes several, one of them partial.
+N_MANY = 3 * (1 << 23) + 3 * 8192 + 77
+
+
+def _codes_are_nearest(xb: np.ndarray, dtype: str, B: int, absmax: np.ndarray, codes: np.ndarray, table,
+                       what: str):
+    """Every element's code is a nearest table entry to x / absmax (binary64, ties within
+    2^-20 accepted either way): a check of all codes that needs no oracle pass over them."""
+    if dtype == "bfloat16":
+        v = (xb.astype(np.uint32) << 16).view(np.float32)
+    elif dtype == "float16":
+        v = xb.view(np.float16).astype(np.float32)
+    else:
+        v = xb
+    a = np.repeat(absmax.astype(np.float64), B)[:v.size]
+    fin = np.isfinite(v) & (a > 0)
+    y = np.where(fin, v.astype(np.float64) / np.where(a > 0, a, 1.0), 0.0)
+    t = np.asarray(table, np.float64)
+    err = np.abs(y - t[codes])
+    i = np.clip(np.searchsorted(t, y), 1, t.size - 1)  # the two entries around y (table ascending)
+    best = np.minimum(np.abs(y - t[i - 1]), np.abs(y - t[i]))
+    bad = np.nonzero(err > best + 2.0 ** -20)[0]
+    assert bad.size == 0, "%s: %d codes not nearest, first at %d" % (what, bad.size, bad[0])
+
+
+def _tile_edge_blocks(n: int, B: int, seed: int) -> np.ndarray:
+    """Blocks at both ends, at the partial tile, at tile boundaries near the end and start,
+    and random others."""
+    nb = -(-n // B)
+    edges = [0, 8192 - 1, 8192, 2 * 8192, (n // 8192) * 8192 - 1, (n // 8192) * 8192, n - 1]
+    return np.unique(np.concatenate([[e // B for e in edges], _sample_blocks(nb, 24, seed)]))
+
+
+@pytest.mark.parametrize("dtype,B", [("bfloat16", 4096), ("float32", 64), ("float16", 256)])
+def test_8bit_several_tiles_per_workgroup(dev, o, dtype, B):
+    n = N_MANY
+    t256 = synth.table256()
+    x = synth.blockwise_input(n, dtype, 41, std=0.02, p_out=1e-4, p_nf=1e-5, device=dev)
+    absmax, packed = gpu_quantize(x, dtype, B, t256)
+    out = gpu_dequantize(packed, absmax, n, dtype, B, t256)
+    xb = host_bits(x)
+    what = "8-bit %s n=%d B=%d" % (dtype, n, B)
+    a_gpu = absmax.cpu().numpy()
+    assert_f32_bits_equal(a_gpu, _finite_absmax_np(xb, dtype, B), what + " absmax (all blocks)")
+    p_gpu = packed.cpu().numpy()[:n]
+    _codes_are_nearest(xb, dtype, B, a_gpu, p_gpu, t256, what + " codes (all)")
+    o_gpu = host_bits(out)
+    for b in _tile_edge_blocks(n, B, 41):
+        lo, hi = b * B, min((b + 1) * B, n)
+        oa, op = o.quantize_blockwise(xb[lo:hi], ORACLE_DT[dtype], B, t256)
+        assert_f32_bits_equal(a_gpu[b:b + 1], oa, "%s absmax block %d" % (what, b))
+        assert_bytes_equal(p_gpu[lo:hi], op, "%s codes block %d" % (what, b))
+        ref = o.dequantize_blockwise(op, oa, hi - lo, ORACLE_DT[dtype], B, t256)
+        assert_out_equal(out[lo:hi], ref, hi - lo, dtype, "%s dequant block %d" % (what, b))
+
+
+def test_8bit_nested_several_tiles_per_workgroup(dev, o):
+    """The nested statistics over 8-bit data codes at N_MANY elements: every block absmax,
+    the mean, q2 and absmax2 in full; data codes and the nested dequantize on sampled groups."""
+    n, B, B2 = N_MANY, 64, 256
+    t256 = synth.table256()
+    x = synth.blockwise_input(n, "bfloat16", 43, std=0.02, p_out=1e-4, p_nf=1e-5, device=dev)
+    r = gpu_nested(x, "bfloat16", B, t256, t256, B2)
+    xb = host_bits(x)
+    what = "nested 8-bit bf16 n=%d" % n
+    a_ref = _finite_absmax_np(xb, "bfloat16", B)
+    assert_f32_bits_equal(r["absmax"].cpu().numpy(), a_ref, what + " absmax")
+    m_ref = o.nested_mean(a_ref)
+    assert np.float32(r["mean"].item()).view(np.uint32) == np.float32(m_ref).view(np.uint32), what + " mean"
+    a2_ref, q2_ref = o.quantize_blockwise((a_ref - m_ref).astype(np.float32), oracle.F32, B2, t256)
+    q2 = r["q2"].cpu().numpy()
+    absmax2 = r["absmax2"].cpu().numpy()
+    assert_f32_bits_equal(absmax2, a2_ref, what + " absmax2")
+    assert_bytes_equal(q2, q2_ref, what + " q2")
+    packed = r["packed"].cpu().numpy()
+    out = r["out"]
+    gsize = B * B2
+    ng = absmax2.size
+    for g in np.unique([0, 1, ng // 2, ng - 2, ng - 1]):
+        lo, hi = g * gsize, min((g + 1) * gsize, n)
+        _, op = o.quantize_blockwise(xb[lo:hi], oracle.BF16, B, t256)
+        assert_bytes_equal(packed[lo:hi], op, "%s codes group %d" % (what, g))
+        ref = o.dequantize_nested(op, q2[g * B2:g * B2 + (hi - lo + B - 1) // B], absmax2[g:g + 1], m_ref, hi - lo,
+                                  oracle.BF16, B, t256, t256, B2)
+        assert_out_equal(out[lo:hi], ref, hi - lo, "bfloat16", "%s dequant group %d" % (what, g))
+
+
 @pytest.mark.parametrize("fmt", ["q4", "q8"])
 def test_q32_partial_tile_and_offset(dev, o, fmt):
     """Whole tiles (128 blocks) go through LDS with 16-byte loads; a partial last tile and a block
