@@ -262,9 +262,9 @@ def detail_configs(bq, synth, torch, dev, peak):
 
 def fused_linear(bq, synth, torch, dev, t16, t256, peak, N=14336, K=4096, B=64, sets=24):
     """bq_linear_blockwise at a decode shape (a 14336 x 4096 weight, bf16 activations) for M = 1
-    and 4, 4- and 8-bit codes, with the weights rotated over enough sets to miss the 256 MB
-    last-level cache.  Beside it, the unfused path: dequantize to bf16 with this library, then
-    torch's matmul."""
+    and 4, and bq_gemm_blockwise for M = 16, 64 and 256, 4- and 8-bit codes, with the weights
+    rotated over enough sets to miss the 256 MB last-level cache.  Beside each, the unfused
+    path: dequantize to bf16 with this library, then torch's matmul."""
     out = {}
     g = torch.Generator(device=dev)
     g.manual_seed(11)
@@ -296,6 +296,32 @@ def fused_linear(bq, synth, torch, dev, t16, t256, peak, N=14336, K=4096, B=64, 
             byts = per + 4 * (N * K // B) + 2 * M * K + 4 * M * N
             out["linear %dx%d %d-bit B=%d M=%d bf16" % (N, K, KB, B, M)] = dict(
                 us=round(f_ms * 1e3, 2), rw_gbs=round(byts / f_ms / 1e6, 1),
+                pct_hbm_peak=round(100 * byts / f_ms / 1e6 / peak, 1),
+                unfused_us=round(u_ms * 1e3, 2), speedup_vs_unfused=round(u_ms / f_ms, 2))
+        for M in (16, 64, 256):  # bq_gemm_blockwise: 16-bit weights on the matrix cores
+            x = torch.randn(M, K, device=dev, generator=g).to(torch.bfloat16)
+            y = torch.empty(M, N, device=dev)
+            i = [0]
+
+            def fused():
+                p, a = ws[i[0] % sets]
+                i[0] += 1
+                bq.check(bq.bq_gemm_blockwise(x, bq.BQ_BF16, M, K, N, B, table, a, p, y))
+
+            def unfused():
+                p, a = ws[i[0] % sets]
+                i[0] += 1
+                bq.check(bq.bq_dequantize_blockwise(wbf, bq.BQ_BF16, N * K, B, table, a, p))
+                torch.matmul(x, wbf.t())
+            fused()
+            unfused()
+            torch.cuda.synchronize()
+            f_ms = statistics.median(time_calls(fused, torch, 24) for _ in range(ROUNDS))
+            u_ms = statistics.median(time_calls(unfused, torch, 24) for _ in range(ROUNDS))
+            byts = per + 4 * (N * K // B) + 2 * M * K + 4 * M * N
+            out["gemm %dx%d %d-bit B=%d M=%d bf16" % (N, K, KB, B, M)] = dict(
+                us=round(f_ms * 1e3, 2), tflops=round(2 * M * N * K / f_ms / 1e9, 1),
+                pct_bf16_mfma_peak=round(100 * 2 * M * N * K / f_ms / 1e9 / 2500.0, 1),
                 pct_hbm_peak=round(100 * byts / f_ms / 1e6 / peak, 1),
                 unfused_us=round(u_ms * 1e3, 2), speedup_vs_unfused=round(u_ms / f_ms, 2))
         del ws, wbf

@@ -23,7 +23,7 @@ BQ_Q32_Q4, BQ_Q32_Q8 = 0, 1
 
 EXPORTS = ("bq_quantize_blockwise", "bq_dequantize_blockwise", "bq_quantize_nested",
            "bq_dequantize_nested", "bq_dequant_q32", "bq_nested_workspace_bytes", "bq_status_string",
-           "bq_debug_nearest_codes", "bq_last_hip_error", "bq_linear_blockwise")
+           "bq_debug_nearest_codes", "bq_last_hip_error", "bq_linear_blockwise", "bq_gemm_blockwise")
 
 
 class BQError(RuntimeError):
@@ -66,6 +66,7 @@ def _load() -> ctypes.CDLL:
         "bq_dequantize_nested": [vp, st, i64, i32, tp, sp, vp, vp],
         "bq_dequant_q32": [vp, st, i64, i32, st, vp, vp],
         "bq_linear_blockwise": [vp, st, i64, i64, i64, i32, tp, vp, vp, vp, vp],
+        "bq_gemm_blockwise": [vp, st, i64, i64, i64, i32, tp, vp, vp, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -184,6 +185,12 @@ def bq_linear_blockwise(x, dtype, M: int, K: int, N: int, blocksize: int, table,
                         stream=None) -> int:
     return _lib.bq_linear_blockwise(_addr(x), dtype_code(dtype), int(M), int(K), int(N), int(blocksize),
                                     _table_ptr(table), _addr(absmax), _addr(packed), _addr(y), _stream(stream))
+
+
+def bq_gemm_blockwise(x, dtype, M: int, K: int, N: int, blocksize: int, table, absmax, packed, y,
+                      stream=None) -> int:
+    return _lib.bq_gemm_blockwise(_addr(x), dtype_code(dtype), int(M), int(K), int(N), int(blocksize),
+                                  _table_ptr(table), _addr(absmax), _addr(packed), _addr(y), _stream(stream))
 
 
 def bq_nested_workspace_bytes(n: int, blocksize: int, blocksize2: int = 256) -> int:

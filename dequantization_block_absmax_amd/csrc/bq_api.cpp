@@ -178,6 +178,29 @@ bq_status bq_linear_blockwise(const void* x, bq_dtype dtype, int64_t M, int64_t 
   return hip_status(bq::launch_linear(x, dtype, M, K, N, blocksize, a, absmax, packed, y, stream));
 }
 
+bq_status bq_gemm_blockwise(const void* x, bq_dtype dtype, int64_t M, int64_t K, int64_t N, int32_t blocksize,
+                            const bq_code_table* code_table, const float* absmax, const uint8_t* packed,
+                            float* y, hipStream_t stream) {
+  if (dtype != BQ_BF16 && dtype != BQ_F16) return BQ_ERR_DTYPE;
+  // grid rows: ceil(M / 64) <= 65535
+  if (M < 1 || M > 65535 * 64 || K <= 0 || K % 64 != 0 || N < 0) return BQ_ERR_SIZE;
+  if (N > 0 && K > INT64_MAX / N) return BQ_ERR_SIZE;
+  if (M > INT64_MAX / K || (N > 0 && M > INT64_MAX / N)) return BQ_ERR_SIZE;
+  if (!valid_blocksize(blocksize)) return BQ_ERR_BLOCKSIZE;
+  Tables t;
+  bq_status st = check_table(code_table, &t.data);
+  if (st != BQ_OK) return st;
+  if (N == 0) return BQ_OK;
+  if (x == nullptr || absmax == nullptr || packed == nullptr || y == nullptr) return BQ_ERR_NULL;
+  if (nblocks(N * K, blocksize) > INT32_MAX || (N + 63) / 64 > INT32_MAX) return BQ_ERR_SIZE;  // 64 columns a workgroup
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(absmax, 4) || !aligned(y, 4)) return BQ_ERR_ALIGNMENT;
+  bq::DequantArgs a;
+  memset(&a, 0, sizeof(a));
+  memcpy(a.c, t.data.c, sizeof(float) * t.data.K);
+  a.K = t.data.K;
+  return hip_status(bq::launch_gemm(x, dtype, M, K, N, blocksize, a, absmax, packed, y, stream));
+}
+
 size_t bq_nested_workspace_bytes(int64_t n, int32_t blocksize, int32_t blocksize2) {
   (void)blocksize2;
   if (n <= 0 || !valid_blocksize(blocksize)) return 0;

@@ -105,6 +105,10 @@ namespace bq {
 int launch_linear(const void* x, int dtype, int64_t M, int64_t K, int64_t N, int blocksize, const DequantArgs& da,
                   const float* absmax, const uint8_t* packed, float* y, void* stream);
 
+// Fused dequantize + GEMM on MFMA (k_gemm.hip): y (M x N, binary32) = x . W16^T, x bf16/fp16.
+int launch_gemm(const void* x, int dtype, int64_t M, int64_t K, int64_t N, int blocksize, const DequantArgs& da,
+                const float* absmax, const uint8_t* packed, float* y, void* stream);
+
 int launch_quantize(const void* in, int dtype, int64_t n, int blocksize, const PreparedTable& t,
                     float* absmax, uint8_t* packed, double* partials, void* stream);
 // Workgroups of a quantize launch over n elements.

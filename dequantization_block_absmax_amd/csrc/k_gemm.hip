@@ -1,0 +1,269 @@
+// k_gemm.hip -- fused dequantize + GEMM on the gfx950 matrix cores, for batches of rows:
+// y = x . W16^T, where W16 = RN16(fl32(c[q] * a)) is exactly the 16-bit tensor that
+// bq_dequantize_blockwise writes for W, formed in registers and never stored (the
+// 16-bit-activation, 4-bit-weight GEMM of "stable-diffusion.cpp PR 2278", Summary, on the
+// blockwise codes of this library).
+//
+//   W: N x K row-major, quantized blockwise over its flat index (element (n, k) is flat
+//      element n*K + k); x: M x K row-major, bf16 or fp16 (the type of W16 as well).
+//   y[m][n] = sum_k x[m][k] * W16[n][k], products exact in binary32, accumulated in binary32.
+//
+// Work decomposition.  A workgroup owns an output tile of 32*MT rows of x by 32*NT rows of
+// W, and its 4 waves split K in chunks of 64 (wave w takes chunks w, w + 4, ...).  Each wave
+// computes the whole tile for its chunks with v_mfma_f32_32x32x16 (bf16 or f16): lane l
+// (g = l / 32, r = l % 32) supplies A[r][8g + t] and B[8g + t][r], t < 8, and holds
+// C[8 (v / 4) + 4 g + v % 4][r] in accumulator element v.  Lane group g takes the 32
+// consecutive k from k0 + 32 g of its row: 64 bytes of x (four 16-byte loads) and 16 bytes of
+// 4-bit codes (32 of 8-bit), which lie in one block (B >= 32), so one scale serves them.  MFMA
+// step s (0..3) uses the lane's k0 + 32 g + 8 s .. + 7 on both operands: the instruction sums
+// over 16 values of k, and giving A and B the same assignment of k to lanes and steps leaves
+// the product unchanged while every lane feeds the matrix core from its own loads.  The three
+// other waves' tiles are added to wave 0's through LDS, in wave order, and wave 0 stores y.
+#include <hip/hip_runtime.h>
+
+#include "bq_internal.h"
+#include "bq_launch.h"
+
+namespace bq {
+namespace {
+
+constexpr int kChunk = 64;  // k per wave and chunk (two lane groups of 32)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32x32x16(uint4 a, uint4 b, f32x16 c) {
+  if constexpr (DT == BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+}
+
+// Two weights as the 16-bit dequantize stores them: the binary32 products rounded once to the
+// 16-bit type (round to nearest even, one packed conversion), first value in the low half.
+template <int DT>
+__device__ __forceinline__ uint32_t weight_pair(float c0, float c1, float a) {
+  f32x2 v = {c0 * a, c1 * a};
+  if constexpr (DT == BF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  } else {
+    // rounded to binary32 first: a fused mixed-precision fma would round the product once
+    asm("" : "+v"(v));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+}
+
+// B fragment of MFMA step s: the 8 weights of k offsets 8s .. 8s + 7 of the lane's 32.
+//   4-bit: word s of the 16 code bytes; byte b holds offset 2b (high nibble) and 2b + 1.
+//   8-bit: words 2s and 2s + 1 of the 32 code bytes, one code per byte.
+template <int DT, int KB>
+__device__ __forceinline__ uint4 weight_frag(const uint32_t* codes, int s, float a, const float2* s_pair,
+                                             const float* s_c) {
+  uint32_t w[4];
+  if constexpr (KB == 4) {
+    const uint32_t word = codes[s];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float2 p = s_pair[(word >> (8 * b)) & 0xffu];
+      w[b] = weight_pair<DT>(p.x, p.y, a);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t word = codes[2 * s + h];
+      w[2 * h] = weight_pair<DT>(s_c[word & 0xffu], s_c[(word >> 8) & 0xffu], a);
+      w[2 * h + 1] = weight_pair<DT>(s_c[(word >> 16) & 0xffu], s_c[word >> 24], a);
+    }
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Compiler barrier between a prefetch and the arithmetic on the current chunk (nothing waits
+// for the loads here).  The asm memory clobber keeps the prefetch from sinking to its use in
+// the next iteration; the scheduling barrier keeps arithmetic on the current chunk, which
+// would wait for that chunk's loads, from being scheduled before the prefetch is issued.
+__device__ __forceinline__ void prefetch_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One chunk's operands for a lane: x (MT row tiles x four 16-byte pieces), codes (16 or 32
+// bytes per W row tile) and the block scale of each W row tile.
+template <int KB, int MT, int NT>
+struct Chunk {
+  uint4 xa[MT][4];
+  uint4 codes[NT][KB == 4 ? 1 : 2];
+  float a[NT];
+};
+
+template <int DT, int KB, int MT, int NT, int NW>
+// x, absmax and packed are not declared __restrict__: the compiler barriers below must order
+// their loads, which it may move across a barrier for memory it knows cannot change.
+__global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* x, int64_t M, int64_t K, int64_t N,
+                                                        int log2b, const float* absmax, const uint8_t* packed,
+                                                        float* __restrict__ y, DequantArgs da) {
+  constexpr int kTiles = MT * NT;
+  __shared__ float2 s_pair[KB == 4 ? 256 : 1];
+  __shared__ float s_c[KB == 8 ? 256 : 1];
+  __shared__ float s_red[(NW - 1) * kTiles * 16 * 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // wave-uniform in a scalar register: the chunk loop below then branches on scalars, where a
+  // loop the compiler takes for divergent joins exec masks and waits for every load there
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, r = lane & 31;
+  if (tid < 256) {  // 256 table entries (a workgroup has 256 or 512 threads)
+    if constexpr (KB == 4) s_pair[tid] = make_float2(da.c[tid >> 4], da.c[tid & 15]);
+    else s_c[tid] = da.c[tid];
+  }
+  __syncthreads();
+
+  const int64_t m0 = (int64_t)blockIdx.y * 32 * MT;
+  const int64_t n0 = (int64_t)blockIdx.x * 32 * NT;
+  // Rows past M or N read the last row instead (every load is unconditional) and are never
+  // stored.
+  const uint8_t* xrow[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) xrow[i] = x + (min(m0 + 32 * i + r, M - 1) * K + 32 * g) * 2;
+  int64_t wflat[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) wflat[j] = min(n0 + 32 * j + r, N - 1) * K + 32 * g;
+
+  f32x16 acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  // Chunks wave, wave + 4, ...: the loads of a wave's next chunk are issued before its current
+  // chunk is dequantized and multiplied (M = 8 at 14336 x 4096: 32.3 us with each chunk's
+  // loads waited for in its own iteration).  The chunk index is clamped instead of tested (the
+  // last prefetch reads the wave's last chunk again), so no load sits under a condition.
+  const int64_t nchunks = K / kChunk;
+  const int64_t my_chunks = (nchunks - wave + NW - 1) / NW;  // 0 when wave >= nchunks
+  auto load_chunk = [&](int64_t i, Chunk<KB, MT, NT>& c) {
+    const int64_t k0 = min((int64_t)wave + (int64_t)NW * i, nchunks - 1) * kChunk;
+#pragma unroll
+    for (int ii = 0; ii < MT; ++ii)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) c.xa[ii][s] = *reinterpret_cast<const uint4*>(xrow[ii] + (k0 + 8 * s) * 2);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int64_t f = wflat[j] + k0;
+      if constexpr (KB == 4) {
+        c.codes[j][0] = *reinterpret_cast<const uint4*>(packed + (f >> 1));
+      } else {
+        c.codes[j][0] = *reinterpret_cast<const uint4*>(packed + f);
+        c.codes[j][1] = *reinterpret_cast<const uint4*>(packed + f + 16);
+      }
+      c.a[j] = absmax[f >> log2b];
+    }
+  };
+  auto multiply = [&](const Chunk<KB, MT, NT>& c) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint4 b[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        b[j] = weight_frag<DT, KB>(reinterpret_cast<const uint32_t*>(c.codes[j]), s, c.a[j], s_pair, s_c);
+#pragma unroll
+      for (int ii = 0; ii < MT; ++ii)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[ii][j] = mfma32x32x16<DT>(c.xa[ii][s], b[j], acc[ii][j]);
+    }
+  };
+  // Two buffers alternate (unrolled by two): copying the prefetched chunk into the current one
+  // would make the compiler wait for the prefetch at the end of every iteration.
+  // The loop takes two chunks per iteration and has one exit, at the top: a break between its
+  // halves would meet the back edge with the break path's prefetch still outstanding, and the
+  // compiler would then wait for every load at the top of each iteration.
+  Chunk<KB, MT, NT> ca, cb;
+  load_chunk(0, ca);
+  int64_t i = 0;
+  for (; i + 1 < my_chunks; i += 2) {
+    load_chunk(i + 1, cb);
+    prefetch_fence();
+    multiply(ca);
+    load_chunk(i + 2, ca);
+    prefetch_fence();
+    multiply(cb);
+  }
+  if (i < my_chunks) multiply(ca);  // an odd count: the last chunk, already loaded
+
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s_red[(((wave - 1) * kTiles + i * NT + j) * 16 + v) * 64 + lane] = acc[i][j][v];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int64_t col = n0 + 32 * j + r;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float sum = acc[i][j][v];
+#pragma unroll
+          for (int w = 0; w < NW - 1; ++w) sum += s_red[((w * kTiles + i * NT + j) * 16 + v) * 64 + lane];
+          const int64_t row = m0 + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+          if (row < M && col < N) y[row * N + col] = sum;
+        }
+      }
+  }
+}
+
+// 64 rows of W per workgroup (two column tiles: x is loaded once for both) and 4 waves
+// splitting K (measured against 32 rows and against 8 waves at 14336 x 4096: equal or faster
+// from M = 32 up, 21.7 against 17.4 us at M = 8).
+template <int DT, int KB, int MT>
+hipError_t launch_mt(const void* x, int64_t M, int64_t K, int64_t N, int log2b, const float* absmax,
+                     const uint8_t* packed, float* y, const DequantArgs& da, hipStream_t s) {
+  constexpr int NT = 2, NW = 4;
+  const dim3 grid((unsigned)((N + 32 * NT - 1) / (32 * NT)), (unsigned)((M + 32 * MT - 1) / (32 * MT)));
+  return launch_kernel(gemm_kernel<DT, KB, MT, NT, NW>, grid, dim3(64 * NW), s, static_cast<const uint8_t*>(x), M,
+                       K, N, log2b, absmax, packed, y, da);
+}
+
+template <int DT, int KB>
+hipError_t launch_kb(const void* x, int64_t M, int64_t K, int64_t N, int log2b, const float* absmax,
+                     const uint8_t* packed, float* y, const DequantArgs& da, hipStream_t s) {
+  // 32, 64 or 128 rows of x per workgroup: fewer rows waste matrix-core work on padding, more
+  // rows share each dequantized weight (at 14336 x 4096, 128-row tiles: M = 128 49.1 against
+  // 52.6 us with 64-row tiles, equal at M <= 64)
+  if (M <= 32) return launch_mt<DT, KB, 1>(x, M, K, N, log2b, absmax, packed, y, da, s);
+  if (M <= 64) return launch_mt<DT, KB, 2>(x, M, K, N, log2b, absmax, packed, y, da, s);
+  return launch_mt<DT, KB, 4>(x, M, K, N, log2b, absmax, packed, y, da, s);
+}
+
+}  // namespace
+
+int launch_gemm(const void* x, int dtype, int64_t M, int64_t K, int64_t N, int blocksize, const DequantArgs& da,
+                const float* absmax, const uint8_t* packed, float* y, void* stream) {
+  int log2b = 0;
+  while ((1 << log2b) < blocksize) ++log2b;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == BF16)
+    e = da.K == 16 ? launch_kb<BF16, 4>(x, M, K, N, log2b, absmax, packed, y, da, s)
+                   : launch_kb<BF16, 8>(x, M, K, N, log2b, absmax, packed, y, da, s);
+  else
+    e = da.K == 16 ? launch_kb<F16, 4>(x, M, K, N, log2b, absmax, packed, y, da, s)
+                   : launch_kb<F16, 8>(x, M, K, N, log2b, absmax, packed, y, da, s);
+  return (int)e;
+}
+
+}  // namespace bq

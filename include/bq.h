@@ -169,6 +169,28 @@ bq_status bq_linear_blockwise(const void* x, bq_dtype dtype, int64_t M, int64_t 
                               const bq_code_table* code_table, const float* absmax, const uint8_t* packed,
                               float* y, hipStream_t stream);
 
+/* Fused dequantize + GEMM on the matrix cores, for batches of rows (the 16-bit-activation,
+ * 4-bit-weight GEMM named in "stable-diffusion.cpp PR 2278", Summary, here for the blockwise
+ * codes of bq_quantize_blockwise): y = x . W16^T, where W16 is exactly the 16-bit tensor
+ * bq_dequantize_blockwise writes for W with this `dtype`, w16 = RN16(fl32(c[q] * a)), formed
+ * in registers and never written out.
+ *   x          [device] M x K row-major activations, BQ_BF16 or BQ_F16, 16-byte aligned.
+ *   M, K, N    M >= 1 (at most 4,194,240); K > 0 and a multiple of 64; N >= 0 (N = 0:
+ *              nothing enqueued).
+ *   blocksize, code_table, absmax, packed
+ *              W, as for bq_linear_blockwise (packed 16-byte aligned).
+ *   y          [device] out: M x N row-major binary32.
+ * Each product x[m][k] * w16[n][k] is exact in binary32; the products are accumulated in
+ * binary32 in an unspecified order, so y[m][n] lies within (K + 64) * 2^-24 * sum_k
+ * |x[m][k] w16[n][k]| of the exact sum (products below the binary32 normal range may be
+ * flushed to zero by the matrix cores).  The result is the same on every call.
+ * Errors: BQ_ERR_DTYPE for BQ_F32; BQ_ERR_SIZE for M outside [1, 4194240], K not a positive
+ * multiple of 64, N < 0, or more than INT32_MAX blocks; otherwise as
+ * bq_dequantize_blockwise. */
+bq_status bq_gemm_blockwise(const void* x, bq_dtype dtype, int64_t M, int64_t K, int64_t N, int32_t blocksize,
+                            const bq_code_table* code_table, const float* absmax, const uint8_t* packed,
+                            float* y, hipStream_t stream);
+
 /* The hipError_t (as int) of the most recent launch that failed on the calling thread with
  * BQ_ERR_HIP, or 0 if none has. */
 int bq_last_hip_error(void);

@@ -56,6 +56,8 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
                                                     fp, u8p]),
         "bqo_linear_blockwise": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, i64, i32, fp, ctypes.c_int,
                                                 fp, u8p, vp]),
+        "bqo_gemm_blockwise": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, i64, i32, fp, ctypes.c_int,
+                                              fp, u8p, vp]),
         "bqo_quantize_nested": (ctypes.c_int, [vp, ctypes.c_int, i64, i32, fp, ctypes.c_int, fp,
                                                ctypes.c_int, i32, fp, u8p, fp, fp, u8p]),
         "bqo_dequantize_nested": (ctypes.c_int, [vp, ctypes.c_int, i64, i32, fp, ctypes.c_int,
@@ -181,6 +183,21 @@ class Oracle:
                                            _ptr(p), _ptr(y))
         if rc != 0:
             raise ValueError("oracle linear_blockwise rejected its arguments (%d)" % rc)
+        return y[:M * N].reshape(M, N)
+
+    def gemm_blockwise(self, x: np.ndarray, dtype: int, M: int, K: int, N: int, blocksize: int,
+                       table: np.ndarray, absmax: np.ndarray, packed: np.ndarray) -> np.ndarray:
+        """y (M x N, binary64) = x (M x K, raw fp16/bf16 elements) . W16^T, W16 the 16-bit
+        dequantized weights of the N x K tensor quantized blockwise over its flat index."""
+        xx = np.ascontiguousarray(x)
+        t = np.ascontiguousarray(table, dtype=np.float32)
+        a = np.ascontiguousarray(absmax, dtype=np.float32)
+        p = np.ascontiguousarray(packed, dtype=np.uint8)
+        y = np.zeros(max(M * N, 1), np.float64)
+        rc = self.lib.bqo_gemm_blockwise(_ptr(xx), dtype, M, K, N, blocksize, _ptr(t), len(t), _ptr(a),
+                                         _ptr(p), _ptr(y))
+        if rc != 0:
+            raise ValueError("oracle gemm_blockwise rejected its arguments (%d)" % rc)
         return y[:M * N].reshape(M, N)
 
     def quantize_nested(self, x: np.ndarray, dtype: int, blocksize: int, table: np.ndarray,

@@ -279,6 +279,30 @@ int bqo_linear_blockwise(const void* x, int dtype, int64_t M, int64_t K, int64_t
   return 0;
 }
 
+/* Fused dequantize + GEMM with 16-bit weights (the 16-bit-activation, 4-bit-weight GEMM
+ * named in stable-diffusion.cpp PR 2278, Summary): each weight is the 16-bit value the
+ * dequantize of A6 stores for `dtype` (fp16 or bf16), w16 = RN16(fl32(c[q] * a_b)), and
+ * y[m][n] = sum over k of x[m][k] * w16[n][k], accumulated in binary64 in ascending k.  W is
+ * the N x K row-major tensor quantized over its flat index; x is M x K row-major in `dtype`;
+ * y is M x N row-major binary64. */
+int bqo_gemm_blockwise(const void* x, int dtype, int64_t M, int64_t K, int64_t N, int32_t B,
+                       const float* c, int Kc, const float* absmax, const uint8_t* packed, double* y) {
+  if (dtype == BQO_F32 || M < 0 || K < 0 || N < 0 || !valid_args(dtype, M * K, B, Kc)) return -1;
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const int64_t f = n * K + k;
+        const float w32 = c[unpack_code(packed, f, Kc)] * absmax[f / B];
+        const float w16 = dtype == BQO_F16 ? bqo_f16_to_f32(bqo_f32_to_f16(w32))
+                                           : bqo_bf16_to_f32(bqo_f32_to_bf16(w32));
+        acc += (double)load_elem(x, dtype, m * K + k) * (double)w16;
+      }
+      y[m * N + n] = acc;
+    }
+  return 0;
+}
+
 /* ------------------------------------------------------------------------------------ */
 /* Nested statistics (nested General8 / compressed-statistics NF4).                     */
 /* ------------------------------------------------------------------------------------ */

@@ -618,4 +618,75 @@ def pin_linear_exact_rational(o):
                 assert abs(Fraction(float(y[m, n])) - exact) <= bound, (K, m, n, float(y[m, n]), float(exact))
 
 
+def pin_gemm_weights_rounded_to_16_bits(o):
+    """Hand-worked: entry 1/8 of the hand table times the block scale fl32(1/3) =
+    0x3EAAAAAB is the exact binary32 product 0x3D2AAAAB (0.0416666679...).  Rounded to
+    nearest even it is bf16 0x3D2B = 0.041748046875 (the dropped half 0xAAAB is above the
+    midpoint) and fp16 0x2955 = 0.041656494140625 (1.3333... x 1024 = 1365.33 rounds down).
+    With x a unit vector y picks that one weight, so y must equal those values, not the
+    binary32 product."""
+    table = _hand_table()
+    q_eighth = int(np.nonzero(table == np.float32(0.125))[0][0])
+    N, K, B = 2, 64, 32
+    flat = np.full(N * K, q_eighth, np.int64)
+    packed = ((flat[0::2] << 4) | flat[1::2]).astype(np.uint8)
+    absmax = np.full(N * K // B, np.float32(1.0) / np.float32(3.0), np.float32)
+    assert absmax[0].view(np.uint32) == 0x3EAAAAAB
+    for dtype, bits_one, expect in ((oracle.BF16, 0x3F80, 0.041748046875), (oracle.F16, 0x3C00, 0.041656494140625)):
+        x = np.zeros((1, K), np.uint16)
+        x[0, 5] = bits_one  # 1.0
+        y = o.gemm_blockwise(x, dtype, 1, K, N, B, table, absmax, packed)
+        assert np.all(y == expect), (dtype, y, expect)
+
+
+def pin_gemm_dyadic_closed_form(o):
+    """Every weight a multiple of 1/8 times a power of two (exact in bf16 and fp16) and small
+    integer activations: y must equal the exact rational sum, with the codes written into the
+    packed bytes here."""
+    table = _hand_table()
+    M, N, K, B = 3, 4, 128, 32
+    q = (np.arange(N)[:, None] * 7 + np.arange(K)[None, :] * 5) % 16
+    flat = q.reshape(-1)
+    packed = ((flat[0::2] << 4) | flat[1::2]).astype(np.uint8)
+    nb = N * K // B
+    absmax = np.ldexp(np.float32(1), (np.arange(nb) % 5) - 2).astype(np.float32)
+    xi = ((np.arange(M * K).reshape(M, K) * 5) % 13 - 6).astype(np.float32)
+    for dtype, to16 in ((oracle.BF16, torch.bfloat16), (oracle.F16, torch.float16)):
+        xb = torch.from_numpy(xi).to(to16).view(torch.int16).numpy().view(np.uint16)
+        y = o.gemm_blockwise(xb, dtype, M, K, N, B, table, absmax, packed)
+        for m in range(M):
+            for n in range(N):
+                exact = sum(Fraction(float(xi[m, k])) * Fraction(float(table[q[n, k]])) *
+                            Fraction(float(absmax[(n * K + k) // B])) for k in range(K))
+                assert y[m, n] == exact, (dtype, m, n, y[m, n], float(exact))
+
+
+def pin_gemm_exact_rational(o):
+    """Random activations and quantized weights: each weight rounded to the activation type
+    by torch (an independent round-to-nearest-even) from numpy's binary32 product, and y within
+    the binary64 summation bound of the exact rational sum."""
+    rng = _rng(67)
+    for K, table, B, dtype, to16 in ((16, synth.table16(), 64, oracle.BF16, torch.bfloat16),
+                                     (256, synth.table256(), 32, oracle.F16, torch.float16)):
+        M, N, Kd = 2, 3, 128
+        xt = torch.from_numpy(rng.standard_normal((M, Kd)).astype(np.float32)).to(to16)
+        xb = xt.view(torch.int16).numpy().view(np.uint16)
+        xf = xt.float().numpy()
+        w_in = (rng.standard_normal(N * Kd) * 0.02).astype(np.float32)
+        absmax, packed = o.quantize_blockwise(w_in, oracle.F32, B, table)
+        y = o.gemm_blockwise(xb, dtype, M, Kd, N, B, table, absmax, packed)
+        codes = _codes_high_first(packed, N * Kd, K).reshape(N, Kd)
+        t32 = np.float32(table)
+        w32 = np.array([[t32[codes[n, k]] * absmax[(n * Kd + k) // B] for k in range(Kd)] for n in range(N)],
+                       np.float32)
+        w16 = torch.from_numpy(w32).to(to16).float().numpy()
+        assert not np.array_equal(w16, w32)  # the rounding is visible in this case
+        for m in range(M):
+            for n in range(N):
+                terms = [Fraction(float(xf[m, k])) * Fraction(float(w16[n, k])) for k in range(Kd)]
+                exact = sum(terms)
+                bound = Fraction(Kd, 2 ** 53) * sum(abs(t) for t in terms) * Fraction(1 + 2 ** -40)
+                assert abs(Fraction(float(y[m, n])) - exact) <= bound, (K, m, n, float(y[m, n]), float(exact))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -190,6 +190,31 @@ def test_linear_validation():
     assert call(y=FAKE + 2) == bq.BQ_ERR_ALIGNMENT
 
 
+def test_gemm_validation():
+    def call(**kw):
+        args = dict(x=FAKE, dtype=bq.BQ_BF16, M=64, K=4096, N=14336, blocksize=64, table=T16, absmax=FAKE,
+                    packed=FAKE, y=FAKE, stream=0)
+        args.update(kw)
+        return bq.bq_gemm_blockwise(**args)
+
+    assert call(dtype=bq.BQ_F32) == bq.BQ_ERR_DTYPE
+    assert call(dtype=5) == bq.BQ_ERR_DTYPE
+    for kw in (dict(M=0), dict(M=65535 * 64 + 1), dict(K=0), dict(K=32), dict(K=96), dict(K=-64), dict(N=-1)):
+        assert call(**kw) == bq.BQ_ERR_SIZE, kw
+    assert call(K=64, N=(2**31) * 32, blocksize=32) == bq.BQ_ERR_SIZE  # more than INT32_MAX blocks
+    assert call(blocksize=48) == bq.BQ_ERR_BLOCKSIZE
+    assert call(table=np.float32(T16[::-1])) == bq.BQ_ERR_TABLE
+    assert call(table=None) == bq.BQ_ERR_NULL
+    assert call(N=0) == bq.BQ_OK  # nothing enqueued
+    assert call(N=0, x=None, y=None) == bq.BQ_OK
+    for name in ("x", "absmax", "packed", "y"):
+        assert call(**{name: None}) == bq.BQ_ERR_NULL, name
+    assert call(x=FAKE + 8) == bq.BQ_ERR_ALIGNMENT
+    assert call(packed=FAKE + 8) == bq.BQ_ERR_ALIGNMENT
+    assert call(absmax=FAKE + 2) == bq.BQ_ERR_ALIGNMENT
+    assert call(y=FAKE + 2) == bq.BQ_ERR_ALIGNMENT
+
+
 # ---- host table preparation vs the oracle ------------------------------------------------
 
 def _search_probes(table, rng):

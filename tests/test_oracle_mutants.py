@@ -43,6 +43,12 @@ MUTANTS = {
                                "if (k + 1 < K) s += (double)load_elem(x, dtype, m * K + k) * (double)w;"),
     "linear_binary32_sum": ("      double s = 0.0;\n      for (int64_t k = 0; k < K; ++k) {\n        const int64_t flat",
                             "      float s = 0.0f;\n      for (int64_t k = 0; k < K; ++k) {\n        const int64_t flat"),
+    "gemm_weight_not_rounded": ("""        const float w16 = dtype == BQO_F16 ? bqo_f16_to_f32(bqo_f32_to_f16(w32))
+                                           : bqo_bf16_to_f32(bqo_f32_to_bf16(w32));""",
+                                "        const float w16 = w32;"),
+    "gemm_rounds_to_the_other_type": ("const float w16 = dtype == BQO_F16 ?", "const float w16 = dtype != BQO_F16 ?"),
+    "gemm_transposed_weight": ("const int64_t f = n * K + k;", "const int64_t f = k * N + n;"),
+    "gemm_binary32_sum": ("double acc = 0.0;", "float acc = 0.0f;"),
 }
 
 
