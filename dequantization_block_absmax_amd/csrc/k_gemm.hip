@@ -9,7 +9,7 @@
 //   y[m][n] = sum_k x[m][k] * W16[n][k], products exact in binary32, accumulated in binary32.
 //
 // Work decomposition.  A workgroup owns an output tile of 32*MT rows of x by 32*NT rows of
-// W, and its 4 waves split K in chunks of 64 (wave w takes chunks w, w + 4, ...).  Each wave
+// W, and its NW waves split K in chunks of 64 (wave w takes chunks w, w + NW, ...).  Each wave
 // computes the whole tile for its chunks with v_mfma_f32_32x32x16 (bf16 or f16): lane l
 // (g = l / 32, r = l % 32) supplies A[r][8g + t] and B[8g + t][r], t < 8, and holds
 // C[8 (v / 4) + 4 g + v % 4][r] in accumulator element v.  Lane group g takes the 32
@@ -17,8 +17,8 @@
 // 4-bit codes (32 of 8-bit), which lie in one block (B >= 32), so one scale serves them.  MFMA
 // step s (0..3) uses the lane's k0 + 32 g + 8 s .. + 7 on both operands: the instruction sums
 // over 16 values of k, and giving A and B the same assignment of k to lanes and steps leaves
-// the product unchanged while every lane feeds the matrix core from its own loads.  The three
-// other waves' tiles are added to wave 0's through LDS, in wave order, and wave 0 stores y.
+// the product unchanged while every lane feeds the matrix core from its own loads.  The other
+// waves' tiles are added to wave 0's through LDS, in wave order, and wave 0 stores y.
 #include <hip/hip_runtime.h>
 
 #include "bq_internal.h"
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* x, int64_t
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // Chunks wave, wave + 4, ...: the loads of a wave's next chunk are issued before its current
+  // Chunks wave, wave + NW, ...: the loads of a wave's next chunk are issued before its current
   // chunk is dequantized and multiplied (M = 8 at 14336 x 4096: 32.3 us with each chunk's
   // loads waited for in its own iteration).  The chunk index is clamped instead of tested (the
   // last prefetch reads the wave's last chunk again), so no load sits under a condition.
@@ -226,13 +226,16 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* x, int64_t
   }
 }
 
-// 64 rows of W per workgroup (two column tiles: x is loaded once for both) and 4 waves
-// splitting K (measured against 32 rows and against 8 waves at 14336 x 4096: equal or faster
-// from M = 32 up, 21.7 against 17.4 us at M = 8).
-template <int DT, int KB, int MT>
+// 64 rows of W per workgroup (two column tiles: x is loaded once for both), 32, 64 or 128 rows
+// of x, and NW waves splitting K.  Measured at 14336 x 4096 against 32 rows of W and against
+// other wave counts: 8 waves for 32 rows of x (M = 8: 17.4 against 21.7 us with 4; the grid
+// has only N / 64 workgroups, so more waves hide more latency), 4 waves for more rows (M = 64:
+// 30.6 against 34.0 us with 8).  128-row tiles from M = 65 share each dequantized weight
+// among more rows (M = 128: 49.1 against 52.6 us with 64-row tiles).
+template <int DT, int KB, int MT, int NW>
 hipError_t launch_mt(const void* x, int64_t M, int64_t K, int64_t N, int log2b, const float* absmax,
                      const uint8_t* packed, float* y, const DequantArgs& da, hipStream_t s) {
-  constexpr int NT = 2, NW = 4;
+  constexpr int NT = 2;
   const dim3 grid((unsigned)((N + 32 * NT - 1) / (32 * NT)), (unsigned)((M + 32 * MT - 1) / (32 * MT)));
   return launch_kernel(gemm_kernel<DT, KB, MT, NT, NW>, grid, dim3(64 * NW), s, static_cast<const uint8_t*>(x), M,
                        K, N, log2b, absmax, packed, y, da);
@@ -241,12 +244,9 @@ hipError_t launch_mt(const void* x, int64_t M, int64_t K, int64_t N, int log2b, 
 template <int DT, int KB>
 hipError_t launch_kb(const void* x, int64_t M, int64_t K, int64_t N, int log2b, const float* absmax,
                      const uint8_t* packed, float* y, const DequantArgs& da, hipStream_t s) {
-  // 32, 64 or 128 rows of x per workgroup: fewer rows waste matrix-core work on padding, more
-  // rows share each dequantized weight (at 14336 x 4096, 128-row tiles: M = 128 49.1 against
-  // 52.6 us with 64-row tiles, equal at M <= 64)
-  if (M <= 32) return launch_mt<DT, KB, 1>(x, M, K, N, log2b, absmax, packed, y, da, s);
-  if (M <= 64) return launch_mt<DT, KB, 2>(x, M, K, N, log2b, absmax, packed, y, da, s);
-  return launch_mt<DT, KB, 4>(x, M, K, N, log2b, absmax, packed, y, da, s);
+  if (M <= 32) return launch_mt<DT, KB, 1, 8>(x, M, K, N, log2b, absmax, packed, y, da, s);
+  if (M <= 64) return launch_mt<DT, KB, 2, 4>(x, M, K, N, log2b, absmax, packed, y, da, s);
+  return launch_mt<DT, KB, 4, 4>(x, M, K, N, log2b, absmax, packed, y, da, s);
 }
 
 }  // namespace

@@ -38,6 +38,8 @@ def test_graph_replay_matches_eager(dev):
     wpk = torch.randint(0, 256, (Nl * Kl // 2,), dtype=torch.uint8, device=dev, generator=gen)
     wam = 0.01 + 0.02 * torch.rand(Nl * Kl // B, device=dev, generator=gen)
     xl = torch.randn(Ml, Kl, device=dev, generator=gen).to(torch.bfloat16)
+    Mg = 40  # fused GEMM on the same weight
+    xg = torch.randn(Mg, Kl, device=dev, generator=gen).to(torch.bfloat16)
 
     def buffers():
         ws_bytes = bq.bq_nested_workspace_bytes(n, B, B2)
@@ -48,7 +50,8 @@ def test_graph_replay_matches_eager(dev):
                     ws=torch.zeros(ws_bytes, dtype=torch.uint8, device=dev),
                     out=torch.zeros(n, dtype=torch.bfloat16, device=dev),
                     out4=torch.zeros(m, dtype=torch.bfloat16, device=dev),
-                    y=torch.zeros(Ml, Nl, dtype=torch.float32, device=dev))
+                    y=torch.zeros(Ml, Nl, dtype=torch.float32, device=dev),
+                    yg=torch.zeros(Mg, Nl, dtype=torch.float32, device=dev))
 
     def run(b, stream=None):
         st = bq.nested_stats(b["q2"], b["a2"], b["mean"], t256, B2, b["ws"])
@@ -57,11 +60,12 @@ def test_graph_replay_matches_eager(dev):
                  "dequantize_nested")
         bq.check(bq.bq_dequant_q32(q4, bq.BQ_BF16, m, cols, bq.BQ_Q32_Q4, b["out4"], stream), "dequant_q32")
         bq.check(bq.bq_linear_blockwise(xl, bq.BQ_BF16, Ml, Kl, Nl, B, t16, wam, wpk, b["y"], stream), "linear")
+        bq.check(bq.bq_gemm_blockwise(xg, bq.BQ_BF16, Mg, Kl, Nl, B, t16, wam, wpk, b["yg"], stream), "gemm")
 
     eager = buffers()
     run(eager)
     torch.cuda.synchronize()
-    keys = ("packed", "q2", "a2", "mean", "out", "out4", "y")
+    keys = ("packed", "q2", "a2", "mean", "out", "out4", "y", "yg")
     want = {k: eager[k].clone() for k in keys}
 
     g = buffers()
