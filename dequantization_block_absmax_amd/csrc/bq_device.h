@@ -72,6 +72,20 @@ __device__ __forceinline__ uint32_t group_max_u32(uint32_t v, int g) {
   return v;
 }
 
+// Maximum of v over the whole wave, returned in every lane: the DPP steps of group_max_u32
+// leave each 16-lane row's maximum in all its lanes, and four lane reads join the rows.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // half-row mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row mirror
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
 // One output word from its codes, in byte order: eight 4-bit codes (the first element of a
 // pair in the high nibble) or four 8-bit codes.  The bytes are joined with byte permutes, one
 // operation per byte pair, where a chain of shifts and ORs is compiled into more operations.

@@ -249,9 +249,14 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, in
 
   // Block absmax over G lanes.
   uint32_t key = chunk_key<DT>(w);
-  // LDS shuffles here: the DPP form of group_max_u32 measured slower in this kernel (2^29
-  // bf16 4-bit 221.1 against 218.5 us), where the statistics kernel gains from it.
-  for (int m = 1; m < G && m < 64; m <<= 1) key = max(key, (uint32_t)__shfl_xor((int)key, m));
+  // Blocks of a whole wave or more (B >= 2048): DPP steps and lane reads, no LDS round trips.
+  // Smaller blocks: LDS shuffles (the DPP form of group_max_u32, with its steps chosen at run
+  // time, measured slower here: 2^29 bf16 4-bit 221.1 against 218.5 us).
+  if (G >= 64) {
+    key = wave_max_u32(key);
+  } else {
+    for (int m = 1; m < G; m <<= 1) key = max(key, (uint32_t)__shfl_xor((int)key, m));
+  }
   if (G > 64) {  // B = 4096: two waves per block
     if (lane == 0) sh.red[tid >> 6] = key;
     __syncthreads();
