@@ -262,7 +262,7 @@ def detail_configs(bq, synth, torch, dev, peak):
 
 def fused_linear(bq, synth, torch, dev, t16, t256, peak, N=14336, K=4096, B=64, sets=24):
     """bq_linear_blockwise at a decode shape (a 14336 x 4096 weight, bf16 activations) for M = 1
-    and 4, and bq_gemm_blockwise for M = 16, 64 and 256, 4- and 8-bit codes, with the weights
+    and 4, and bq_gemm_blockwise for M = 16, 64, 256 and 1024, 4- and 8-bit codes, with the weights
     rotated over enough sets to miss the 256 MB last-level cache.  Beside each, the unfused
     path: dequantize to bf16 with this library, then torch's matmul."""
     out = {}
@@ -298,7 +298,7 @@ def fused_linear(bq, synth, torch, dev, t16, t256, peak, N=14336, K=4096, B=64, 
                 us=round(f_ms * 1e3, 2), rw_gbs=round(byts / f_ms / 1e6, 1),
                 pct_hbm_peak=round(100 * byts / f_ms / 1e6 / peak, 1),
                 unfused_us=round(u_ms * 1e3, 2), speedup_vs_unfused=round(u_ms / f_ms, 2))
-        for M in (16, 64, 256):  # bq_gemm_blockwise: 16-bit weights on the matrix cores
+        for M in (16, 64, 256, 1024):  # bq_gemm_blockwise: 16-bit weights on the matrix cores
             x = torch.randn(M, K, device=dev, generator=g).to(torch.bfloat16)
             y = torch.empty(M, N, device=dev)
             i = [0]

@@ -1,4 +1,5 @@
-// k_gemm.hip -- fused dequantize + GEMM on the gfx950 matrix cores, for batches of rows:
+// k_gemm.hip -- fused dequantize + GEMM on the gfx950 matrix cores, for batches of rows
+// (gemm_kernel up to 128 rows of x, gemm_tiled_kernel above):
 // y = x . W16^T, where W16 = RN16(fl32(c[q] * a)) is exactly the 16-bit tensor that
 // bq_dequantize_blockwise writes for W, formed in registers and never stored (the
 // 16-bit-activation, 4-bit-weight GEMM of "stable-diffusion.cpp PR 2278", Summary, on the
@@ -33,6 +34,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -232,6 +234,152 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* x, int64_t
 // has only N / 64 workgroups, so more waves hide more latency), 4 waves for more rows (M = 64:
 // 30.6 against 34.0 us with 8).  128-row tiles from M = 65 share each dequantized weight
 // among more rows (M = 128: 49.1 against 52.6 us with 64-row tiles).
+// Large batches: a 128 x 128 output tile per workgroup, its waves arranged 2 x 2 (64 x 64
+// each: 2 x 2 accumulator tiles), K in steps of 64 staged through LDS.  Each step, thread t
+// loads 32 consecutive k of x row t / 2 and of W row t / 2 (half t % 2), forms the 32 16-bit
+// weights, and writes both into the step's LDS buffer; the waves then read standard MFMA
+// fragments from LDS, so each x and W16 element is read once per tile.  Two LDS buffers
+// alternate (one barrier per step), and a step's global loads are issued two steps ahead.
+constexpr int kTileB = 128;        // rows of x and of W per tile
+constexpr int kTileK = 64;         // k per step
+constexpr int kRowPad = kTileK + 8;  // LDS row stride in 16-bit elements: 144 bytes, so the
+                                     // 16-byte fragment reads of 16 lanes hit distinct banks
+
+// (native vectors, not the uint4 struct: a struct copied through LDS stays in scratch memory
+// across the compiler barrier)
+template <int KB>
+struct Stage {
+  u32x4 x[4];
+  u32x4 codes[KB == 4 ? 1 : 2];
+  float a;
+};
+
+// One step's global loads for a staging thread: x row and W row (already offset to the
+// thread's row and k half), step kt clamped to the last (the last prefetch reads it again).
+template <int KB>
+__device__ __forceinline__ Stage<KB> load_stage(const uint8_t* xsrc, const uint8_t* packed, const float* absmax,
+                                                int64_t wf, int64_t kt, int64_t nk, int log2b) {
+  Stage<KB> st;
+  const int64_t k0 = min(kt, nk - 1) * kTileK;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) st.x[s] = *reinterpret_cast<const u32x4*>(xsrc + (k0 + 8 * s) * 2);
+  const int64_t f = wf + k0;
+  if constexpr (KB == 4) {
+    st.codes[0] = *reinterpret_cast<const u32x4*>(packed + (f >> 1));
+  } else {
+    st.codes[0] = *reinterpret_cast<const u32x4*>(packed + f);
+    st.codes[1] = *reinterpret_cast<const u32x4*>(packed + f + 16);
+  }
+  st.a = absmax[f >> log2b];
+  return st;
+}
+
+// Writes a staging thread's 32 x values and its 32 16-bit weights into one LDS buffer.
+template <int DT, int KB>
+__device__ __forceinline__ void store_stage(const Stage<KB>& st, uint16_t* sx, uint16_t* sw, int srow, int shalf,
+                                            const float2* s_pair, const float* s_c) {
+  uint16_t* xr = sx + srow * kRowPad + 32 * shalf;
+  uint16_t* wr = sw + srow * kRowPad + 32 * shalf;
+  uint32_t codes[KB == 4 ? 4 : 8];
+#pragma unroll
+  for (int h = 0; h < (KB == 4 ? 1 : 2); ++h) {
+    codes[4 * h] = st.codes[h][0];
+    codes[4 * h + 1] = st.codes[h][1];
+    codes[4 * h + 2] = st.codes[h][2];
+    codes[4 * h + 3] = st.codes[h][3];
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    *reinterpret_cast<u32x4*>(xr + 8 * s) = st.x[s];
+    const uint4 w = weight_frag<DT, KB>(codes, s, st.a, s_pair, s_c);
+    *reinterpret_cast<u32x4*>(wr + 8 * s) = u32x4{w.x, w.y, w.z, w.w};
+  }
+}
+
+template <int DT, int KB>
+__global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint8_t* x, int64_t M, int64_t K, int64_t N,
+                                                         int log2b, const float* absmax, const uint8_t* packed,
+                                                         float* __restrict__ y, DequantArgs da) {
+  __shared__ float2 s_pair[KB == 4 ? 256 : 1];
+  __shared__ float s_c[KB == 8 ? 256 : 1];
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[2][kTileB * kRowPad];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[2][kTileB * kRowPad];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, r = lane & 31;
+  const int wm = wave >> 1, wn = wave & 1;
+  if constexpr (KB == 4) s_pair[tid] = make_float2(da.c[tid >> 4], da.c[tid & 15]);
+  else s_c[tid] = da.c[tid];
+  __syncthreads();
+
+  const int64_t m0 = (int64_t)blockIdx.y * kTileB;
+  const int64_t n0 = (int64_t)blockIdx.x * kTileB;
+  // staging: row tid / 2 of both tiles, k half tid % 2; rows past M or N read the last row
+  const int srow = tid >> 1, shalf = tid & 1;
+  const uint8_t* xsrc = x + (min(m0 + srow, M - 1) * K + 32 * shalf) * 2;
+  const int64_t wf = min(n0 + srow, N - 1) * K + 32 * shalf;
+  const int64_t nk = K / kTileK;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  auto multiply = [&](int buf) {
+#pragma unroll
+    for (int s = 0; s < kTileK / 16; ++s) {
+      uint4 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const uint4*>(&s_x[buf][(64 * wm + 32 * i + r) * kRowPad + 16 * s + 8 * g]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[j] = *reinterpret_cast<const uint4*>(&s_w[buf][(64 * wn + 32 * j + r) * kRowPad + 16 * s + 8 * g]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16<DT>(a[i], b[j], acc[i][j]);
+    }
+  };
+  auto load = [&](int64_t kt) { return load_stage<KB>(xsrc, packed, absmax, wf, kt, nk, log2b); };
+  // Steps are loaded two ahead, into two register stages that alternate with the two LDS
+  // buffers: at the top of each iteration buffer 0 holds step kt and stage s1 step kt + 1
+  // (its loads possibly still in flight).  The loop takes two steps and exits only at the top;
+  // an odd last step is multiplied after it.
+  Stage<KB> s0 = load(0), s1 = load(1);
+  store_stage<DT, KB>(s0, s_x[0], s_w[0], srow, shalf, s_pair, s_c);
+  __syncthreads();
+  int64_t kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    s0 = load(kt + 2);
+    prefetch_fence();
+    multiply(0);
+    store_stage<DT, KB>(s1, s_x[1], s_w[1], srow, shalf, s_pair, s_c);  // step kt + 1
+    __syncthreads();
+    s1 = load(kt + 3);
+    prefetch_fence();
+    multiply(1);
+    store_stage<DT, KB>(s0, s_x[0], s_w[0], srow, shalf, s_pair, s_c);  // step kt + 2
+    __syncthreads();
+  }
+  if (kt < nk) multiply(0);
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = n0 + 64 * wn + 32 * j + r;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = m0 + 64 * wm + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+        if (row < M && col < N) y[row * N + col] = acc[i][j][v];
+      }
+    }
+}
+
 template <int DT, int KB, int MT, int NW>
 hipError_t launch_mt(const void* x, int64_t M, int64_t K, int64_t N, int log2b, const float* absmax,
                      const uint8_t* packed, float* y, const DequantArgs& da, hipStream_t s) {
@@ -246,7 +394,12 @@ hipError_t launch_kb(const void* x, int64_t M, int64_t K, int64_t N, int log2b, 
                      const uint8_t* packed, float* y, const DequantArgs& da, hipStream_t s) {
   if (M <= 32) return launch_mt<DT, KB, 1, 8>(x, M, K, N, log2b, absmax, packed, y, da, s);
   if (M <= 64) return launch_mt<DT, KB, 2, 4>(x, M, K, N, log2b, absmax, packed, y, da, s);
-  return launch_mt<DT, KB, 4, 4>(x, M, K, N, log2b, absmax, packed, y, da, s);
+  // Above 128 rows the LDS-tiled kernel: x and W16 read once per 128 x 128 tile (at 14336 x
+  // 4096: M = 256 56.4 against 95.3 us, M = 1024 181 against 335; M = 128 55.6 against 52.1)
+  if (M <= 128) return launch_mt<DT, KB, 4, 4>(x, M, K, N, log2b, absmax, packed, y, da, s);
+  const dim3 grid((unsigned)((N + kTileB - 1) / kTileB), (unsigned)((M + kTileB - 1) / kTileB));
+  return launch_kernel(gemm_tiled_kernel<DT, KB>, grid, dim3(256), s, static_cast<const uint8_t*>(x), M, K, N,
+                       log2b, absmax, packed, y, da);
 }
 
 }  // namespace

@@ -79,9 +79,10 @@ def host_bits_to_float(bits: np.ndarray, dtype: str) -> np.ndarray:
     return t.float().numpy().astype(np.float64)
 
 
-SHAPES = [  # (M, K, N, B): single tiles, ragged rows and columns, several chunks per wave
+SHAPES = [  # (M, K, N, B): single tiles, ragged rows and columns, several chunks per wave; from
+    # M = 129 the LDS-tiled kernel, with an odd number of 64-k steps (K = 192, 320)
     (1, 64, 1, 32), (5, 128, 33, 64), (32, 256, 64, 128), (33, 512, 65, 32), (64, 1024, 100, 256),
-    (70, 192, 130, 4096), (129, 2048, 37, 1024),
+    (70, 192, 130, 4096), (129, 2048, 37, 1024), (257, 192, 131, 64), (300, 320, 260, 512),
 ]
 
 
