@@ -228,12 +228,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* x, int64_t
   }
 }
 
-// 64 rows of W per workgroup (two column tiles: x is loaded once for both), 32, 64 or 128 rows
-// of x, and NW waves splitting K.  Measured at 14336 x 4096 against 32 rows of W and against
-// other wave counts: 8 waves for 32 rows of x (M = 8: 17.4 against 21.7 us with 4; the grid
-// has only N / 64 workgroups, so more waves hide more latency), 4 waves for more rows (M = 64:
-// 30.6 against 34.0 us with 8).  128-row tiles from M = 65 share each dequantized weight
-// among more rows (M = 128: 49.1 against 52.6 us with 64-row tiles).
 // Large batches: a 128 x 128 output tile per workgroup, its waves arranged 2 x 2 (64 x 64
 // each: 2 x 2 accumulator tiles), K in steps of 64 staged through LDS.  Each step, thread t
 // loads 32 consecutive k of x row t / 2 and of W row t / 2 (half t % 2), forms the 32 16-bit
@@ -380,6 +374,12 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint8_t* x, int64
     }
 }
 
+// 64 rows of W per workgroup (two column tiles: x is loaded once for both), 32, 64 or 128 rows
+// of x, and NW waves splitting K.  Measured at 14336 x 4096 against 32 rows of W and against
+// other wave counts: 8 waves for 32 rows of x (M = 8: 17.4 against 21.7 us with 4; the grid
+// has only N / 64 workgroups, so more waves hide more latency), 4 waves for more rows (M = 64:
+// 30.6 against 34.0 us with 8).  128-row tiles from M = 65 share each dequantized weight
+// among more rows (M = 128: 49.1 against 52.6 us with 64-row tiles).
 template <int DT, int KB, int MT, int NW>
 hipError_t launch_mt(const void* x, int64_t M, int64_t K, int64_t N, int log2b, const float* absmax,
                      const uint8_t* packed, float* y, const DequantArgs& da, hipStream_t s) {
