@@ -104,17 +104,18 @@ def test_gemm_exact_when_all_terms_exact(dev, o):
     summation gives the oracle's value exactly, for both 16-bit types."""
     table = np.float32([-1, -0.875, -0.75, -0.625, -0.5, -0.375, -0.25, -0.125, 0, 0.125, 0.25, 0.375,
                         0.5, 0.625, 0.75, 1])
-    M, N, K, B = 40, 70, 1024, 64
+    N, K, B = 70, 1024, 64
     q = (np.arange(N)[:, None] * 5 + np.arange(K)[None, :] * 3) % 16
     flat = q.reshape(-1)
     packed = ((flat[0::2] << 4) | flat[1::2]).astype(np.uint8)
     absmax = np.ldexp(np.float32(1), (np.arange(N * K // B) % 5) - 2).astype(np.float32)
-    xi = ((np.arange(M * K).reshape(M, K) * 7) % 11 - 5).astype(np.float32)
-    for dtype in DTYPES:
-        x = torch.from_numpy(xi).to(TORCH_DT[dtype])
-        y = run_gpu(dev, x, dtype, N, B, table, absmax, packed)
-        ref = o.gemm_blockwise(host_bits(x), ORACLE_DT[dtype], M, K, N, B, table, absmax, packed)
-        assert np.array_equal(y.astype(np.float64), ref), dtype
+    for M in (40, 150):  # the register-tiled kernel, then the LDS-tiled one
+        xi = ((np.arange(M * K).reshape(M, K) * 7) % 11 - 5).astype(np.float32)
+        for dtype in DTYPES:
+            x = torch.from_numpy(xi).to(TORCH_DT[dtype])
+            y = run_gpu(dev, x, dtype, N, B, table, absmax, packed)
+            ref = o.gemm_blockwise(host_bits(x), ORACLE_DT[dtype], M, K, N, B, table, absmax, packed)
+            assert np.array_equal(y.astype(np.float64), ref), (dtype, M)
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -126,16 +127,17 @@ def test_gemm_weights_match_the_16_bit_dequantize(dev, o, dtype, K_table):
     table = TABLES[K_table]
     N, K, B = 96, 512, 64
     absmax, packed = quantized_weights(o, N, K, B, table, seed=500 + K_table)
-    ks = np.array([0, 1, 7, 63, 64, 65, 200, 255, 256, 333, 448, 510, 511])
-    xf = np.zeros((len(ks), K), np.float32)
-    xf[np.arange(len(ks)), ks] = 1.0
-    x = torch.from_numpy(xf).to(TORCH_DT[dtype])
-    y = run_gpu(dev, x, dtype, N, B, table, absmax, packed)
     w16 = host_bits_to_float(o.dequantize_blockwise(packed, absmax, N * K, ORACLE_DT[dtype], B, table), dtype)
-    assert np.array_equal(y.astype(np.float64), w16.reshape(N, K)[:, ks].T)
+    # 13 rows (register-tiled kernel), then 171 (LDS-tiled kernel: every third k)
+    for ks in (np.array([0, 1, 7, 63, 64, 65, 200, 255, 256, 333, 448, 510, 511]), np.arange(0, K, 3)):
+        xf = np.zeros((len(ks), K), np.float32)
+        xf[np.arange(len(ks)), ks] = 1.0
+        x = torch.from_numpy(xf).to(TORCH_DT[dtype])
+        y = run_gpu(dev, x, dtype, N, B, table, absmax, packed)
+        assert np.array_equal(y.astype(np.float64), w16.reshape(N, K)[:, ks].T), len(ks)
 
 
-@pytest.mark.parametrize("K_table,M", [(16, 64), (256, 200)])
+@pytest.mark.parametrize("K_table,M", [(16, 64), (256, 200), (16, 1024)])
 def test_gemm_prefill_shape_sampled_rows(dev, o, K_table, M):
     """A 14336 x 4096 weight (bf16 activations, B = 64), every output computed on the GPU; the
     oracle checks 24 sampled weight rows (first, last and random) for every activation row.
