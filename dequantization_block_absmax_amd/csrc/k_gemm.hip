@@ -233,7 +233,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* x, int64_t
 // loads 32 consecutive k of x row t / 2 and of W row t / 2 (half t % 2), forms the 32 16-bit
 // weights, and writes both into the step's LDS buffer; the waves then read standard MFMA
 // fragments from LDS, so each x and W16 element is read once per tile.  Two LDS buffers
-// alternate (one barrier per step), and a step's global loads are issued two steps ahead.
+// alternate (one barrier per step): the next step is formed and written into the other buffer
+// between the current step's MFMAs, and a step's global loads are issued two steps ahead.
 constexpr int kTileB = 128;        // rows of x and of W per tile
 constexpr int kTileK = 64;         // k per step
 constexpr int kRowPad = kTileK + 8;  // LDS row stride in 16-bit elements: 144 bytes, so the
@@ -338,6 +339,34 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint8_t* x, int64
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16<DT>(a[i], b[j], acc[i][j]);
     }
   };
+  // The step in buffer buf, with the next step (stage st) written into the other buffer piece by
+  // piece between its MFMAs, so that the weight formation issues while the MFMAs run.
+  auto multiply_store = [&](int buf, const Stage<KB>& st) {
+    uint16_t* xr = s_x[buf ^ 1] + srow * kRowPad + 32 * shalf;
+    uint16_t* wr = s_w[buf ^ 1] + srow * kRowPad + 32 * shalf;
+    uint32_t codes[KB == 4 ? 4 : 8];
+#pragma unroll
+    for (int h = 0; h < (KB == 4 ? 1 : 2); ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) codes[4 * h + i] = st.codes[h][i];
+#pragma unroll
+    for (int s = 0; s < kTileK / 16; ++s) {
+      uint4 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const uint4*>(&s_x[buf][(64 * wm + 32 * i + r) * kRowPad + 16 * s + 8 * g]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[j] = *reinterpret_cast<const uint4*>(&s_w[buf][(64 * wn + 32 * j + r) * kRowPad + 16 * s + 8 * g]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16<DT>(a[i], b[j], acc[i][j]);
+      *reinterpret_cast<u32x4*>(xr + 8 * s) = st.x[s];
+      const uint4 w = weight_frag<DT, KB>(codes, s, st.a, s_pair, s_c);
+      *reinterpret_cast<u32x4*>(wr + 8 * s) = u32x4{w.x, w.y, w.z, w.w};
+    }
+  };
   auto load = [&](int64_t kt) { return load_stage<KB>(xsrc, packed, absmax, wf, kt, nk, log2b); };
   // Steps are loaded two ahead, into two register stages that alternate with the two LDS
   // buffers: at the top of each iteration buffer 0 holds step kt and stage s1 step kt + 1
@@ -350,13 +379,11 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint8_t* x, int64
   for (; kt + 1 < nk; kt += 2) {
     s0 = load(kt + 2);
     prefetch_fence();
-    multiply(0);
-    store_stage<DT, KB>(s1, s_x[1], s_w[1], srow, shalf, s_pair, s_c);  // step kt + 1
+    multiply_store(0, s1);  // step kt; step kt + 1 into buffer 1
     __syncthreads();
     s1 = load(kt + 3);
     prefetch_fence();
-    multiply(1);
-    store_stage<DT, KB>(s0, s_x[0], s_w[0], srow, shalf, s_pair, s_c);  // step kt + 2
+    multiply_store(1, s0);  // step kt + 1; step kt + 2 into buffer 0
     __syncthreads();
   }
   if (kt < nk) multiply(0);
