@@ -169,7 +169,8 @@ bq_status bq_linear_blockwise(const void* x, bq_dtype dtype, int64_t M, int64_t 
   if (st != BQ_OK) return st;
   if (N == 0) return BQ_OK;
   if (x == nullptr || absmax == nullptr || packed == nullptr || y == nullptr) return BQ_ERR_NULL;
-  if (nblocks(N * K, blocksize) > INT32_MAX || (N + 3) / 4 > INT32_MAX) return BQ_ERR_SIZE;  // one workgroup per 4 rows
+  // at least 4 rows per workgroup of 256 threads, and a launch holds at most 2^32 - 1 threads
+  if (nblocks(N * K, blocksize) > INT32_MAX || (N + 3) / 4 * 256 > UINT32_MAX) return BQ_ERR_SIZE;
   if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(absmax, 4) || !aligned(y, 4)) return BQ_ERR_ALIGNMENT;
   bq::DequantArgs a;
   memset(&a, 0, sizeof(a));
@@ -192,7 +193,8 @@ bq_status bq_gemm_blockwise(const void* x, bq_dtype dtype, int64_t M, int64_t K,
   if (st != BQ_OK) return st;
   if (N == 0) return BQ_OK;
   if (x == nullptr || absmax == nullptr || packed == nullptr || y == nullptr) return BQ_ERR_NULL;
-  if (nblocks(N * K, blocksize) > INT32_MAX || (N + 63) / 64 > INT32_MAX) return BQ_ERR_SIZE;  // 64 columns a workgroup
+  // at least 64 columns per workgroup of at most 512 threads; at most 2^32 - 1 threads a launch
+  if (nblocks(N * K, blocksize) > INT32_MAX || (N + 63) / 64 * 512 > UINT32_MAX) return BQ_ERR_SIZE;
   if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(absmax, 4) || !aligned(y, 4)) return BQ_ERR_ALIGNMENT;
   bq::DequantArgs a;
   memset(&a, 0, sizeof(a));

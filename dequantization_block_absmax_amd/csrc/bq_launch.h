@@ -7,14 +7,20 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdint>
 #include <tuple>
 #include <type_traits>
 #include <utility>
 
 namespace bq {
 
+// A launch's threads per dimension (workgroups times workgroup size) must fit in 32 bits;
+// larger grids are refused here rather than left to the runtime.
 template <typename... KArgs, typename... Args>
 hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream, Args&&... args) {
+  if ((uint64_t)grid.x * block.x > UINT32_MAX || (uint64_t)grid.y * block.y > UINT32_MAX ||
+      (uint64_t)grid.z * block.z > UINT32_MAX)
+    return hipErrorInvalidConfiguration;
   std::tuple<std::decay_t<KArgs>...> vals(std::forward<Args>(args)...);
   return std::apply(
       [&](auto&... v) {

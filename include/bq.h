@@ -152,7 +152,8 @@ bq_status bq_dequant_q32(const void* blocks, bq_dtype dtype, int64_t n, int32_t 
  * expanding the full tensor, as in the mixed-input GEMMs of "stable-diffusion.cpp PR 2278",
  * Summary; here for the blockwise codes of bq_quantize_blockwise).
  *   x          [device] M x K row-major activations of `dtype`, 16-byte aligned.
- *   M, K, N    1 <= M <= 4; K > 0 and a multiple of 16; N >= 0 (N = 0: nothing enqueued).
+ *   M, K, N    1 <= M <= 4; K > 0 and a multiple of 16; 0 <= N <= 67,108,860 (a launch holds
+ *              at most 2^32 - 1 threads; N = 0: nothing enqueued).
  *   blocksize, code_table
  *              the block size and table W was quantized with.
  *   absmax     [device] ceil(N*K / blocksize) binary32 block maxima of W.
@@ -163,8 +164,8 @@ bq_status bq_dequant_q32(const void* blocks, bq_dtype dtype, int64_t n, int32_t 
  * y[m][n] approximates sum_k x[m][k] * w[n][k], w = fl32(c[q] * a) the binary32 dequantized
  * weight (never rounded to 16 bits), accumulated in binary32 in an unspecified order: its
  * error is at most (K/1024 + 64) * 2^-24 * sum_k |x[m][k] w[n][k]|.
- * Errors: BQ_ERR_SIZE for M outside [1, 4], K not a positive multiple of 16, N < 0, or more
- * than INT32_MAX blocks; otherwise as bq_dequantize_blockwise. */
+ * Errors: BQ_ERR_SIZE for M outside [1, 4], K not a positive multiple of 16, N outside
+ * [0, 67108860], or more than INT32_MAX blocks; otherwise as bq_dequantize_blockwise. */
 bq_status bq_linear_blockwise(const void* x, bq_dtype dtype, int64_t M, int64_t K, int64_t N, int32_t blocksize,
                               const bq_code_table* code_table, const float* absmax, const uint8_t* packed,
                               float* y, hipStream_t stream);
@@ -175,8 +176,8 @@ bq_status bq_linear_blockwise(const void* x, bq_dtype dtype, int64_t M, int64_t 
  * bq_dequantize_blockwise writes for W with this `dtype`, w16 = RN16(fl32(c[q] * a)), formed
  * in registers and never written out.
  *   x          [device] M x K row-major activations, BQ_BF16 or BQ_F16, 16-byte aligned.
- *   M, K, N    M >= 1 (at most 4,194,240); K > 0 and a multiple of 64; N >= 0 (N = 0:
- *              nothing enqueued).
+ *   M, K, N    M >= 1 (at most 4,194,240); K > 0 and a multiple of 64; 0 <= N <= 536,870,848
+ *              (a launch holds at most 2^32 - 1 threads; N = 0: nothing enqueued).
  *   blocksize, code_table, absmax, packed
  *              W, as for bq_linear_blockwise (packed 16-byte aligned).
  *   y          [device] out: M x N row-major binary32.
@@ -185,7 +186,7 @@ bq_status bq_linear_blockwise(const void* x, bq_dtype dtype, int64_t M, int64_t 
  * |x[m][k] w16[n][k]| of the exact sum (products below the binary32 normal range may be
  * flushed to zero by the matrix cores).  The result is the same on every call.
  * Errors: BQ_ERR_DTYPE for BQ_F32; BQ_ERR_SIZE for M outside [1, 4194240], K not a positive
- * multiple of 64, N < 0, or more than INT32_MAX blocks; otherwise as
+ * multiple of 64, N outside [0, 536870848], or more than INT32_MAX blocks; otherwise as
  * bq_dequantize_blockwise. */
 bq_status bq_gemm_blockwise(const void* x, bq_dtype dtype, int64_t M, int64_t K, int64_t N, int32_t blocksize,
                             const bq_code_table* code_table, const float* absmax, const uint8_t* packed,

@@ -177,6 +177,7 @@ def test_linear_validation():
     for kw in (dict(M=0), dict(M=5), dict(K=0), dict(K=17), dict(K=-16), dict(N=-1)):
         assert call(**kw) == bq.BQ_ERR_SIZE, kw
     assert call(K=16, N=(2**31) * 32, blocksize=32) == bq.BQ_ERR_SIZE  # more than INT32_MAX blocks
+    assert call(K=16, N=67108861, blocksize=4096) == bq.BQ_ERR_SIZE  # more than 2^32 - 1 threads
     assert call(blocksize=48) == bq.BQ_ERR_BLOCKSIZE
     assert call(table=np.float32(T16[::-1])) == bq.BQ_ERR_TABLE
     assert call(table=None) == bq.BQ_ERR_NULL
@@ -202,6 +203,7 @@ def test_gemm_validation():
     for kw in (dict(M=0), dict(M=65535 * 64 + 1), dict(K=0), dict(K=32), dict(K=96), dict(K=-64), dict(N=-1)):
         assert call(**kw) == bq.BQ_ERR_SIZE, kw
     assert call(K=64, N=(2**31) * 32, blocksize=32) == bq.BQ_ERR_SIZE  # more than INT32_MAX blocks
+    assert call(K=64, N=536870849, blocksize=4096) == bq.BQ_ERR_SIZE  # more than 2^32 - 1 threads
     assert call(blocksize=48) == bq.BQ_ERR_BLOCKSIZE
     assert call(table=np.float32(T16[::-1])) == bq.BQ_ERR_TABLE
     assert call(table=None) == bq.BQ_ERR_NULL
