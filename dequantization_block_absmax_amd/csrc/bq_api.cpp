@@ -31,6 +31,8 @@ thread_local int g_last_hip_error = 0;
 
 bq_status hip_status(int e) {
   if (e == 0) return BQ_OK;
+  // the launcher's own refusal of a grid over 2^32 - 1 threads (no launch was made)
+  if (e == (int)hipErrorInvalidConfiguration) return BQ_ERR_SIZE;
   g_last_hip_error = e;
   return BQ_ERR_HIP;
 }

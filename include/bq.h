@@ -57,7 +57,10 @@ typedef enum {
   BQ_OK = 0,
   BQ_ERR_NULL = 1,      /* a required pointer is NULL */
   BQ_ERR_DTYPE = 2,     /* dtype is not a bq_dtype */
-  BQ_ERR_SIZE = 3,      /* n < 0, more than INT32_MAX blocks, or n not a whole number of rows */
+  BQ_ERR_SIZE = 3,      /* n < 0, more than INT32_MAX blocks, n not a whole number of rows, or a
+                           launch of more than 2^32 - 1 threads, refused before any work is
+                           enqueued (quantize and 4-bit dequantize from 2^37 elements, 8-bit
+                           dequantize from 2^36) */
   BQ_ERR_BLOCKSIZE = 4, /* blocksize not a power of two in [32, 4096] */
   BQ_ERR_TABLE = 5,     /* code table: size, order, range or spacing (see bq_code_table) */
   BQ_ERR_ALIGNMENT = 6, /* a device pointer is not aligned as required */
