@@ -270,3 +270,12 @@ def test_host_search_matches_oracle(name):
         assert mode == 2
     if name in ("table16", "hand16"):
         assert mode == 0 and cmp == 1
+
+
+def test_launch_size_limit():
+    """A call whose launch would hold more than 2^32 - 1 threads is refused with BQ_ERR_SIZE
+    before anything is enqueued (no device is touched: the addresses are never used)."""
+    t16, t256 = bq.code_table(T16), bq.code_table(T256)
+    assert bq.bq_dequantize_blockwise(FAKE, bq.BQ_BF16, 1 << 36, 4096, t256, FAKE, FAKE, stream=0) == bq.BQ_ERR_SIZE
+    assert bq.bq_dequantize_blockwise(FAKE, bq.BQ_BF16, 1 << 37, 4096, t16, FAKE, FAKE, stream=0) == bq.BQ_ERR_SIZE
+    assert bq.bq_quantize_blockwise(FAKE, bq.BQ_BF16, 1 << 37, 4096, t16, FAKE, FAKE, stream=0) == bq.BQ_ERR_SIZE
