@@ -420,8 +420,8 @@ def cpu_baseline(w: Workload, torch):
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the method needs no cross-GPU communication and this build "
-              "targets a single MI355X; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the method needs no cross-GPU communication, and each GPU "
+              "would quantize its own shard independently; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
 
