@@ -64,6 +64,9 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
                                                  fp, ctypes.c_int, i32, u8p, fp, ctypes.c_float,
                                                  u8p]),
         "bqo_dequant_q32": (ctypes.c_int, [u8p, ctypes.c_int, i64, i32, ctypes.c_int, vp]),
+        "bqo_prepare_table": (ctypes.c_int, [fp, ctypes.c_int, fp]),
+        "bqo_nested_groups": (ctypes.c_int, [fp, i64, ctypes.c_float, fp, ctypes.c_int, i32, i64, i64, u8p, fp]),
+        "bqo_nested_stats": (ctypes.c_int, [fp, i64, fp, ctypes.c_int, i32, u8p, fp, fp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -139,6 +142,14 @@ class Oracle:
 
     def f16_to_f32(self, h: int) -> np.float32:
         return np.float32(self.lib.bqo_f16_to_f32(int(h)))
+
+    def prepare_table(self, table: np.ndarray):
+        """The table as the oracle uses it (-0.0 read as +0.0), or None when it breaks R7."""
+        t = np.ascontiguousarray(table, dtype=np.float32)
+        out = np.zeros(max(t.size, 1), np.float32)
+        if self.lib.bqo_prepare_table(_ptr(t), t.size, _ptr(out)) != 0:
+            return None
+        return out[:t.size]
 
     # array entry points ----------------------------------------------------------------
     @staticmethod
@@ -243,6 +254,145 @@ class Oracle:
         rc = self.lib.bqo_dequant_q32(_ptr(b), dtype, n, row_len, fmt, _ptr(out))
         if rc != 0:
             raise ValueError("oracle dequant_q32 rejected its arguments (%d)" % rc)
+        return out[:n]
+
+
+def default_threads() -> int:
+    """Host threads for the range-split entry points: the CPU count, at most 16."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _ranges(units: int, parts: int):
+    """[lo, hi) ranges splitting 0..units into at most `parts` contiguous pieces."""
+    parts = max(1, min(parts, units))
+    step = -(-units // parts)
+    return [(lo, min(units, lo + step)) for lo in range(0, units, step)]
+
+
+def _run_all(jobs, threads: int):
+    """Runs the callables in `jobs` on `threads` host threads (ctypes releases the GIL during a
+    call into the C oracle) and raises if any returns a nonzero status."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        codes = list(ex.map(lambda f: f(), jobs))
+    bad = [c for c in codes if c != 0]
+    if bad:
+        raise ValueError("oracle rejected its arguments (%d)" % bad[0])
+
+
+class ParallelOracle(Oracle):
+    """The same C functions, called on contiguous ranges of whole blocks (groups, rows) from
+    several host threads.  Blocks are independent in every step except the nested mean, which
+    stays one call over the whole absmax array, so the outputs are bit-identical to one call
+    over everything; this class only splits index ranges and points each call at its slice
+    of the input and output arrays (no arithmetic of the method happens here)."""
+
+    def __init__(self, threads: int | None = None, lib: ctypes.CDLL | None = None):
+        super().__init__(lib)
+        self.threads = threads or default_threads()
+
+    def _parts(self, units: int):
+        return _ranges(units, 4 * self.threads)
+
+    def quantize_blockwise(self, x: np.ndarray, dtype: int, blocksize: int, table: np.ndarray):
+        x = np.ascontiguousarray(x).reshape(-1)
+        n = x.size
+        t = np.ascontiguousarray(table, dtype=np.float32)
+        K = t.size
+        nb = -(-n // blocksize)
+        absmax = np.zeros(max(nb, 1), np.float32)
+        packed = np.zeros(max(self.packed_bytes(n, K), 1), np.uint8)
+        lib = self.lib
+
+        def job(b0, b1):
+            e0, e1 = b0 * blocksize, min(n, b1 * blocksize)  # e0 is even: 4-bit bytes start at e0 / 2
+            p0 = e0 if K == 256 else e0 // 2
+            return lambda: lib.bqo_quantize_blockwise(_ptr(x) + e0 * x.itemsize, dtype, e1 - e0, blocksize,
+                                                      _ptr(t), K, _ptr(absmax) + 4 * b0, _ptr(packed) + p0)
+        _run_all([job(b0, b1) for b0, b1 in self._parts(nb)], self.threads)
+        return absmax[:nb], packed[:self.packed_bytes(n, K)]
+
+    def dequantize_blockwise(self, packed: np.ndarray, absmax: np.ndarray, n: int, dtype: int,
+                             blocksize: int, table: np.ndarray) -> np.ndarray:
+        t = np.ascontiguousarray(table, dtype=np.float32)
+        K = t.size
+        out = np.zeros(max(n, 1), np.float32 if dtype == F32 else np.uint16)
+        p = np.ascontiguousarray(packed, dtype=np.uint8)
+        a = np.ascontiguousarray(absmax, dtype=np.float32)
+        lib = self.lib
+        nb = -(-n // blocksize)
+
+        def job(b0, b1):
+            e0, e1 = b0 * blocksize, min(n, b1 * blocksize)
+            p0 = e0 if K == 256 else e0 // 2
+            return lambda: lib.bqo_dequantize_blockwise(_ptr(out) + e0 * out.itemsize, dtype, e1 - e0, blocksize,
+                                                        _ptr(t), K, _ptr(a) + 4 * b0, _ptr(p) + p0)
+        _run_all([job(b0, b1) for b0, b1 in self._parts(nb)], self.threads)
+        return out[:n]
+
+    def nested_stats(self, absmax: np.ndarray, table2: np.ndarray, blocksize2: int = 256):
+        """mean (one call over the whole array), then q2 / absmax2 over ranges of groups."""
+        a = np.ascontiguousarray(absmax, dtype=np.float32)
+        nb = a.size
+        t2 = np.ascontiguousarray(table2, dtype=np.float32)
+        ng = -(-nb // blocksize2)
+        q2 = np.zeros(max(nb, 1), np.uint8)
+        absmax2 = np.zeros(max(ng, 1), np.float32)
+        mean = self.nested_mean(a)
+        lib = self.lib
+
+        def job(g0, g1):
+            return lambda: lib.bqo_nested_groups(_ptr(a), nb, float(mean), _ptr(t2), t2.size, blocksize2, g0, g1,
+                                                 _ptr(q2), _ptr(absmax2))
+        _run_all([job(g0, g1) for g0, g1 in self._parts(ng)], self.threads)
+        return q2[:nb], absmax2[:ng], mean
+
+    def quantize_nested(self, x: np.ndarray, dtype: int, blocksize: int, table: np.ndarray,
+                        table2: np.ndarray, blocksize2: int = 256):
+        if self.prepare_table(table2) is None or np.asarray(table2).size != 256:
+            raise ValueError("oracle quantize_nested rejected its arguments (-1)")
+        absmax, packed = self.quantize_blockwise(x, dtype, blocksize, table)
+        q2, absmax2, mean = self.nested_stats(absmax, table2, blocksize2)
+        return dict(absmax=absmax, q2=q2, absmax2=absmax2, mean=mean, packed=packed)
+
+    def dequantize_nested(self, packed, q2, absmax2, mean, n: int, dtype: int, blocksize: int,
+                          table, table2, blocksize2: int = 256) -> np.ndarray:
+        t = np.ascontiguousarray(table, dtype=np.float32)
+        t2 = np.ascontiguousarray(table2, dtype=np.float32)
+        K = t.size
+        out = np.zeros(max(n, 1), np.float32 if dtype == F32 else np.uint16)
+        p = np.ascontiguousarray(packed, dtype=np.uint8)
+        q = np.ascontiguousarray(q2, dtype=np.uint8)
+        a2 = np.ascontiguousarray(absmax2, dtype=np.float32)
+        lib = self.lib
+        nb = -(-n // blocksize)
+        ng = -(-nb // blocksize2)
+
+        def job(g0, g1):  # whole groups: block b0 = g0 * B2 starts absmax2 slice g0
+            b0, b1 = g0 * blocksize2, min(nb, g1 * blocksize2)
+            e0, e1 = b0 * blocksize, min(n, b1 * blocksize)
+            p0 = e0 if K == 256 else e0 // 2
+            return lambda: lib.bqo_dequantize_nested(_ptr(out) + e0 * out.itemsize, dtype, e1 - e0, blocksize,
+                                                     _ptr(t), K, _ptr(t2), t2.size, blocksize2, _ptr(q) + b0,
+                                                     _ptr(a2) + 4 * g0, float(np.float32(mean)), _ptr(p) + p0)
+        _run_all([job(g0, g1) for g0, g1 in self._parts(ng)], self.threads)
+        return out[:n]
+
+    def dequant_q32(self, blocks: np.ndarray, n: int, row_len: int, fmt: int,
+                    dtype: int = BF16) -> np.ndarray:
+        b = np.ascontiguousarray(blocks, dtype=np.uint8)
+        out = np.zeros(max(n, 1), np.float32 if dtype == F32 else np.uint16)
+        bs = 18 if fmt == Q4 else 34
+        lib = self.lib
+        rows = n // row_len if row_len > 0 else 0
+
+        def job(r0, r1):  # whole rows
+            e0, e1 = r0 * row_len, r1 * row_len
+            return lambda: lib.bqo_dequant_q32(_ptr(b) + e0 // 32 * bs, dtype, e1 - e0, row_len, fmt,
+                                               _ptr(out) + e0 * out.itemsize)
+        if rows == 0 or n % row_len != 0:
+            return super().dequant_q32(blocks, n, row_len, fmt, dtype)
+        _run_all([job(r0, r1) for r0, r1 in self._parts(rows)], self.threads)
         return out[:n]
 
 

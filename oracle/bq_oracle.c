@@ -157,6 +157,27 @@ int bqo_nearest(float y, const float* c, int K) {
 /* Code of a non-finite element and of a zero block (R4, R5): the nearest code to 0.0. */
 int bqo_zero_code(const float* c, int K) { return bqo_nearest(0.0f, c, K); }
 
+/* Step 1, the code table (R7).  K is 16 or 256; every entry is finite, within [-1, 1], and
+ * larger than the one before it; a nonzero entry has magnitude at least 2^-20.  Under these
+ * conditions every entry is a multiple of 2^-43 of magnitude at most 1, which is what makes
+ * the binary64 midpoint test of bqo_nearest exact.  A -0.0 entry is read as +0.0, the way
+ * the IQ packing review treats a negative-zero scale as zero ("[OMNIML-5899] Add CUDA
+ * kernels for IQ packing", the later review's negative-zero finding): its code then
+ * dequantizes to +0.0.  Writes the table as used into c_out; returns 0, or -1 when the
+ * table breaks a condition. */
+int bqo_prepare_table(const float* c_in, int K, float* c_out) {
+  if (c_in == NULL || (K != 16 && K != 256)) return -1;
+  for (int k = 0; k < K; ++k) {
+    float v = c_in[k];
+    if (!isfinite(v) || v < -1.0f || v > 1.0f) return -1;
+    if (v == 0.0f) v = 0.0f; /* -0.0 -> +0.0 */
+    if (v != 0.0f && fabsf(v) < 0x1p-20f) return -1;
+    if (k > 0 && !(v > c_out[k - 1])) return -1;
+    c_out[k] = v;
+  }
+  return 0;
+}
+
 /* Power-of-two guard of R3: keeps fl32(1/(a*s)) a normal, finite binary32 number. */
 float bqo_guard_scale(float a) {
   if (a < 0x1p-64f) return 0x1p64f;
@@ -228,9 +249,10 @@ static int valid_args(int dtype, int64_t n, int32_t B, int K) {
 }
 
 /* absmax[ceil(n/B)], packed[ceil(n/2) or n]. Returns 0, or -1 on invalid arguments. */
-int bqo_quantize_blockwise(const void* in, int dtype, int64_t n, int32_t B, const float* c,
+int bqo_quantize_blockwise(const void* in, int dtype, int64_t n, int32_t B, const float* c_in,
                            int K, float* absmax, uint8_t* packed) {
-  if (!valid_args(dtype, n, B, K)) return -1;
+  float c[256];
+  if (!valid_args(dtype, n, B, K) || bqo_prepare_table(c_in, K, c) != 0) return -1;
   if (n == 0) return 0;
   uint8_t* codes = (uint8_t*)malloc((size_t)n);
   if (!codes) return -2;
@@ -246,9 +268,10 @@ int bqo_quantize_blockwise(const void* in, int dtype, int64_t n, int32_t B, cons
 
 /* out_i = RN_dtype(fl32(c[q_i] * a_b)): one binary32 multiply by the block absmax, one
  * rounding to the output type. */
-int bqo_dequantize_blockwise(void* out, int dtype, int64_t n, int32_t B, const float* c, int K,
+int bqo_dequantize_blockwise(void* out, int dtype, int64_t n, int32_t B, const float* c_in, int K,
                              const float* absmax, const uint8_t* packed) {
-  if (!valid_args(dtype, n, B, K)) return -1;
+  float c[256];
+  if (!valid_args(dtype, n, B, K) || bqo_prepare_table(c_in, K, c) != 0) return -1;
   for (int64_t i = 0; i < n; ++i) {
     float v = c[unpack_code(packed, i, K)] * absmax[i / B];
     store_elem(out, dtype, i, v);
@@ -262,9 +285,11 @@ int bqo_dequantize_blockwise(void* out, int dtype, int64_t n, int32_t B, const f
  * and y[m][n] = sum over k of x[m][k] * w[n][k], accumulated in binary64 in ascending k.
  * x is M x K row-major in `dtype`; y is M x N row-major binary64. */
 int bqo_linear_blockwise(const void* x, int dtype, int64_t M, int64_t K, int64_t N, int32_t B,
-                         const float* c, int Kc, const float* absmax, const uint8_t* packed,
+                         const float* c_in, int Kc, const float* absmax, const uint8_t* packed,
                          double* y) {
+  float c[256];
   if (M < 0 || K < 0 || N < 0 || !valid_args(dtype, M * K, B, Kc)) return -1;
+  if (bqo_prepare_table(c_in, Kc, c) != 0) return -1;
   for (int64_t m = 0; m < M; ++m)
     for (int64_t n = 0; n < N; ++n) {
       double s = 0.0;
@@ -286,8 +311,10 @@ int bqo_linear_blockwise(const void* x, int dtype, int64_t M, int64_t K, int64_t
  * the N x K row-major tensor quantized over its flat index; x is M x K row-major in `dtype`;
  * y is M x N row-major binary64. */
 int bqo_gemm_blockwise(const void* x, int dtype, int64_t M, int64_t K, int64_t N, int32_t B,
-                       const float* c, int Kc, const float* absmax, const uint8_t* packed, double* y) {
+                       const float* c_in, int Kc, const float* absmax, const uint8_t* packed, double* y) {
+  float c[256];
   if (dtype == BQO_F32 || M < 0 || K < 0 || N < 0 || !valid_args(dtype, M * K, B, Kc)) return -1;
+  if (bqo_prepare_table(c_in, Kc, c) != 0) return -1;
   for (int64_t m = 0; m < M; ++m)
     for (int64_t n = 0; n < N; ++n) {
       double acc = 0.0;
@@ -327,6 +354,36 @@ float bqo_nested_mean(const float* absmax, int64_t nb) {
   return (float)(S / (double)nb);
 }
 
+/* Statistics of the groups g_lo <= g < g_hi, given the mean (R12): d_b = fl32(a_b - mean) for
+ * the blocks of each group of B2 blocks, then the group's maximum |d_b| and the code of each
+ * d_b by the same absmax / normalize / nearest rules as the data (R2..R6), with the 256-entry
+ * table c2.  Writes q2[b] for the group's blocks and absmax2[g].  Groups are independent, so
+ * any split of [0, ceil(nb / B2)) into ranges gives the same outputs. */
+int bqo_nested_groups(const float* absmax, int64_t nb, float mean, const float* c2, int K2,
+                      int32_t B2, int64_t g_lo, int64_t g_hi, uint8_t* q2, float* absmax2) {
+  if (K2 != 256 || !valid_args(BQO_F32, 1, B2, K2) || nb < 0) return -1;
+  const int64_t ng = (nb + B2 - 1) / B2;
+  if (g_lo < 0 || g_hi > ng || g_lo > g_hi) return -1;
+  if (g_lo == g_hi) return 0;
+  const int64_t b_lo = g_lo * B2, b_hi = g_hi * B2 < nb ? g_hi * B2 : nb;
+  float* d = (float*)malloc((size_t)(b_hi - b_lo) * sizeof(float));
+  if (!d) return -2;
+  for (int64_t b = b_lo; b < b_hi; ++b) d[b - b_lo] = absmax[b] - mean;
+  int rc = bqo_quantize_blockwise(d, BQO_F32, b_hi - b_lo, B2, c2, K2, absmax2 + g_lo, q2 + b_lo);
+  free(d);
+  return rc;
+}
+
+/* The whole second level of the nested statistics: mean = RN32(S / nb) (R11), then every
+ * group's q2 and absmax2 (bqo_nested_groups). */
+int bqo_nested_stats(const float* absmax, int64_t nb, const float* c2, int K2, int32_t B2,
+                     uint8_t* q2, float* absmax2, float* mean) {
+  if (nb <= 0) return nb == 0 ? 0 : -1;
+  const float m = bqo_nested_mean(absmax, nb);
+  *mean = m;
+  return bqo_nested_groups(absmax, nb, m, c2, K2, B2, 0, (nb + B2 - 1) / B2, q2, absmax2);
+}
+
 /* Quantizes `in` with table c (K entries) and block size B, then quantizes the statistics:
  * d_b = fl32(a_b - mean) in groups of B2 blocks with the 256-entry table c2 (R12), using
  * the same absmax / normalize / nearest rules as the data (R2..R6).
@@ -335,26 +392,20 @@ float bqo_nested_mean(const float* absmax, int64_t nb) {
 int bqo_quantize_nested(const void* in, int dtype, int64_t n, int32_t B, const float* c, int K,
                         const float* c2, int K2, int32_t B2, float* absmax, uint8_t* q2,
                         float* absmax2, float* mean, uint8_t* packed) {
-  if (K2 != 256 || !valid_args(BQO_F32, 1, B2, K2)) return -1;
+  float c2p[256];
+  if (K2 != 256 || !valid_args(BQO_F32, 1, B2, K2) || bqo_prepare_table(c2, K2, c2p) != 0) return -1;
   int rc = bqo_quantize_blockwise(in, dtype, n, B, c, K, absmax, packed);
   if (rc != 0 || n == 0) return rc;
-  int64_t nb = (n + B - 1) / B;
-  float m = bqo_nested_mean(absmax, nb);
-  *mean = m;
-  float* d = (float*)malloc((size_t)nb * sizeof(float));
-  if (!d) return -2;
-  for (int64_t b = 0; b < nb; ++b) d[b] = absmax[b] - m;
-  rc = bqo_quantize_blockwise(d, BQO_F32, nb, B2, c2, K2, absmax2, q2);
-  free(d);
-  return rc;
+  return bqo_nested_stats(absmax, (n + B - 1) / B, c2, K2, B2, q2, absmax2, mean);
 }
 
 /* Rebuilt absmax a'_b = fl32(fl32(c2[q2_b] * a2_g) + mean), then the blockwise dequantize
  * with a'_b. */
 int bqo_dequantize_nested(void* out, int dtype, int64_t n, int32_t B, const float* c, int K,
-                          const float* c2, int K2, int32_t B2, const uint8_t* q2,
+                          const float* c2_in, int K2, int32_t B2, const uint8_t* q2,
                           const float* absmax2, float mean, const uint8_t* packed) {
-  if (K2 != 256 || !valid_args(BQO_F32, 1, B2, K2)) return -1;
+  float c2[256];
+  if (K2 != 256 || !valid_args(BQO_F32, 1, B2, K2) || bqo_prepare_table(c2_in, K2, c2) != 0) return -1;
   if (!valid_args(dtype, n, B, K)) return -1;
   int64_t nb = (n + B - 1) / B;
   float* a = (float*)malloc((size_t)(nb ? nb : 1) * sizeof(float));

@@ -289,6 +289,71 @@ def pin_golden_nested(o):
 
 
 # ------------------------------------------------------------------------------------------
+# The code table (step 1, reading R7)
+# ------------------------------------------------------------------------------------------
+
+def pin_negative_zero_entry_reads_as_positive_zero(o):
+    """A -0.0 entry is the zero entry +0.0 (the IQ packing review takes a negative-zero scale
+    as zero).  Worked by hand with the dyadic table whose entry 8 is written as -0.0:
+      - a block of 32 zeros has absmax 0, every code is z = 8, and c[8] * 0 = +0.0;
+      - the block (2, 1/16, -1/16, 0, ...) has absmax 2, r = 1/2, so y = 1/32, -1/32 and 0
+        all lie inside (-1/16, 1/16), the half-gaps around entry 8: code 8, and c[8] * 2 = +0.0;
+    so every dequantized value is +0.0 (bits 0x00000000 in binary32, 0x0000 in bf16 / fp16),
+    where the raw -0.0 entry would give -0.0 (0x80000000 / 0x8000)."""
+    table = _hand_table().copy()
+    assert table[8] == 0
+    table[8] = np.float32(-0.0)
+    prepared = o.prepare_table(table)
+    assert prepared is not None and int(_bits32(prepared)[8]) == 0
+    blocks = [np.zeros(32, np.float32), np.float32([2.0, 1 / 16, -1 / 16] + [0.0] * 29)]
+    for x in blocks:
+        absmax, packed = o.quantize_blockwise(x, oracle.F32, 32, table)
+        assert list(oracle.unpack_codes(packed, 32, 16)[1:]) == [8] * 31
+        for dt, zero in ((oracle.F32, 0), (oracle.BF16, 0), (oracle.F16, 0)):
+            out = o.dequantize_blockwise(packed, absmax, 32, dt, 32, table)
+            raw = _bits32(out) if dt == oracle.F32 else np.asarray(out, np.uint16)
+            codes = oracle.unpack_codes(packed, 32, 16)
+            assert all(int(v) == zero for v, c in zip(raw, codes) if c == 8), (dt, raw[:4])
+    # the statistics table of the nested path too: c2 entry -0.0 is read as +0.0
+    t2 = synth.dyadic_table(256).copy()
+    assert t2[128] == 0
+    t2[128] = np.float32(-0.0)
+    assert int(_bits32(o.prepare_table(t2))[128]) == 0
+
+
+def pin_table_preconditions(o):
+    """Tables that break R7 are rejected by every entry point that takes one; the edge cases
+    of the conditions are accepted (entries exactly +-1, a nonzero entry of exactly 2^-20)."""
+    good = _hand_table()
+    bad = {
+        "unsorted": np.concatenate([good[:3][::-1], good[3:]]),
+        "duplicate": np.concatenate([good[:1], good[:15]]),
+        "nan": np.where(np.arange(16) == 5, np.float32(np.nan), good),
+        "inf": np.where(np.arange(16) == 15, np.float32(np.inf), good),
+        "above_one": np.where(np.arange(16) == 15, np.float32(1.5), good),
+        "below_minus_one": np.where(np.arange(16) == 0, np.float32(-1.0000001), good),
+        "tiny_nonzero": np.where(np.arange(16) == 9, np.float32(2.0**-21), good),
+        "both_zeros": np.concatenate([good[:8], [np.float32(-0.0)], good[8:15]]),
+        "size_15": good[:15],
+    }
+    x = np.float32([0.5, -0.25] * 16)
+    for name, t in bad.items():
+        t = np.float32(t)
+        assert o.prepare_table(t) is None, name
+        for call in (lambda: o.quantize_blockwise(x, oracle.F32, 32, t),
+                     lambda: o.dequantize_blockwise(np.zeros(16, np.uint8), np.float32([1]), 32, oracle.F32, 32, t)):
+            try:
+                call()
+            except ValueError:
+                continue
+            raise AssertionError("table %s accepted" % name)
+    edge = good.copy()
+    edge[9] = np.float32(2.0**-20)
+    assert o.prepare_table(edge) is not None
+    assert o.prepare_table(np.float32(np.linspace(-1, 1, 16))) is not None
+
+
+# ------------------------------------------------------------------------------------------
 # Blockwise: exact rational checks and invariants on random data
 # ------------------------------------------------------------------------------------------
 

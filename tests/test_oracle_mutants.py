@@ -29,8 +29,10 @@ MUTANTS = {
     "sequential_sum": ("return pairwise_sum(a, n, 0, len);",
                        "double S = 0; for (int64_t i = 0; i < n; ++i) S += a[i]; return S;"),
     "mean_in_binary32": ("return (float)(S / (double)nb);", "return (float)S / (float)nb;"),
-    "mean_not_subtracted": ("for (int64_t b = 0; b < nb; ++b) d[b] = absmax[b] - m;",
-                            "for (int64_t b = 0; b < nb; ++b) d[b] = absmax[b];"),
+    "mean_not_subtracted": ("d[b - b_lo] = absmax[b] - mean;", "d[b - b_lo] = absmax[b];"),
+    "table_negative_zero_kept": ("if (v == 0.0f) v = 0.0f; /* -0.0 -> +0.0 */", ""),
+    "table_range_unchecked": ("if (!isfinite(v) || v < -1.0f || v > 1.0f) return -1;", ""),
+    "table_order_unchecked": ("if (k > 0 && !(v > c_out[k - 1])) return -1;", ""),
     "mean_not_added_back": ("a[b] = scaled + mean;", "a[b] = scaled;"),
     "q32_nibbles_swapped": ("int lo = blk[2 + j] & 0x0f, hi = blk[2 + j] >> 4;",
                             "int hi = blk[2 + j] & 0x0f, lo = blk[2 + j] >> 4;"),
