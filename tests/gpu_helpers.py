@@ -94,3 +94,38 @@ def check_blockwise(o: oracle.Oracle, x: torch.Tensor, dtype: str, blocksize: in
         ref = o.dequantize_blockwise(op, oa, n, ORACLE_DT[odt], blocksize, table)
         assert_out_equal(out, ref, n, odt, what + " dequant->" + odt)
     return absmax, packed
+
+
+def check_linear_against_oracle(o: oracle.Oracle, y: np.ndarray, x: torch.Tensor, dtype: str, N: int, B: int,
+                                table, absmax, packed, tag: str):
+    """bq_linear_blockwise output y (M x N, host) within the bound its C ABI states of the
+    oracle's binary64 sum: |y - y_oracle| <= (K/1024 + 64) * 2^-24 * sum_k |x w|."""
+    M, K = x.shape
+    ref = o.linear_blockwise(host_bits(x), ORACLE_DT[dtype], M, K, N, B, table, absmax, packed)
+    wdeq = o.dequantize_blockwise(packed, absmax, N * K, oracle.F32, B, table).astype(np.float64).reshape(N, K)
+    mag = np.abs(x.float().cpu().numpy().astype(np.float64)) @ np.abs(wdeq).T
+    tol = (K / 1024 + 64) * 2.0 ** -24 * mag
+    err = np.abs(y.astype(np.float64) - ref)
+    bad = np.argwhere(~(err <= tol))
+    assert bad.size == 0, (tag, [(int(m), int(n), float(y[m, n]), float(ref[m, n]), float(tol[m, n]))
+                                 for m, n in bad[:5]])
+
+
+def bits_to_float64(bits: np.ndarray, dtype: str) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(TORCH_DT[dtype])
+    return t.float().numpy().astype(np.float64)
+
+
+def check_gemm_against_oracle(o: oracle.Oracle, y: np.ndarray, x: torch.Tensor, dtype: str, N: int, B: int,
+                              table, absmax, packed, tag: str):
+    """bq_gemm_blockwise output y (M x N, host) within the bound its C ABI states of the
+    oracle's binary64 sum over the 16-bit weights: |y - y_oracle| <= (K + 64) * 2^-24 * sum_k |x w16|."""
+    M, K = x.shape
+    ref = o.gemm_blockwise(host_bits(x), ORACLE_DT[dtype], M, K, N, B, table, absmax, packed)
+    w16 = bits_to_float64(o.dequantize_blockwise(packed, absmax, N * K, ORACLE_DT[dtype], B, table), dtype)
+    mag = np.abs(x.float().cpu().numpy().astype(np.float64)) @ np.abs(w16.reshape(N, K)).T
+    tol = (K + 64) * 2.0 ** -24 * mag
+    err = np.abs(y.astype(np.float64) - ref)
+    bad = np.argwhere(~(err <= tol))
+    assert bad.size == 0, (tag, [(int(m), int(n), float(y[m, n]), float(ref[m, n]), float(tol[m, n]))
+                                 for m, n in bad[:5]])

@@ -129,6 +129,8 @@ def test_nested_validation():
     assert call(stats=nstats(workspace_bytes=10)) == bq.BQ_ERR_WORKSPACE
     assert call(stats=nstats(workspace=FAKE + 16)) == bq.BQ_ERR_ALIGNMENT
     assert call(stats=nstats(mean=FAKE + 1)) == bq.BQ_ERR_ALIGNMENT
+    assert call(stats=nstats(qabsmax=FAKE + 2)) == bq.BQ_ERR_ALIGNMENT
+    assert call(stats=nstats(absmax2=FAKE + 2)) == bq.BQ_ERR_ALIGNMENT
     assert call(inp=None) == bq.BQ_ERR_NULL
     assert call(n=0) == bq.BQ_OK
     # the nested dequantize needs no workspace but checks the rest
@@ -136,6 +138,9 @@ def test_nested_validation():
     assert bq.bq_dequantize_nested(FAKE, bq.BQ_BF16, 0, 64, T16, st, FAKE, 0) == bq.BQ_OK
     assert bq.bq_dequantize_nested(FAKE, bq.BQ_BF16, 1000, 64, T16, nstats(absmax2=None), FAKE, 0) == bq.BQ_ERR_NULL
     assert bq.bq_dequantize_nested(None, bq.BQ_BF16, 1000, 64, T16, st, FAKE, 0) == bq.BQ_ERR_NULL
+    assert bq.bq_dequantize_nested(FAKE, bq.BQ_BF16, 1000, 64, T16, nstats(qabsmax=FAKE + 1, workspace=None,
+                                                                           workspace_bytes=0), FAKE, 0) \
+        == bq.BQ_ERR_ALIGNMENT
 
 
 def test_workspace_bytes():

@@ -14,7 +14,7 @@ import torch
 import dequantization_block_absmax_amd as bq
 import oracle
 import synth
-from gpu_helpers import BQ_DT, ORACLE_DT, TORCH_DT, host_bits
+from gpu_helpers import BQ_DT, ORACLE_DT, TORCH_DT, bits_to_float64, check_gemm_against_oracle, host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -62,23 +62,6 @@ def run_gpu(dev, x, dtype, N, B, table, absmax, packed):
     return y.cpu().numpy()[:, :N]
 
 
-def check_against_oracle(o, y, x, dtype, N, B, table, absmax, packed, tag):
-    M, K = x.shape
-    ref = o.gemm_blockwise(host_bits(x), ORACLE_DT[dtype], M, K, N, B, table, absmax, packed)
-    w16 = host_bits_to_float(o.dequantize_blockwise(packed, absmax, N * K, ORACLE_DT[dtype], B, table), dtype)
-    mag = np.abs(x.float().numpy().astype(np.float64)) @ np.abs(w16.reshape(N, K)).T
-    tol = (K + 64) * 2.0 ** -24 * mag
-    err = np.abs(y.astype(np.float64) - ref)
-    bad = np.argwhere(~(err <= tol))
-    assert bad.size == 0, (tag, [(int(m), int(n), float(y[m, n]), float(ref[m, n]), float(tol[m, n]))
-                                 for m, n in bad[:5]])
-
-
-def host_bits_to_float(bits: np.ndarray, dtype: str) -> np.ndarray:
-    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(TORCH_DT[dtype])
-    return t.float().numpy().astype(np.float64)
-
-
 SHAPES = [  # (M, K, N, B): single tiles, ragged rows and columns, several chunks per wave; from
     # M = 129 the LDS-tiled kernel, with an odd number of 64-k steps (K = 192, 320)
     (1, 64, 1, 32), (5, 128, 33, 64), (32, 256, 64, 128), (33, 512, 65, 32), (64, 1024, 100, 256),
@@ -94,7 +77,7 @@ def test_gemm_small_shapes(dev, o, dtype, K_table):
         absmax, packed = quantized_weights(o, N, K, B, table, seed=300 + i)
         x = activations(M, K, dtype, seed=400 + i)
         y = run_gpu(dev, x, dtype, N, B, table, absmax, packed)
-        check_against_oracle(o, y, x, dtype, N, B, table, absmax, packed,
+        check_gemm_against_oracle(o, y, x, dtype, N, B, table, absmax, packed,
                              "%s M=%d K=%d N=%d B=%d table=%d" % (dtype, M, K, N, B, K_table))
 
 
@@ -127,7 +110,7 @@ def test_gemm_weights_match_the_16_bit_dequantize(dev, o, dtype, K_table):
     table = TABLES[K_table]
     N, K, B = 96, 512, 64
     absmax, packed = quantized_weights(o, N, K, B, table, seed=500 + K_table)
-    w16 = host_bits_to_float(o.dequantize_blockwise(packed, absmax, N * K, ORACLE_DT[dtype], B, table), dtype)
+    w16 = bits_to_float64(o.dequantize_blockwise(packed, absmax, N * K, ORACLE_DT[dtype], B, table), dtype)
     # 13 rows (register-tiled kernel), then 171 (LDS-tiled kernel: every third k)
     for ks in (np.array([0, 1, 7, 63, 64, 65, 200, 255, 256, 333, 448, 510, 511]), np.arange(0, K, 3)):
         xf = np.zeros((len(ks), K), np.float32)
@@ -157,5 +140,5 @@ def test_gemm_prefill_shape_sampled_rows(dev, o, K_table, M):
     per_row = K // 2 if K_table == 16 else K
     sub_packed = np.concatenate([packed[r * per_row:(r + 1) * per_row] for r in rows])
     sub_absmax = np.concatenate([absmax[r * (K // B):(r + 1) * (K // B)] for r in rows])
-    check_against_oracle(o, y[:, rows], x, "bfloat16", len(rows), B, table, sub_absmax, sub_packed,
+    check_gemm_against_oracle(o, y[:, rows], x, "bfloat16", len(rows), B, table, sub_absmax, sub_packed,
                          "prefill shape table=%d M=%d" % (K_table, M))

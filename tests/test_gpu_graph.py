@@ -1,31 +1,43 @@
-"""The C ABI under HIP graph capture and on a two-stream copy/quantize pipeline.
+"""The C ABI under HIP graph capture and on a two-stream copy/quantize pipeline, against the
+oracle.
 
 Every call enqueues kernels only (no allocation, no host synchronization, no per-call
 host-to-device copy), so a sequence of calls can be captured once and replayed ("Respect the
 current CUDA stream in blockwise quantization", bitsandbytes PR 2052, Limitations: its graph
-capture failed on a per-call code-map copy).  Each replay is checked bit for bit against the
-eager results, with eager work and synchronizations between replays.
+capture failed on a per-call code-map copy).  Each replay is compared with the oracle (bit
+for bit for quantize / dequantize / GGUF outputs, within the stated bound for the fused
+linear and GEMM, which must also repeat the eager bits), with eager work and
+synchronizations between replays.  The pipeline's outputs are compared with the oracle run
+over the whole host array.
 """
 import numpy as np
 import pytest
 import torch
 
 import dequantization_block_absmax_amd as bq
+import oracle
 import synth
+from gpu_helpers import (assert_bytes_equal, assert_f32_bits_equal, check_gemm_against_oracle,
+                         check_linear_against_oracle, host_bits)
 
 pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(scope="module")
 def dev():
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
     return torch.device("cuda:0")
 
 
-def test_graph_replay_matches_eager(dev):
+@pytest.fixture(scope="module")
+def po():
+    return oracle.ParallelOracle()
+
+
+def test_graph_replay_matches_oracle(dev, po):
     n, B, B2 = (1 << 22) + 4099, 64, 256
-    t16, t256 = bq.code_table(synth.table16()), bq.code_table(synth.table256())
+    t16_np, t256_np = synth.table16(), synth.table256()
+    t16, t256 = bq.code_table(t16_np), bq.code_table(t256_np)
     x = synth.blockwise_input(n, "bfloat16", 41, std=0.02, p_out=1e-3, p_nf=1e-4, device=dev)
     nb = bq.num_blocks(n, B)
     ng = bq.num_blocks(nb, B2)
@@ -40,6 +52,14 @@ def test_graph_replay_matches_eager(dev):
     xl = torch.randn(Ml, Kl, device=dev, generator=gen).to(torch.bfloat16)
     Mg = 40  # fused GEMM on the same weight
     xg = torch.randn(Mg, Kl, device=dev, generator=gen).to(torch.bfloat16)
+
+    # the oracle's outputs for the same inputs
+    xb = host_bits(x)
+    ref = po.quantize_nested(xb, oracle.BF16, B, t16_np, t256_np, B2)
+    ref_out = po.dequantize_nested(ref["packed"], ref["q2"], ref["absmax2"], ref["mean"], n, oracle.BF16, B, t16_np,
+                                   t256_np, B2)
+    ref_out4 = po.dequant_q32(q4.cpu().numpy(), m, cols, oracle.Q4, oracle.BF16)
+    wpk_h, wam_h = wpk.cpu().numpy(), wam.cpu().numpy()
 
     def buffers():
         ws_bytes = bq.bq_nested_workspace_bytes(n, B, B2)
@@ -62,11 +82,23 @@ def test_graph_replay_matches_eager(dev):
         bq.check(bq.bq_linear_blockwise(xl, bq.BQ_BF16, Ml, Kl, Nl, B, t16, wam, wpk, b["y"], stream), "linear")
         bq.check(bq.bq_gemm_blockwise(xg, bq.BQ_BF16, Mg, Kl, Nl, B, t16, wam, wpk, b["yg"], stream), "gemm")
 
+    def check_against_oracle(b, what):
+        assert_bytes_equal(b["packed"].cpu().numpy(), ref["packed"], what + " packed")
+        assert_bytes_equal(b["q2"].cpu().numpy(), ref["q2"], what + " q2")
+        assert_f32_bits_equal(b["a2"].cpu().numpy(), ref["absmax2"], what + " absmax2")
+        assert_f32_bits_equal(b["mean"].cpu().numpy(), np.float32([ref["mean"]]), what + " mean")
+        assert_bytes_equal(host_bits(b["out"]), ref_out, what + " nested dequant")
+        assert_bytes_equal(host_bits(b["out4"]), ref_out4, what + " q32")
+        check_linear_against_oracle(po, b["y"].cpu().numpy(), xl.cpu(), "bfloat16", Nl, B, t16_np, wam_h, wpk_h,
+                                    what + " linear")
+        check_gemm_against_oracle(po, b["yg"].cpu().numpy(), xg.cpu(), "bfloat16", Nl, B, t16_np, wam_h, wpk_h,
+                                  what + " gemm")
+
     eager = buffers()
     run(eager)
     torch.cuda.synchronize()
-    keys = ("packed", "q2", "a2", "mean", "out", "out4", "y", "yg")
-    want = {k: eager[k].clone() for k in keys}
+    check_against_oracle(eager, "eager")
+    y_eager, yg_eager = eager["y"].clone(), eager["yg"].clone()
 
     g = buffers()
     graph = torch.cuda.CUDAGraph()
@@ -79,22 +111,25 @@ def test_graph_replay_matches_eager(dev):
     with torch.cuda.graph(graph):
         run(g)  # calls pick up torch's current (capturing) stream
     for replay in range(4):
-        for k in keys:  # clear the outputs eagerly between replays
+        for k in g:  # clear the outputs eagerly between replays
             g[k].zero_()
-        run(eager)      # unrelated eager work in between
+        run(eager)   # unrelated eager work in between
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for k in keys:
-            assert torch.equal(g[k].view(torch.uint8), want[k].view(torch.uint8)), (replay, k)
+        check_against_oracle(g, "replay %d" % replay)
+        # the fused products are not unique, but every call gives the same bits
+        assert torch.equal(g["y"].view(torch.int32), y_eager.view(torch.int32)), replay
+        assert torch.equal(g["yg"].view(torch.int32), yg_eager.view(torch.int32)), replay
 
 
-def test_two_stream_copy_quantize_pipeline(dev):
+def test_two_stream_copy_quantize_pipeline(dev, po):
     """Host chunks are copied on one stream (pinned memory) while the previous chunk is
-    quantized on another; events order each quantize after its copy.  The result equals one
-    quantize call per chunk on the default stream."""
+    quantized on another; events order each quantize after its copy.  Every absmax and code
+    byte equals the oracle's over the whole host array."""
     chunk, nchunks, B = 1 << 22, 6, 256
-    t16 = bq.code_table(synth.table16())
+    t16_np = synth.table16()
+    t16 = bq.code_table(t16_np)
     host = synth.blockwise_input(chunk * nchunks, "float16", 43, std=1.0, p_out=1e-3).view(torch.int16)
     host = host.pin_memory()
     dev_in = [torch.empty(chunk, dtype=torch.int16, device=dev) for _ in range(2)]
@@ -115,11 +150,6 @@ def test_two_stream_copy_quantize_pipeline(dev):
         bq.check(bq.bq_quantize_blockwise(buf, bq.BQ_F16, chunk, B, t16, absmax[c], packed[c], work_s))
         used[c].record(work_s)
     torch.cuda.synchronize()
-    full = host.to(dev).view(torch.float16)
-    for c in range(nchunks):
-        a = torch.empty(nb, dtype=torch.float32, device=dev)
-        p = torch.empty(chunk // 2, dtype=torch.uint8, device=dev)
-        bq.check(bq.bq_quantize_blockwise(full[c * chunk:(c + 1) * chunk], bq.BQ_F16, chunk, B, t16, a, p))
-        torch.cuda.synchronize()
-        assert torch.equal(a.view(torch.int32), absmax[c].view(torch.int32)), c
-        assert torch.equal(p, packed[c]), c
+    oa, op = po.quantize_blockwise(host.numpy().view(np.uint16), oracle.F16, B, t16_np)
+    assert_f32_bits_equal(absmax.cpu().numpy().reshape(-1), oa, "pipeline absmax")
+    assert_bytes_equal(packed.cpu().numpy().reshape(-1), op, "pipeline codes")

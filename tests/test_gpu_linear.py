@@ -13,7 +13,7 @@ import torch
 import dequantization_block_absmax_amd as bq
 import oracle
 import synth
-from gpu_helpers import BQ_DT, ORACLE_DT, TORCH_DT, host_bits
+from gpu_helpers import BQ_DT, ORACLE_DT, TORCH_DT, check_linear_against_oracle, host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -61,18 +61,6 @@ def run_gpu(dev, x, dtype, N, B, table, absmax, packed):
     return y.cpu().numpy()[:, :N]
 
 
-def check_against_oracle(o, y, x, dtype, N, B, table, absmax, packed, tag):
-    M, K = x.shape
-    ref = o.linear_blockwise(host_bits(x), ORACLE_DT[dtype], M, K, N, B, table, absmax, packed)
-    wdeq = o.dequantize_blockwise(packed, absmax, N * K, oracle.F32, B, table).astype(np.float64).reshape(N, K)
-    mag = np.abs(x.float().numpy().astype(np.float64)) @ np.abs(wdeq).T
-    tol = (K / 1024 + 64) * 2.0 ** -24 * mag
-    err = np.abs(y.astype(np.float64) - ref)
-    bad = np.argwhere(~(err <= tol))
-    assert bad.size == 0, (tag, [(int(m), int(n), float(y[m, n]), float(ref[m, n]), float(tol[m, n]))
-                                 for m, n in bad[:5]])
-
-
 SHAPES = [  # (K, N, B): one-chunk, ragged chunk, several chunks per wave, partial row groups
     (16, 1, 32), (48, 9, 32), (1024, 8, 64), (1040, 17, 128), (3072, 5, 2048), (4112, 37, 4096),
     (9216, 11, 256),
@@ -88,7 +76,7 @@ def test_linear_small_shapes(dev, o, dtype, K_table):
         for M in (1, 2, 3, 4):
             x = activations(M, K, dtype, seed=200 + 10 * i + M)
             y = run_gpu(dev, x, dtype, N, B, table, absmax, packed)
-            check_against_oracle(o, y, x, dtype, N, B, table, absmax, packed,
+            check_linear_against_oracle(o, y, x, dtype, N, B, table, absmax, packed,
                                  "%s K=%d N=%d B=%d M=%d table=%d" % (dtype, K, N, B, M, K_table))
 
 
@@ -127,5 +115,5 @@ def test_linear_decode_shape_sampled_rows(dev, o, K_table, M):
     per_row = K // 2 if K_table == 16 else K
     sub_packed = np.concatenate([packed[r * per_row:(r + 1) * per_row] for r in rows])
     sub_absmax = np.concatenate([absmax[r * (K // B):(r + 1) * (K // B)] for r in rows])
-    check_against_oracle(o, y[:, rows], x, "bfloat16", len(rows), B, table, sub_absmax, sub_packed,
+    check_linear_against_oracle(o, y[:, rows], x, "bfloat16", len(rows), B, table, sub_absmax, sub_packed,
                          "decode shape table=%d M=%d" % (K_table, M))

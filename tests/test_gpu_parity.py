@@ -1,10 +1,10 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle, bit for bit.
 
-Sizes where the oracle finishes in seconds are compared in full (several 8192-element tiles
-and ragged tails, every dtype, table size and block size).  The full-size workloads are the
-five benchmark configurations; where the oracle is too slow for all of one (256-entry codes
-of 2^26 elements, 2^29 nested elements) it checks sampled blocks and groups, and
-size-independent properties cover the rest (every block absmax against numpy)."""
+Every output is compared in full with the oracle: small and ragged shapes (several
+8192-element tiles and tails, every dtype, table size and block size) and the five full-size
+benchmark workloads.  At the full sizes the oracle runs on contiguous ranges of whole blocks
+(groups, rows) from several host threads (oracle.ParallelOracle), which gives the same bytes
+as one call over the whole input."""
 import json
 import os
 
@@ -35,6 +35,11 @@ def dev():
 @pytest.fixture(scope="module")
 def o():
     return oracle.Oracle()
+
+
+@pytest.fixture(scope="module")
+def po():
+    return oracle.ParallelOracle()
 
 
 def _sync():
@@ -247,7 +252,7 @@ def gpu_nested(x: torch.Tensor, dtype: str, B: int, t16, t256, B2=256, out_dtype
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("B,B2", [(64, 256), (32, 32), (128, 64), (4096, 256), (256, 4096), (512, 32), (1024, 64),
-                                  (2048, 128)])
+                                  (2048, 128), (32, 512), (64, 1024), (128, 2048)])
 def test_nested_full_parity(dev, o, dtype, B, B2):
     t16, t256 = synth.table16(), synth.table256()
     for n in (B * B2 * 3 + B * 7 + 5, 777, B * B2):
@@ -325,92 +330,38 @@ def test_fp32_2pow19_4bit_blocksize64(dev, o):
     check_blockwise(o, x, "float32", 64, synth.table16(), "fp32 2^19 B=64")
 
 
-def test_fp16_2pow23plus1_4bit_all_blocksizes(dev, o):
+def test_fp16_2pow23plus1_4bit_all_blocksizes(dev, po):
     x = synth.blockwise_input(8388609, "float16", 2, std=1.0, p_out=1e-3, p_nf=1e-4, device=dev)
     for B in BLOCKSIZES:
-        check_blockwise(o, x, "float16", B, synth.table16(), "fp16 2^23+1 B=%d" % B)
+        check_blockwise(po, x, "float16", B, synth.table16(), "fp16 2^23+1 B=%d" % B)
 
 
-def _finite_absmax_np(xbits: np.ndarray, dtype: str, B: int) -> np.ndarray:
-    """Block max of |x| over finite x, with numpy (an independent check at any size)."""
-    n = xbits.size
-    nb = -(-n // B)
-    if dtype == "bfloat16":
-        v = (xbits.astype(np.uint32) << 16).view(np.float32)
-    elif dtype == "float16":
-        v = xbits.view(np.float16).astype(np.float32)
-    else:
-        v = xbits
-    a = np.where(np.isfinite(v), np.abs(v), np.float32(0))
-    pad = nb * B - n
-    if pad:
-        a = np.concatenate([a, np.zeros(pad, np.float32)])
-    return a.reshape(nb, B).max(axis=1)
-
-
-def _sample_blocks(nb: int, count: int, seed: int) -> np.ndarray:
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, nb - 1], rng.integers(0, nb, count)]))
-
-
-def test_bf16_2pow26_8bit_blocksize4096(dev, o):
+def test_bf16_2pow26_8bit_blocksize4096(dev, po):
+    """bf16, n = 2^26 (128 MiB), 8-bit codes, B = 4096: every absmax, code byte and
+    dequantized element against the oracle."""
     n, B = 67108864, 4096
     t256 = synth.table256()
     x = synth.blockwise_input(n, "bfloat16", 3, std=0.02, device=dev)
     absmax, packed = gpu_quantize(x, "bfloat16", B, t256)
     out = gpu_dequantize(packed, absmax, n, "bfloat16", B, t256)
     xb = host_bits(x)
-    a_gpu = absmax.cpu().numpy()
-    assert_f32_bits_equal(a_gpu, _finite_absmax_np(xb, "bfloat16", B), "bf16 2^26 8-bit absmax (all blocks)")
-    p_gpu = packed.cpu().numpy()
-    o_gpu = host_bits(out)
-    for b in _sample_blocks(n // B, 30, 3):
-        sl = slice(b * B, (b + 1) * B)
-        oa, op = o.quantize_blockwise(xb[sl], oracle.BF16, B, t256)
-        assert_f32_bits_equal(a_gpu[b:b + 1], oa, "bf16 2^26 8-bit absmax block %d" % b)
-        assert_bytes_equal(p_gpu[sl], op, "bf16 2^26 8-bit codes block %d" % b)
-        ref = o.dequantize_blockwise(op, oa, B, oracle.BF16, B, t256)
-        assert_bytes_equal(o_gpu[sl], ref, "bf16 2^26 8-bit dequant block %d" % b)
+    what = "bf16 2^26 8-bit B=4096"
+    oa, op = po.quantize_blockwise(xb, oracle.BF16, B, t256)
+    assert_f32_bits_equal(absmax.cpu().numpy()[:oa.size], oa, what + " absmax")
+    assert_bytes_equal(packed.cpu().numpy()[:op.size], op, what + " codes")
+    ref = po.dequantize_blockwise(op, oa, n, oracle.BF16, B, t256)
+    assert_bytes_equal(host_bits(out)[:n], ref, what + " dequant")
 
 
 # ---- 8-bit codes, several tiles per workgroup ----------------------------------------------
 
-# 3,075 tiles of 8192 elements, the last one partial: more tiles than workgroups resident on
-# the device, so each workgroup of the 8-bit quantizer takes several, one of them partial.
+# 3,075 tiles of 8192 elements, the last one partial: several times more workgroups than the
+# device holds at once, with 8-bit codes.
 N_MANY = 3 * (1 << 23) + 3 * 8192 + 77
 
 
-def _codes_are_nearest(xb: np.ndarray, dtype: str, B: int, absmax: np.ndarray, codes: np.ndarray, table,
-                       what: str):
-    """Every element's code is a nearest table entry to x / absmax (binary64, ties within
-    2^-20 accepted either way): a check of all codes that needs no oracle pass over them."""
-    if dtype == "bfloat16":
-        v = (xb.astype(np.uint32) << 16).view(np.float32)
-    elif dtype == "float16":
-        v = xb.view(np.float16).astype(np.float32)
-    else:
-        v = xb
-    a = np.repeat(absmax.astype(np.float64), B)[:v.size]
-    fin = np.isfinite(v) & (a > 0)
-    y = np.where(fin, v.astype(np.float64) / np.where(a > 0, a, 1.0), 0.0)
-    t = np.asarray(table, np.float64)
-    err = np.abs(y - t[codes])
-    i = np.clip(np.searchsorted(t, y), 1, t.size - 1)  # the two entries around y (table ascending)
-    best = np.minimum(np.abs(y - t[i - 1]), np.abs(y - t[i]))
-    bad = np.nonzero(err > best + 2.0 ** -20)[0]
-    assert bad.size == 0, "%s: %d codes not nearest, first at %d" % (what, bad.size, bad[0])
-
-
-def _tile_edge_blocks(n: int, B: int, seed: int) -> np.ndarray:
-    """Blocks at both ends, at the partial tile, at tile boundaries near the end and start,
-    and random others."""
-    nb = -(-n // B)
-    edges = [0, 8192 - 1, 8192, 2 * 8192, (n // 8192) * 8192 - 1, (n // 8192) * 8192, n - 1]
-    return np.unique(np.concatenate([[e // B for e in edges], _sample_blocks(nb, 24, seed)]))
-
-
 @pytest.mark.parametrize("dtype,B", [("bfloat16", 4096), ("float32", 64), ("float16", 256)])
-def test_8bit_several_tiles_per_workgroup(dev, o, dtype, B):
+def test_8bit_several_tiles_per_workgroup(dev, po, dtype, B):
     n = N_MANY
     t256 = synth.table256()
     x = synth.blockwise_input(n, dtype, 41, std=0.02, p_out=1e-4, p_nf=1e-5, device=dev)
@@ -418,49 +369,33 @@ def test_8bit_several_tiles_per_workgroup(dev, o, dtype, B):
     out = gpu_dequantize(packed, absmax, n, dtype, B, t256)
     xb = host_bits(x)
     what = "8-bit %s n=%d B=%d" % (dtype, n, B)
-    a_gpu = absmax.cpu().numpy()
-    assert_f32_bits_equal(a_gpu, _finite_absmax_np(xb, dtype, B), what + " absmax (all blocks)")
-    p_gpu = packed.cpu().numpy()[:n]
-    _codes_are_nearest(xb, dtype, B, a_gpu, p_gpu, t256, what + " codes (all)")
-    o_gpu = host_bits(out)
-    for b in _tile_edge_blocks(n, B, 41):
-        lo, hi = b * B, min((b + 1) * B, n)
-        oa, op = o.quantize_blockwise(xb[lo:hi], ORACLE_DT[dtype], B, t256)
-        assert_f32_bits_equal(a_gpu[b:b + 1], oa, "%s absmax block %d" % (what, b))
-        assert_bytes_equal(p_gpu[lo:hi], op, "%s codes block %d" % (what, b))
-        ref = o.dequantize_blockwise(op, oa, hi - lo, ORACLE_DT[dtype], B, t256)
-        assert_out_equal(out[lo:hi], ref, hi - lo, dtype, "%s dequant block %d" % (what, b))
+    oa, op = po.quantize_blockwise(xb, ORACLE_DT[dtype], B, t256)
+    assert_f32_bits_equal(absmax.cpu().numpy()[:oa.size], oa, what + " absmax")
+    assert_bytes_equal(packed.cpu().numpy()[:op.size], op, what + " codes")
+    ref = po.dequantize_blockwise(op, oa, n, ORACLE_DT[dtype], B, t256)
+    assert_out_equal(out, ref, n, dtype, what + " dequant")
 
 
-def test_8bit_nested_several_tiles_per_workgroup(dev, o):
-    """The nested statistics over 8-bit data codes at N_MANY elements: every block absmax,
-    the mean, q2 and absmax2 in full; data codes and the nested dequantize on sampled groups."""
+def test_8bit_nested_several_tiles_per_workgroup(dev, po):
+    """The nested statistics over 8-bit data codes at N_MANY elements, every output in full."""
     n, B, B2 = N_MANY, 64, 256
     t256 = synth.table256()
     x = synth.blockwise_input(n, "bfloat16", 43, std=0.02, p_out=1e-4, p_nf=1e-5, device=dev)
     r = gpu_nested(x, "bfloat16", B, t256, t256, B2)
-    xb = host_bits(x)
-    what = "nested 8-bit bf16 n=%d" % n
-    a_ref = _finite_absmax_np(xb, "bfloat16", B)
-    assert_f32_bits_equal(r["absmax"].cpu().numpy(), a_ref, what + " absmax")
-    m_ref = o.nested_mean(a_ref)
-    assert np.float32(r["mean"].item()).view(np.uint32) == np.float32(m_ref).view(np.uint32), what + " mean"
-    a2_ref, q2_ref = o.quantize_blockwise((a_ref - m_ref).astype(np.float32), oracle.F32, B2, t256)
-    q2 = r["q2"].cpu().numpy()
-    absmax2 = r["absmax2"].cpu().numpy()
-    assert_f32_bits_equal(absmax2, a2_ref, what + " absmax2")
-    assert_bytes_equal(q2, q2_ref, what + " q2")
-    packed = r["packed"].cpu().numpy()
-    out = r["out"]
-    gsize = B * B2
-    ng = absmax2.size
-    for g in np.unique([0, 1, ng // 2, ng - 2, ng - 1]):
-        lo, hi = g * gsize, min((g + 1) * gsize, n)
-        _, op = o.quantize_blockwise(xb[lo:hi], oracle.BF16, B, t256)
-        assert_bytes_equal(packed[lo:hi], op, "%s codes group %d" % (what, g))
-        ref = o.dequantize_nested(op, q2[g * B2:g * B2 + (hi - lo + B - 1) // B], absmax2[g:g + 1], m_ref, hi - lo,
-                                  oracle.BF16, B, t256, t256, B2)
-        assert_out_equal(out[lo:hi], ref, hi - lo, "bfloat16", "%s dequant group %d" % (what, g))
+    check_nested_full(po, r, host_bits(x), "bfloat16", n, B, t256, t256, B2, "nested 8-bit bf16 n=%d" % n)
+
+
+def check_nested_full(po, r, xb, dtype, n, B, t_data, t_stats, B2, what):
+    """Every output of a nested quantize + dequantize on the GPU against the oracle."""
+    ref = po.quantize_nested(xb, ORACLE_DT[dtype], B, t_data, t_stats, B2)
+    assert_f32_bits_equal(r["absmax"].cpu().numpy(), ref["absmax"], what + " absmax")
+    assert np.float32(r["mean"].item()).view(np.uint32) == np.float32(ref["mean"]).view(np.uint32), what + " mean"
+    assert_bytes_equal(r["q2"].cpu().numpy(), ref["q2"], what + " q2")
+    assert_f32_bits_equal(r["absmax2"].cpu().numpy(), ref["absmax2"], what + " absmax2")
+    assert_bytes_equal(r["packed"].cpu().numpy()[:ref["packed"].size], ref["packed"], what + " packed")
+    out_ref = po.dequantize_nested(ref["packed"], ref["q2"], ref["absmax2"], ref["mean"], n, ORACLE_DT[dtype], B,
+                                   t_data, t_stats, B2)
+    assert_out_equal(r["out"], out_ref, n, dtype, what + " dequant")
 
 
 @pytest.mark.parametrize("fmt", ["q4", "q8"])
@@ -502,30 +437,105 @@ def test_gguf_4096x14336(dev, o, fmt):
         assert_out_equal(out2, ref2, m, odt, "gguf 4096x14336 %s -> %s" % (fmt, odt))
 
 
-def test_bf16_2pow29_4bit_nested(dev, o):
+def test_bf16_2pow29_4bit_nested(dev, po):
+    """bf16, n = 2^29 (1 GiB), 4-bit codes, B = 64, nested statistics in groups of 256: every
+    absmax, code byte, q2, absmax2, the mean and every dequantized element against the oracle."""
     n, B, B2 = 536870912, 64, 256
     t16, t256 = synth.table16(), synth.table256()
     x = synth.blockwise_input(n, "bfloat16", 5, std=0.02, device=dev)
     r = gpu_nested(x, "bfloat16", B, t16, t256, B2)
     _sync()
-    nb = n // B
     xb = host_bits(x)
-    a_gpu = r["absmax"].cpu().numpy()
-    assert_f32_bits_equal(a_gpu, _finite_absmax_np(xb, "bfloat16", B), "bf16 2^29 nested absmax (all blocks)")
-    m_ref = o.nested_mean(a_gpu)
-    assert np.float32(r["mean"].item()).view(np.uint32) == np.float32(m_ref).view(np.uint32), "bf16 2^29 nested mean"
-    q2 = r["q2"].cpu().numpy()
-    a2 = r["absmax2"].cpu().numpy()
-    p_gpu = r["packed"].cpu().numpy()
-    o_gpu = host_bits(r["out"])
-    d = (a_gpu - np.float32(m_ref)).astype(np.float32)
-    for g in _sample_blocks(nb // B2, 6, 5):
-        gs = slice(g * B2, (g + 1) * B2)
-        ra2, rq2 = o.quantize_blockwise(d[gs], oracle.F32, B2, t256)
-        assert_f32_bits_equal(a2[g:g + 1], ra2, "bf16 2^29 nested absmax2 group %d" % g)
-        assert_bytes_equal(q2[gs], rq2, "bf16 2^29 nested q2 group %d" % g)
-        es = slice(g * B2 * B, (g + 1) * B2 * B)
-        oa, op = o.quantize_blockwise(xb[es], oracle.BF16, B, t16)
-        assert_bytes_equal(p_gpu[g * B2 * B // 2:(g + 1) * B2 * B // 2], op, "bf16 2^29 nested codes group %d" % g)
-        ref = o.dequantize_nested(op, rq2, ra2, m_ref, B2 * B, oracle.BF16, B, t16, t256, B2)
-        assert_bytes_equal(o_gpu[es], ref, "bf16 2^29 nested dequant group %d" % g)
+    del x
+    check_nested_full(po, r, xb, "bfloat16", n, B, t16, t256, B2, "bf16 2^29 nested")
+
+
+# ---- GGUF blocks with special scales, and a table with a -0.0 entry ----------------------
+
+@pytest.mark.parametrize("fmt", ["q4", "q8"])
+def test_q32_special_scales(dev, o, fmt):
+    """Blocks whose fp16 scale is NaN (either sign), +-Inf, +-0, negative, subnormal or the
+    largest finite value, in whole and partial tiles, against the oracle.  A NaN result is
+    compared as a NaN (its sign and payload are not defined by IEEE 754 for 0 * Inf, and a NaN
+    scale's sign may be dropped by the multiply); every other element bit for bit."""
+    bs = 18 if fmt == "q4" else 34
+    f = bq.BQ_Q32_Q4 if fmt == "q4" else bq.BQ_Q32_Q8
+    of = oracle.Q4 if fmt == "q4" else oracle.Q8
+    nblk = 128 * 3 + 21
+    blocks = synth.q32_blocks(nblk, fmt, seed=12).cpu().numpy().copy()
+    scales = [0x7E00, 0xFE00, 0x7C01, 0x7C00, 0xFC00, 0x0000, 0x8000, 0xBC00, 0x8001, 0x0001, 0x7BFF, 0xFBFF,
+              0xC500, 0x83FF]
+    rng = np.random.default_rng(3)
+    for b in range(nblk):  # every fourth block takes a special scale, the rest random signs
+        d = scales[(b // 4) % len(scales)] if b % 4 == 0 else int(blocks[b * bs]) | (int(blocks[b * bs + 1]) << 8)
+        if b % 4 == 2:
+            d |= 0x8000 * int(rng.integers(0, 2))
+        blocks[b * bs] = d & 0xFF
+        blocks[b * bs + 1] = d >> 8
+    if fmt == "q4":  # make sure q - 8 == 0 meets an infinite scale: byte 0x88 in some blocks
+        blocks[np.arange(0, nblk, 4) * bs + 2] = 0x88
+    dblk = torch.tensor(blocks, device=dev)
+    n = nblk * 32
+    for odt in DTYPES:
+        out = torch.empty(n, dtype=TORCH_DT[odt], device=dev)
+        bq.check(bq.bq_dequant_q32(dblk, BQ_DT[odt], n, 32, f, out))
+        ref = o.dequant_q32(blocks, n, 32, of, ORACLE_DT[odt])
+        got = host_bits(out)[:n]
+        what = "q32 %s special scales -> %s" % (fmt, odt)
+        if odt == "float32":
+            assert_f32_bits_equal(got, ref, what)
+        else:
+            exp_mask = 0x7F80 if odt == "bfloat16" else 0x7C00
+            g_nan = ((got & exp_mask) == exp_mask) & ((got & ~np.uint16(0x8000 | exp_mask)) != 0)
+            r_nan = ((ref & exp_mask) == exp_mask) & ((ref & ~np.uint16(0x8000 | exp_mask)) != 0)
+            assert np.array_equal(g_nan, r_nan), what + ": NaN positions differ"
+            assert_bytes_equal(got[~r_nan], ref[~r_nan], what)
+
+
+def test_negative_zero_table_entry(dev, o):
+    """A table whose zero entry is written as -0.0 quantizes and dequantizes exactly like the
+    oracle, which reads it as +0.0: zero blocks and elements near zero dequantize to +0.0."""
+    base = synth.table16().copy()
+    t = base.copy()
+    t[base == 0] = np.float32(-0.0)
+    assert np.signbit(t[base == 0]).all()
+    x = synth.blockwise_input(3 * 8192 + 77, "bfloat16", 19, std=1.0, p_out=0.01, p_nf=0.001, device=dev)
+    x[:4096] = 0  # zero blocks
+    x[8192:8192 + 64:2] = 0
+    for B in (32, 64, 4096):
+        absmax, packed = check_blockwise(o, x, "bfloat16", B, t, "-0.0 entry B=%d" % B, out_dtypes=DTYPES)
+        out = gpu_dequantize(packed, absmax, x.numel(), "float32", B, t)
+        assert not np.signbit(out[:4096].cpu().numpy()).any(), "a zero block dequantized to -0.0"
+    z = torch.zeros(8192 * 2, dtype=torch.float32, device=dev)
+    check_blockwise(o, z, "float32", 64, synth.dyadic_table(256), "zeros, dyadic 256 table")
+    d = synth.dyadic_table(256).copy()
+    d[128] = np.float32(-0.0)
+    check_blockwise(o, z, "float32", 64, d, "zeros, dyadic 256 table with -0.0", out_dtypes=DTYPES)
+
+
+def test_data_kernel_timing_hook(dev, o):
+    """Events armed with bq_debug_time_next_data_kernel bracket the data kernel of the next
+    nested quantize only (a positive elapsed time, shorter than the whole call), are forgotten
+    after it, and leave the outputs unchanged."""
+    n, B = 1 << 22, 64
+    t16, t256 = synth.table16(), synth.table256()
+    x = synth.blockwise_input(n, "bfloat16", 17, std=0.02, device=dev)
+    r0 = gpu_nested(x, "bfloat16", B, t16, t256)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    assert bq.bq_debug_time_next_data_kernel(e0, None) == bq.BQ_ERR_NULL
+    bq.check(bq.bq_debug_time_next_data_kernel(e0, e1))
+    c0.record()
+    r1 = gpu_nested(x, "bfloat16", B, t16, t256)
+    c1.record()
+    torch.cuda.synchronize()
+    k_ms, call_ms = e0.elapsed_time(e1), c0.elapsed_time(c1)
+    assert 0 < k_ms < call_ms, (k_ms, call_ms)
+    for k in ("absmax", "q2", "absmax2", "packed", "out"):
+        assert torch.equal(r0[k].view(torch.uint8), r1[k].view(torch.uint8)), k
+    # disarmed after one use: a later call records nothing into the events
+    e1.record()
+    torch.cuda.synchronize()
+    gpu_nested(x, "bfloat16", B, t16, t256)
+    torch.cuda.synchronize()
+    assert e0.elapsed_time(e1) >= k_ms
