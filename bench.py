@@ -10,9 +10,14 @@ One step is one pass of the whole hot path over one batch of synthetic input:
 Inputs are generated on the device before timing (they are resident in HBM when the timed
 region starts).  `value` is input bytes of the step / step time (the metric's "effective
 GB/s (input bytes)"); every call's algorithmic read+write bytes against the 8 TB/s HBM peak
-is in `detail`.  `roofline` is the slower of the two 1 GiB kernels (data quantize, nested
-dequantize), timed with HIP events on the stream it runs on; `cpu_baseline` is the CPU
-oracle on a bounded sample of the same workload.
+is in `detail`.  `roofline` is the slower of the two 1 GiB kernels, each timed per launch
+inside the timed steps with HIP events on the stream it runs on: the data kernel of
+bq_quantize_nested (events armed through bq_debug_time_next_data_kernel, so they bracket that
+kernel as the call launches it) and the one kernel of bq_dequantize_nested.  `cpu_baseline` is
+the CPU oracle on the whole step input from as many host threads as the oracle may use (at
+most 16), plus the same oracle on one thread over a sixteenth of the step; the threaded
+oracle's outputs are also this run's parity reference (`parity`: every output byte of the
+step's calls against the oracle's).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-detail] [--no-cpu-baseline]
     python bench.py --profile     (a few launches of each kernel plus a 1 GiB copy, for rocprofv3)
@@ -82,6 +87,7 @@ class Workload:
         self.q4 = synth.q32_blocks(self.n4 // 32, "q4", seed=4, device=dev)
         self.q8 = synth.q32_blocks(self.n4 // 32, "q8", seed=4, device=dev)
         self.out4 = torch.empty(self.n4, dtype=torch.bfloat16, device=dev)
+        self.out8 = torch.empty(self.n4, dtype=torch.bfloat16, device=dev)
         self.q32_sets = {}  # rotated GGUF buffer sets of the per-call timing
         e = 2 ** 29
         # input bytes and algorithmic read+write bytes of each call
@@ -118,7 +124,7 @@ class Workload:
         elif name == "dequant_q32_q4":
             st = bq.bq_dequant_q32(self.q4, bq.BQ_BF16, self.n4, self.COLS, bq.BQ_Q32_Q4, self.out4)
         elif name == "dequant_q32_q8":
-            st = bq.bq_dequant_q32(self.q8, bq.BQ_BF16, self.n4, self.COLS, bq.BQ_Q32_Q8, self.out4)
+            st = bq.bq_dequant_q32(self.q8, bq.BQ_BF16, self.n4, self.COLS, bq.BQ_Q32_Q8, self.out8)
         elif name == "quantize_kernel":  # the data kernel of quantize_nested on its own
             st = bq.bq_quantize_blockwise(self.x, bq.BQ_BF16, self.N5, self.B5, self.t16, self.absmax, self.packed)
         else:
@@ -130,20 +136,34 @@ STEP = ["quantize_nested", "dequantize_nested", "dequant_q32_q4", "dequant_q32_q
 ROUNDS, REPS = 7, 10  # per-call breakdown: interleaved rounds of back-to-back calls
 
 
-def timed_step_loop(w: Workload, torch, steps: int):
+def timed_step_loop(w: Workload, bq, torch, steps: int):
     """Runs `steps` steps between two HIP events on the current stream (the stream every call
-    is enqueued on); returns the elapsed ms of the whole region and the host wall ms."""
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    is enqueued on).  Inside, each step's nested-quantize data kernel and nested-dequantize
+    kernel are bracketed by events of their own.  Returns the elapsed ms of the whole region,
+    the host wall ms, and the per-launch ms of the two kernels."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    a, b = ev(), ev()
+    qk = [(ev(), ev()) for _ in range(steps)]
+    dk = [(ev(), ev()) for _ in range(steps)]
+    for e0, e1 in qk + dk:  # create the events before the timed region
+        e0.record()
+        e1.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     a.record()
-    for _ in range(steps):
-        for name in STEP:
-            w.run(name)
+    for i in range(steps):
+        bq.check(bq.bq_debug_time_next_data_kernel(*qk[i]), "arm data-kernel events")
+        w.run("quantize_nested")
+        dk[i][0].record()
+        w.run("dequantize_nested")
+        dk[i][1].record()
+        w.run("dequant_q32_q4")
+        w.run("dequant_q32_q8")
     b.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
-    return a.elapsed_time(b), wall_ms
+    return (a.elapsed_time(b), wall_ms, [e0.elapsed_time(e1) for e0, e1 in qk],
+            [e0.elapsed_time(e1) for e0, e1 in dk])
 
 
 def time_calls(fn, torch, reps: int) -> float:
@@ -391,30 +411,87 @@ def loading_pipeline(bq, synth, torch, dev, table, chunks=8, chunk=1 << 25, B=64
         quantize_hidden=round(copy_ms / pipe_ms, 3))}
 
 
-def cpu_baseline(w: Workload, torch):
-    """The CPU oracle (single-threaded, as it stands) on a bounded sample of the step."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def step_outputs(w: Workload, torch):
+    """Host copies of every output of one step (the last one run)."""
+    import numpy as np
+
+    def bits(t):
+        return t.cpu().view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.cpu().numpy()
+    return dict(packed=w.packed.cpu().numpy(), q2=w.q2.cpu().numpy(), absmax2=w.absmax2.cpu().numpy(),
+                mean=w.mean.cpu().numpy()[:1], out=bits(w.out), out4=bits(w.out4), out8=bits(w.out8))
+
+
+def oracle_step(o, w: Workload, xs, b4, b8, n5: int, rows: int) -> dict:
+    """The oracle on the first n5 elements of the 1 GiB tensor and the first `rows` rows of
+    both GGUF matrices: the calls of one step, in order."""
     import numpy as np
 
     import oracle
-    o = oracle.Oracle()
-    n5 = 1 << 27
-    rows = 2048
-    xs = w.x[:n5].cpu().view(torch.int16).numpy().view(np.uint16)
-    m4 = rows * w.COLS
-    b4 = w.q4[: m4 // 32 * 18].cpu().numpy()
-    b8 = w.q8[: m4 // 32 * 34].cpu().numpy()
-    t0 = time.perf_counter()
-    r = o.quantize_nested(xs, oracle.BF16, w.B5, w.t16_np, w.t256_np, w.B2)
-    o.dequantize_nested(r["packed"], r["q2"], r["absmax2"], r["mean"], n5, oracle.BF16, w.B5, w.t16_np, w.t256_np,
-                        w.B2)
-    o.dequant_q32(b4, m4, w.COLS, oracle.Q4, oracle.BF16)
-    o.dequant_q32(b8, m4, w.COLS, oracle.Q8, oracle.BF16)
-    dt = time.perf_counter() - t0
+    r = o.quantize_nested(xs[:n5], oracle.BF16, w.B5, w.t16_np, w.t256_np, w.B2)
+    out = o.dequantize_nested(r["packed"], r["q2"], r["absmax2"], r["mean"], n5, oracle.BF16, w.B5, w.t16_np,
+                              w.t256_np, w.B2)
+    m = rows * w.COLS
+    out4 = o.dequant_q32(b4[:m // 32 * 18], m, w.COLS, oracle.Q4, oracle.BF16)
+    out8 = o.dequant_q32(b8[:m // 32 * 34], m, w.COLS, oracle.Q8, oracle.BF16)
+    return dict(packed=r["packed"], q2=r["q2"], absmax2=r["absmax2"], mean=np.float32([r["mean"]]), out=out,
+                out4=out4, out8=out8)
+
+
+def step_input_bytes(w: Workload, n5: int, rows: int) -> int:
     nb = n5 // w.B5
-    inp = 2 * n5 + (n5 // 2 + nb + 4 * (-(-nb // w.B2)) + 4) + b4.size + b8.size
-    return dict(value=round(inp / dt / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                sample="first 2^27 elements of the 2^29 bf16 tensor (nested quantize + dequantize) and the first "
-                       "2048 of 4096 rows of both GGUF matrices; %.1f s single-threaded" % dt)
+    q2_in = n5 // 2 + nb + 4 * (-(-nb // w.B2)) + 4
+    return 2 * n5 + q2_in + rows * w.COLS // 32 * (18 + 34)
+
+
+def cpu_baseline_and_parity(w: Workload, torch, gpu: dict):
+    """The CPU oracle as it stands, on this run's inputs.  (i) The whole step from as many host
+    threads as the oracle uses (contiguous ranges of whole blocks, groups and rows; at most
+    16); its outputs are compared byte for byte with the step's GPU outputs.  (ii) One thread
+    over a sixteenth of the step (the first 2^25 elements and 256 rows), the single-core rate."""
+    import numpy as np
+
+    import oracle
+    xs = w.x.cpu().view(torch.int16).numpy().view(np.uint16)
+    b4, b8 = w.q4.cpu().numpy(), w.q8.cpu().numpy()
+    po = oracle.ParallelOracle()
+    t0 = time.perf_counter()
+    ref = oracle_step(po, w, xs, b4, b8, w.N5, w.ROWS)
+    dt_n = time.perf_counter() - t0
+    mismatched = []
+    for k, v in ref.items():
+        g = gpu[k][:v.size]
+        if g.shape != v.shape or not np.array_equal(g.view(np.uint8), np.ascontiguousarray(v).view(np.uint8)):
+            mismatched.append(k)
+    del ref
+    o1 = oracle.Oracle()
+    n1, rows1 = w.N5 // 16, w.ROWS // 16
+    t0 = time.perf_counter()
+    oracle_step(o1, w, xs, b4, b8, n1, rows1)
+    dt_1 = time.perf_counter() - t0
+    full = step_input_bytes(w, w.N5, w.ROWS)
+    part = step_input_bytes(w, n1, rows1)
+    cpu = dict(value=round(full / dt_n / 1e9, 4), unit="GB/s", cores=po.threads, kind="oracle",
+               sample="the whole step input (bf16 2^29 nested quantize + dequantize, both 4096x14336 GGUF "
+                      "matrices) on %d host threads over contiguous ranges of whole blocks, groups and rows: "
+                      "%.1f s" % (po.threads, dt_n),
+               cpu_model=cpu_model(), os_cpu_count=os.cpu_count(),
+               single_thread=dict(value=round(part / dt_1 / 1e9, 4), unit="GB/s", cores=1,
+                                  sample="first 2^25 elements and first 256 rows (1/16 of the step): %.1f s" % dt_1))
+    parity = dict(ok=not mismatched, mismatched=mismatched,
+                  compared="every byte of packed, q2, absmax2, mean, the nested dequantize and both GGUF outputs "
+                           "of the last timed step against the threaded oracle")
+    return cpu, parity
 
 
 def main():
@@ -462,8 +539,9 @@ def main():
     for _ in range(args.warmup):
         for name in STEP:
             w.run(name)
-    total_ms, wall_ms = timed_step_loop(w, torch, args.steps)
+    total_ms, wall_ms, qk_ms, dk_ms = timed_step_loop(w, bq, torch, args.steps)
     ms_per_step = total_ms / args.steps
+    gpu_out = None if args.no_cpu_baseline else step_outputs(w, torch)  # the last timed step's outputs
     # Per-call breakdown: each call back to back between two events (an event between calls
     # adds a few microseconds of its own), REPS calls per round.  The GGUF calls rotate over
     # buffer sets of more than 1 GiB in total, so that back-to-back calls do not find their data
@@ -472,7 +550,7 @@ def main():
     # The call types take turns over several rounds and each reports its median round: clocks
     # drift under sustained load, and a fixed order would hand the drift to whichever call is
     # timed at the wrong moment.
-    rounds = {name: [] for name in STEP + ["quantize_kernel"]}
+    rounds = {name: [] for name in STEP + ["quantize_kernel"]}  # + the blockwise quantize alone
     for _ in range(ROUNDS):
         for name in rounds:
             if name.startswith("dequant_q32"):
@@ -491,31 +569,47 @@ def main():
         detail[name] = dict(us=round(ms * 1e3, 2), input_gbs=round(c["inp"] / ms / 1e6, 1),
                             rw_gbs=round(c["rw"] / ms / 1e6, 1), pct_hbm_peak=round(100 * c["rw"] / ms / 1e6 / PEAK_GBS, 1))
 
-    # Roofline of the dominant kernel: the slower of the data quantize kernel (timed on its own,
-    # same launch as inside quantize_nested) and the nested dequantize kernel (one launch per
-    # call), each as the median round of back-to-back launches between two HIP events.
-    qk_ms = per["quantize_kernel"]
+    # Roofline of the dominant kernel: the slower (by mean launch time over the timed steps) of
+    # the data kernel inside bq_quantize_nested and the kernel of bq_dequantize_nested.  The data
+    # kernel's algorithmic bytes are the method's: 2 B of bf16 read and 0.5 B of codes written per
+    # element; what it also writes for the statistics (the block maxima and per-wave partial sums
+    # in the workspace, read back by the statistics kernels) is reported as intermediate bytes.
     n = w.N5
-    q_bytes = 2 * n + n // 2 + 4 * w.nb
+    qk_mean, dk_mean = statistics.fmean(qk_ms), statistics.fmean(dk_ms)
+    q_bytes = 2 * n + n // 2
+    q_inter = w.ws_bytes
     dq_bytes = w.calls["dequantize_nested"]["rw"]
-    detail["quantize_kernel"] = dict(us=round(qk_ms * 1e3, 2), rw_gbs=round(q_bytes / qk_ms / 1e6, 1),
-                                     pct_hbm_peak=round(100 * q_bytes / qk_ms / 1e6 / PEAK_GBS, 1))
-    if qk_ms >= per["dequantize_nested"]:
-        kname, kbytes, kms = "quantize_kernel", q_bytes, qk_ms
+    detail["quantize_nested data kernel (in-step launches)"] = dict(
+        us_mean=round(qk_mean * 1e3, 2), us_median=round(statistics.median(qk_ms) * 1e3, 2),
+        pct_hbm_peak=round(100 * q_bytes / qk_mean / 1e6 / PEAK_GBS, 1),
+        pct_hbm_peak_with_intermediate=round(100 * (q_bytes + q_inter) / qk_mean / 1e6 / PEAK_GBS, 1))
+    detail["dequantize_nested kernel (in-step launches)"] = dict(
+        us_mean=round(dk_mean * 1e3, 2), us_median=round(statistics.median(dk_ms) * 1e3, 2),
+        pct_hbm_peak=round(100 * dq_bytes / dk_mean / 1e6 / PEAK_GBS, 1))
+    detail["quantize_blockwise of the same tensor (no statistics)"] = dict(
+        us=round(per["quantize_kernel"] * 1e3, 2),
+        pct_hbm_peak=round(100 * (q_bytes + 4 * w.nb) / per["quantize_kernel"] / 1e6 / PEAK_GBS, 1))
+    if qk_mean >= dk_mean:
+        roofline = dict(kernel="quantize_kernel<2, 4, 0, 1>, the data kernel of bq_quantize_nested",
+                        bytes_per_launch=q_bytes, intermediate_bytes_per_launch=q_inter, ms=qk_mean,
+                        traffic=traffic_for("quantize_kernel"))
     else:
-        kname, kbytes, kms = "dequantize_nested_kernel", dq_bytes, per["dequantize_nested"]
-    achieved = kbytes / kms / 1e6
+        roofline = dict(kernel="dequantize_nested_kernel<2, 4>, the kernel of bq_dequantize_nested",
+                        bytes_per_launch=dq_bytes, ms=dk_mean, traffic=traffic_for("dequantize_nested_kernel"))
+    kms = roofline.pop("ms")
+    achieved = roofline["bytes_per_launch"] / kms / 1e6
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / PEAK_GBS, 4), traffic=traffic_for(kname), kernel=kname,
-                    bytes_per_launch=kbytes, us_per_launch=round(kms * 1e3, 2))
+                    frac=round(achieved / PEAK_GBS, 4), traffic=roofline.pop("traffic"),
+                    us_per_launch=round(kms * 1e3, 2), launches=len(qk_ms), **roofline)
 
     if not args.no_detail:
         log("timing the individual workloads")
         detail.update(detail_configs(bq, synth, torch, dev, PEAK_GBS))
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a sample")
-        cpu = cpu_baseline(w, torch)
+        log("running the CPU oracle on the step input (threaded), then a single-thread sample")
+        cpu, parity = cpu_baseline_and_parity(w, torch, gpu_out)
+        del gpu_out
 
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -525,7 +619,7 @@ def main():
                                "plus GGUF-style 4096x14336 Q4 and Q8 block dequant to bf16",
                    "n": w.N5, "blocksize": w.B5, "blocksize2": w.B2, "gguf_shape": [w.ROWS, w.COLS],
                    "step_input_bytes": step_input},
-        "roofline": roofline, "cpu_baseline": cpu, "detail": detail,
+        "roofline": roofline, "cpu_baseline": cpu, "parity": parity, "detail": detail,
     }
     print(json.dumps(rec), flush=True)
 

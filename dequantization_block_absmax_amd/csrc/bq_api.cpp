@@ -13,6 +13,7 @@
 #include <mutex>
 
 #include "bq.h"
+#include "bq_debug.h"
 #include "bq_internal.h"
 
 namespace {
@@ -29,10 +30,16 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 
 thread_local int g_last_hip_error = 0;
 
+// Events armed by bq_debug_time_next_data_kernel for the next nested quantize on this thread.
+thread_local hipEvent_t g_data_kernel_start = nullptr, g_data_kernel_stop = nullptr;
+
 bq_status hip_status(int e) {
+  const bool refused = bq::g_launch_refused_for_size;
+  bq::g_launch_refused_for_size = false;
   if (e == 0) return BQ_OK;
-  // the launcher's own refusal of a grid over 2^32 - 1 threads (no launch was made)
-  if (e == (int)hipErrorInvalidConfiguration) return BQ_ERR_SIZE;
+  // the launcher's own refusal of a grid over 2^32 - 1 threads (no launch was made); the same
+  // error code from the runtime is a failed launch like any other
+  if (refused && e == (int)hipErrorInvalidConfiguration) return BQ_ERR_SIZE;
   g_last_hip_error = e;
   return BQ_ERR_HIP;
 }
@@ -105,6 +112,13 @@ struct Tables {
 extern "C" {
 
 int bq_last_hip_error(void) { return g_last_hip_error; }
+
+bq_status bq_debug_time_next_data_kernel(hipEvent_t start, hipEvent_t stop) {
+  if ((start == nullptr) != (stop == nullptr)) return BQ_ERR_NULL;
+  g_data_kernel_start = start;
+  g_data_kernel_stop = stop;
+  return BQ_OK;
+}
 
 const char* bq_status_string(bq_status s) {
   switch (s) {
@@ -220,7 +234,7 @@ static bq_status check_nested(const bq_nested_stats* stats, bq::PreparedTable* t
   if (t2->K != 256) return BQ_ERR_TABLE;
   if (n == 0) return BQ_OK;
   if (stats->qabsmax == nullptr || stats->absmax2 == nullptr || stats->mean == nullptr) return BQ_ERR_NULL;
-  if (!aligned(stats->absmax2, 4) || !aligned(stats->mean, 4)) return BQ_ERR_ALIGNMENT;
+  if (!aligned(stats->qabsmax, 4) || !aligned(stats->absmax2, 4) || !aligned(stats->mean, 4)) return BQ_ERR_ALIGNMENT;
   if (need_ws) {
     if (stats->workspace == nullptr) return BQ_ERR_WORKSPACE;
     if (!aligned(stats->workspace, 256)) return BQ_ERR_ALIGNMENT;
@@ -247,8 +261,12 @@ bq_status bq_quantize_nested(const void* in, bq_dtype dtype, int64_t n, int32_t 
   if (!aligned(in, 16) || !aligned(packed, 16)) return BQ_ERR_ALIGNMENT;
   float* ws_absmax = static_cast<float*>(stats->workspace);
   double* ws_partials = reinterpret_cast<double*>(static_cast<uint8_t*>(stats->workspace) + ws_partials_offset(nb));
+  hipEvent_t ev0 = g_data_kernel_start, ev1 = g_data_kernel_stop;
+  g_data_kernel_start = g_data_kernel_stop = nullptr;
+  if (ev0 != nullptr && hipEventRecord(ev0, stream) != hipSuccess) return hip_status((int)hipErrorInvalidValue);
   int e = bq::launch_quantize(in, dtype, n, blocksize, t.data, ws_absmax, packed, ws_partials, stream);
   if (e != 0) return hip_status(e);
+  if (ev1 != nullptr && hipEventRecord(ev1, stream) != hipSuccess) return hip_status((int)hipErrorInvalidValue);
   e = bq::launch_nested_stats(ws_absmax, nb, stats->blocksize2, t.stats, ws_partials,
                               bq::quantize_partials(n, blocksize),
                               stats->qabsmax, stats->absmax2, stats->mean, stream);

@@ -101,6 +101,11 @@ BQ_HD float bits_f32(uint32_t u) {
 
 // Launchers (k_*.hip).  Each returns the hipError_t of its launches as an int.
 namespace bq {
+// Set when the launcher itself refuses a grid of more than 2^32 - 1 threads (it then returns
+// hipErrorInvalidConfiguration without calling HIP); the C ABI layer reads and clears it, so
+// that this refusal is told apart from the same error coming from the runtime.
+inline thread_local bool g_launch_refused_for_size = false;
+
 // Fused dequantize + linear for M <= 4 (k_linear.hip): y (M x N, binary32) = x . deq(W)^T.
 int launch_linear(const void* x, int dtype, int64_t M, int64_t K, int64_t N, int blocksize, const DequantArgs& da,
                   const float* absmax, const uint8_t* packed, float* y, void* stream);

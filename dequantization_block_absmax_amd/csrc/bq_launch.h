@@ -12,6 +12,8 @@
 #include <type_traits>
 #include <utility>
 
+#include "bq_internal.h"
+
 namespace bq {
 
 // A launch's threads per dimension (workgroups times workgroup size) must fit in 32 bits;
@@ -19,8 +21,10 @@ namespace bq {
 template <typename... KArgs, typename... Args>
 hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream, Args&&... args) {
   if ((uint64_t)grid.x * block.x > UINT32_MAX || (uint64_t)grid.y * block.y > UINT32_MAX ||
-      (uint64_t)grid.z * block.z > UINT32_MAX)
+      (uint64_t)grid.z * block.z > UINT32_MAX) {
+    g_launch_refused_for_size = true;
     return hipErrorInvalidConfiguration;
+  }
   std::tuple<std::decay_t<KArgs>...> vals(std::forward<Args>(args)...);
   return std::apply(
       [&](auto&... v) {

@@ -105,7 +105,7 @@ bq_status bq_dequantize_blockwise(void* out, bq_dtype dtype, int64_t n, int32_t 
  *              `blocksize2` blocks by the same absmax / normalize / nearest rules;
  *   rebuilt  a'_b = fl32(fl32(c2[q2_b] * absmax2_g) + mean), used by the nested dequantize. */
 typedef struct {
-  uint8_t* qabsmax;            /* [device] nb codes q2_b (nb = ceil(n / blocksize)) */
+  uint8_t* qabsmax;            /* [device] nb codes q2_b (nb = ceil(n / blocksize)), 4-byte aligned */
   float* absmax2;              /* [device] ceil(nb / blocksize2) binary32 group maxima */
   float* mean;                 /* [device] 1 binary32 value */
   const bq_code_table* table;  /* [host] 256-entry statistics table */

@@ -1,5 +1,7 @@
 /*
- * bq_debug.h -- test hooks of libbq (host only; no HIP call, usable without a GPU).
+ * bq_debug.h -- test and measurement hooks of libbq.  bq_debug_nearest_codes makes no HIP call
+ * and works without a GPU; bq_debug_time_next_data_kernel only arms events that a later call
+ * records.
  */
 #ifndef BQ_DEBUG_H
 #define BQ_DEBUG_H
@@ -24,6 +26,15 @@ extern "C" {
  * Returns BQ_OK, BQ_ERR_NULL or BQ_ERR_TABLE. */
 bq_status bq_debug_nearest_codes(const bq_code_table* table, const float* y, int64_t count,
                                  int32_t* codes, int32_t* mode, int32_t* compares);
+
+/* Measurement hook: the next bq_quantize_nested call made on the calling thread records
+ * `start` on its stream right before it enqueues its data kernel (the blockwise quantize of
+ * the data, which also writes the workspace) and `stop` right after, then forgets both, so
+ * that hipEventElapsedTime(start, stop) is that kernel's own duration as the call launches
+ * it.  The events are the caller's (created with timing enabled) and must stay valid until
+ * that call returns; a failed hipEventRecord makes that call return BQ_ERR_HIP.  Passing two
+ * NULLs disarms the hook.  Returns BQ_OK, or BQ_ERR_NULL when exactly one event is NULL. */
+bq_status bq_debug_time_next_data_kernel(hipEvent_t start, hipEvent_t stop);
 
 #ifdef __cplusplus
 }
