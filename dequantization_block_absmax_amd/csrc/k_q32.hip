@@ -48,8 +48,13 @@ __device__ __forceinline__ void store8(uint8_t* out, int64_t e, const float* v) 
         lo = __builtin_bit_cast(uint16_t, (__bf16)v[2 * i]);
         hi = __builtin_bit_cast(uint16_t, (__bf16)v[2 * i + 1]);
       } else {
-        lo = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i]);
-        hi = __builtin_bit_cast(uint16_t, (_Float16)v[2 * i + 1]);
+        // The product is held in a register before the conversion: folded into it, the multiply
+        // becomes a mixed-precision fma (v_fma_mixlo_f16) with a +0 addend, which turns the -0
+        // of (q - 8) * d = 0 * (negative d) into +0.
+        float a = v[2 * i], b = v[2 * i + 1];
+        asm("" : "+v"(a), "+v"(b));
+        lo = __builtin_bit_cast(uint16_t, (_Float16)a);
+        hi = __builtin_bit_cast(uint16_t, (_Float16)b);
       }
       w[i] = (uint32_t)lo | ((uint32_t)hi << 16);
     }
