@@ -11,9 +11,9 @@ Inputs are generated on the device before timing (they are resident in HBM when 
 region starts).  `value` is input bytes of the step / step time (the metric's "effective
 GB/s (input bytes)"); every call's algorithmic read+write bytes against the 8 TB/s HBM peak
 is in `detail`.  `roofline` is the slower of the two 1 GiB kernels, each timed per launch
-inside the timed steps with HIP events on the stream it runs on: the data kernel of
-bq_quantize_nested (events armed through bq_debug_time_next_data_kernel, so they bracket that
-kernel as the call launches it) and the one kernel of bq_dequantize_nested.  `cpu_baseline` is
+with HIP events on the stream it runs on, over as many steps again right after the timed
+region: the data kernel of bq_quantize_nested and the one kernel of bq_dequantize_nested
+(bq_debug_time_next_kernel: the launch stamps its own start and end into two events).  `cpu_baseline` is
 the CPU oracle on the whole step input from as many host threads as the oracle may use (at
 most 16), plus the same oracle on one thread over a sixteenth of the step; the threaded
 oracle's outputs are also this run's parity reference (`parity`: every output byte of the
@@ -132,38 +132,90 @@ class Workload:
         bq.check(st, name)
 
 
+class TimingEvents:
+    """HIP events created with hipEventDisableSystemFence, through the HIP runtime torch has
+    loaded (dlopen of the same path returns the same library), for the kernel launches that
+    stamp their own start and end (hipExtLaunchKernel, armed by bq_debug_time_next_kernel).
+    Events recorded between kernels instead put a marker packet there, which on MI355X left
+    about 5 us of idle GPU on each side of the bracketed kernel and counted it in the kernel's
+    time.  Read them after a device synchronization."""
+
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self, torch):
+        import ctypes
+        import re
+        self.torch = torch
+        torch.cuda.init()
+        with open("/proc/self/maps") as f:
+            paths = sorted(set(re.findall(r"(/\S*libamdhip64\S*)", f.read())))
+        if not paths:
+            raise RuntimeError("the HIP runtime torch uses is not loaded")
+        self.hip = ctypes.CDLL(paths[0])
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.c_void_p, ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ctypes = ctypes
+        self.made = []
+
+    def new(self) -> int:
+        ev = self.ctypes.c_void_p()
+        if self.hip.hipEventCreateWithFlags(self.ctypes.byref(ev), self.FLAGS) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self.made.append(ev.value)
+        return ev.value
+
+    def ms(self, a: int, b: int) -> float:
+        out = self.ctypes.c_float()
+        if self.hip.hipEventElapsedTime(self.ctypes.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def close(self):
+        for ev in self.made:
+            self.hip.hipEventDestroy(ev)
+        self.made = []
+
+
 STEP = ["quantize_nested", "dequantize_nested", "dequant_q32_q4", "dequant_q32_q8"]
 ROUNDS, REPS = 7, 10  # per-call breakdown: interleaved rounds of back-to-back calls
 
 
-def timed_step_loop(w: Workload, bq, torch, steps: int):
+def timed_step_loop(w: Workload, torch, steps: int):
     """Runs `steps` steps between two HIP events on the current stream (the stream every call
-    is enqueued on).  Inside, each step's nested-quantize data kernel and nested-dequantize
-    kernel are bracketed by events of their own.  Returns the elapsed ms of the whole region,
-    the host wall ms, and the per-launch ms of the two kernels."""
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    a, b = ev(), ev()
-    qk = [(ev(), ev()) for _ in range(steps)]
-    dk = [(ev(), ev()) for _ in range(steps)]
-    for e0, e1 in qk + dk:  # create the events before the timed region
-        e0.record()
-        e1.record()
+    is enqueued on), with nothing between the kernels; returns the elapsed ms of the whole
+    region and the host wall ms."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     a.record()
-    for i in range(steps):
-        bq.check(bq.bq_debug_time_next_data_kernel(*qk[i]), "arm data-kernel events")
-        w.run("quantize_nested")
-        dk[i][0].record()
-        w.run("dequantize_nested")
-        dk[i][1].record()
-        w.run("dequant_q32_q4")
-        w.run("dequant_q32_q8")
+    for _ in range(steps):
+        for name in STEP:
+            w.run(name)
     b.record()
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
-    return (a.elapsed_time(b), wall_ms, [e0.elapsed_time(e1) for e0, e1 in qk],
-            [e0.elapsed_time(e1) for e0, e1 in dk])
+    return a.elapsed_time(b), (time.perf_counter() - t0) * 1e3
+
+
+def kernel_step_loop(w: Workload, bq, torch, steps: int, tev: TimingEvents):
+    """The same steps again, right after the timed region, with the launches of the
+    nested-quantize data kernel and of the nested-dequantize kernel stamping their own start
+    and end into events (bq_debug_time_next_kernel).  Each stamped launch idles the GPU for a
+    few microseconds on each side, so the stamped steps are kept out of the timed region.
+    Returns the per-launch ms of the two kernels."""
+    qk = [(tev.new(), tev.new()) for _ in range(steps)]
+    dk = [(tev.new(), tev.new()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        bq.check(bq.bq_debug_time_next_kernel(*qk[i]), "arm data-kernel events")
+        w.run("quantize_nested")
+        bq.check(bq.bq_debug_time_next_kernel(*dk[i]), "arm dequantize-kernel events")
+        w.run("dequantize_nested")
+        w.run("dequant_q32_q4")
+        w.run("dequant_q32_q8")
+    torch.cuda.synchronize()
+    return [tev.ms(e0, e1) for e0, e1 in qk], [tev.ms(e0, e1) for e0, e1 in dk]
 
 
 def time_calls(fn, torch, reps: int) -> float:
@@ -539,9 +591,12 @@ def main():
     for _ in range(args.warmup):
         for name in STEP:
             w.run(name)
-    total_ms, wall_ms, qk_ms, dk_ms = timed_step_loop(w, bq, torch, args.steps)
+    total_ms, wall_ms = timed_step_loop(w, torch, args.steps)
     ms_per_step = total_ms / args.steps
     gpu_out = None if args.no_cpu_baseline else step_outputs(w, torch)  # the last timed step's outputs
+    tev = TimingEvents(torch)
+    qk_ms, dk_ms = kernel_step_loop(w, bq, torch, args.steps, tev)
+    tev.close()
     # Per-call breakdown: each call back to back between two events (an event between calls
     # adds a few microseconds of its own), REPS calls per round.  The GGUF calls rotate over
     # buffer sets of more than 1 GiB in total, so that back-to-back calls do not find their data
@@ -569,7 +624,7 @@ def main():
         detail[name] = dict(us=round(ms * 1e3, 2), input_gbs=round(c["inp"] / ms / 1e6, 1),
                             rw_gbs=round(c["rw"] / ms / 1e6, 1), pct_hbm_peak=round(100 * c["rw"] / ms / 1e6 / PEAK_GBS, 1))
 
-    # Roofline of the dominant kernel: the slower (by mean launch time over the timed steps) of
+    # Roofline of the dominant kernel: the slower (by mean launch time over the stamped steps) of
     # the data kernel inside bq_quantize_nested and the kernel of bq_dequantize_nested.  The data
     # kernel's algorithmic bytes are the method's: 2 B of bf16 read and 0.5 B of codes written per
     # element; what it also writes for the statistics (the block maxima and per-wave partial sums
@@ -579,11 +634,11 @@ def main():
     q_bytes = 2 * n + n // 2
     q_inter = w.ws_bytes
     dq_bytes = w.calls["dequantize_nested"]["rw"]
-    detail["quantize_nested data kernel (in-step launches)"] = dict(
+    detail["quantize_nested data kernel (stamped launches)"] = dict(
         us_mean=round(qk_mean * 1e3, 2), us_median=round(statistics.median(qk_ms) * 1e3, 2),
         pct_hbm_peak=round(100 * q_bytes / qk_mean / 1e6 / PEAK_GBS, 1),
         pct_hbm_peak_with_intermediate=round(100 * (q_bytes + q_inter) / qk_mean / 1e6 / PEAK_GBS, 1))
-    detail["dequantize_nested kernel (in-step launches)"] = dict(
+    detail["dequantize_nested kernel (stamped launches)"] = dict(
         us_mean=round(dk_mean * 1e3, 2), us_median=round(statistics.median(dk_ms) * 1e3, 2),
         pct_hbm_peak=round(100 * dq_bytes / dk_mean / 1e6 / PEAK_GBS, 1))
     detail["quantize_blockwise of the same tensor (no statistics)"] = dict(

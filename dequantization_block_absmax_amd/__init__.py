@@ -24,7 +24,7 @@ BQ_Q32_Q4, BQ_Q32_Q8 = 0, 1
 EXPORTS = ("bq_quantize_blockwise", "bq_dequantize_blockwise", "bq_quantize_nested",
            "bq_dequantize_nested", "bq_dequant_q32", "bq_nested_workspace_bytes", "bq_status_string",
            "bq_debug_nearest_codes", "bq_last_hip_error", "bq_linear_blockwise", "bq_gemm_blockwise",
-           "bq_debug_time_next_data_kernel")
+           "bq_debug_time_next_kernel")
 
 
 class BQError(RuntimeError):
@@ -77,8 +77,8 @@ def _load() -> ctypes.CDLL:
     lib.bq_nested_workspace_bytes.restype = ctypes.c_size_t
     lib.bq_debug_nearest_codes.argtypes = [tp, vp, i64, vp, vp, vp]
     lib.bq_debug_nearest_codes.restype = st
-    lib.bq_debug_time_next_data_kernel.argtypes = [vp, vp]
-    lib.bq_debug_time_next_data_kernel.restype = st
+    lib.bq_debug_time_next_kernel.argtypes = [vp, vp]
+    lib.bq_debug_time_next_kernel.restype = st
     lib.bq_last_hip_error.argtypes = []
     lib.bq_last_hip_error.restype = st
     lib.bq_status_string.argtypes = [st]
@@ -219,9 +219,10 @@ def _event(e) -> int | None:
     return e.cuda_event or None
 
 
-def bq_debug_time_next_data_kernel(start, stop) -> int:
-    """Arms two events around the data kernel of the next bq_quantize_nested on this thread."""
-    return _lib.bq_debug_time_next_data_kernel(_event(start), _event(stop))
+def bq_debug_time_next_kernel(start, stop) -> int:
+    """Arms two events that the next kernel the library launches on this thread stamps with its
+    own start and end (the data kernel of a nested quantize, or the only kernel of other calls)."""
+    return _lib.bq_debug_time_next_kernel(_event(start), _event(stop))
 
 
 def bq_last_hip_error() -> int:

@@ -30,9 +30,6 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 
 thread_local int g_last_hip_error = 0;
 
-// Events armed by bq_debug_time_next_data_kernel for the next nested quantize on this thread.
-thread_local hipEvent_t g_data_kernel_start = nullptr, g_data_kernel_stop = nullptr;
-
 bq_status hip_status(int e) {
   const bool refused = bq::g_launch_refused_for_size;
   bq::g_launch_refused_for_size = false;
@@ -46,8 +43,9 @@ bq_status hip_status(int e) {
 
 int64_t nblocks(int64_t n, int32_t b) { return (n + b - 1) / b; }
 
-// Nested workspace: binary32 absmax[nb], then the binary64 partial sums of the quantize launch
-// (one per 2048-element wave).
+// Nested workspace: the block maxima (binary32 absmax[nb] for fp32 input, the 16-bit patterns
+// for fp16 / bf16 input, in the same region), then the binary64 partial sums of the quantize
+// launch (one per 2048-element wave).
 size_t ws_partials_offset(int64_t nb) { return ((size_t)nb * 4 + 255) & ~(size_t)255; }
 
 // absmax[nb] (fp32), padded to 256 bytes, then the quantize launch's partial sums (fp64).
@@ -113,10 +111,10 @@ extern "C" {
 
 int bq_last_hip_error(void) { return g_last_hip_error; }
 
-bq_status bq_debug_time_next_data_kernel(hipEvent_t start, hipEvent_t stop) {
+bq_status bq_debug_time_next_kernel(hipEvent_t start, hipEvent_t stop) {
   if ((start == nullptr) != (stop == nullptr)) return BQ_ERR_NULL;
-  g_data_kernel_start = start;
-  g_data_kernel_stop = stop;
+  bq::g_next_launch_start = start;
+  bq::g_next_launch_stop = stop;
   return BQ_OK;
 }
 
@@ -234,7 +232,7 @@ static bq_status check_nested(const bq_nested_stats* stats, bq::PreparedTable* t
   if (t2->K != 256) return BQ_ERR_TABLE;
   if (n == 0) return BQ_OK;
   if (stats->qabsmax == nullptr || stats->absmax2 == nullptr || stats->mean == nullptr) return BQ_ERR_NULL;
-  if (!aligned(stats->qabsmax, 4) || !aligned(stats->absmax2, 4) || !aligned(stats->mean, 4)) return BQ_ERR_ALIGNMENT;
+  if (!aligned(stats->qabsmax, 16) || !aligned(stats->absmax2, 4) || !aligned(stats->mean, 4)) return BQ_ERR_ALIGNMENT;
   if (need_ws) {
     if (stats->workspace == nullptr) return BQ_ERR_WORKSPACE;
     if (!aligned(stats->workspace, 256)) return BQ_ERR_ALIGNMENT;
@@ -243,34 +241,46 @@ static bq_status check_nested(const bq_nested_stats* stats, bq::PreparedTable* t
   return BQ_OK;
 }
 
-bq_status bq_quantize_nested(const void* in, bq_dtype dtype, int64_t n, int32_t blocksize,
-                             const bq_code_table* code_table, bq_nested_stats* stats,
-                             uint8_t* packed, hipStream_t stream) {
+// Validation of a nested quantize; the workspace is checked only when the caller brings it.
+static bq_status check_quantize_nested(const void* in, bq_dtype dtype, int64_t n, int32_t blocksize,
+                                       const bq_code_table* code_table, const bq_nested_stats* stats,
+                                       const uint8_t* packed, bool caller_ws, Tables* t) {
   if (!valid_dtype(dtype)) return BQ_ERR_DTYPE;
   if (n < 0) return BQ_ERR_SIZE;
   if (!valid_blocksize(blocksize)) return BQ_ERR_BLOCKSIZE;
-  Tables t;
-  bq_status st = check_table(code_table, &t.data);
+  bq_status st = check_table(code_table, &t->data);
   if (st != BQ_OK) return st;
-  st = check_nested(stats, &t.stats, true, n, blocksize);
+  st = check_nested(stats, &t->stats, caller_ws, n, blocksize);
   if (st != BQ_OK) return st;
   if (n == 0) return BQ_OK;
   if (in == nullptr || packed == nullptr) return BQ_ERR_NULL;
-  const int64_t nb = nblocks(n, blocksize);
-  if (nb > INT32_MAX) return BQ_ERR_SIZE;
+  if (nblocks(n, blocksize) > INT32_MAX) return BQ_ERR_SIZE;
   if (!aligned(in, 16) || !aligned(packed, 16)) return BQ_ERR_ALIGNMENT;
-  float* ws_absmax = static_cast<float*>(stats->workspace);
-  double* ws_partials = reinterpret_cast<double*>(static_cast<uint8_t*>(stats->workspace) + ws_partials_offset(nb));
-  hipEvent_t ev0 = g_data_kernel_start, ev1 = g_data_kernel_stop;
-  g_data_kernel_start = g_data_kernel_stop = nullptr;
-  if (ev0 != nullptr && hipEventRecord(ev0, stream) != hipSuccess) return hip_status((int)hipErrorInvalidValue);
+  return BQ_OK;
+}
+
+// The launches of a validated nested quantize (n > 0) with workspace `ws`.
+static bq_status launch_quantize_nested(const void* in, bq_dtype dtype, int64_t n, int32_t blocksize,
+                                        const Tables& t, const bq_nested_stats* stats, uint8_t* packed, void* ws,
+                                        hipStream_t stream) {
+  const int64_t nb = nblocks(n, blocksize);
+  void* ws_absmax = ws;
+  double* ws_partials = reinterpret_cast<double*>(static_cast<uint8_t*>(ws) + ws_partials_offset(nb));
   int e = bq::launch_quantize(in, dtype, n, blocksize, t.data, ws_absmax, packed, ws_partials, stream);
   if (e != 0) return hip_status(e);
-  if (ev1 != nullptr && hipEventRecord(ev1, stream) != hipSuccess) return hip_status((int)hipErrorInvalidValue);
-  e = bq::launch_nested_stats(ws_absmax, nb, stats->blocksize2, t.stats, ws_partials,
+  e = bq::launch_nested_stats(ws_absmax, dtype, nb, stats->blocksize2, t.stats, ws_partials,
                               bq::quantize_partials(n, blocksize),
                               stats->qabsmax, stats->absmax2, stats->mean, stream);
   return hip_status(e);
+}
+
+bq_status bq_quantize_nested(const void* in, bq_dtype dtype, int64_t n, int32_t blocksize,
+                             const bq_code_table* code_table, bq_nested_stats* stats,
+                             uint8_t* packed, hipStream_t stream) {
+  Tables t;
+  const bq_status st = check_quantize_nested(in, dtype, n, blocksize, code_table, stats, packed, true, &t);
+  if (st != BQ_OK || n == 0) return st;
+  return launch_quantize_nested(in, dtype, n, blocksize, t, stats, packed, stats->workspace, stream);
 }
 
 bq_status bq_dequantize_nested(void* out, bq_dtype dtype, int64_t n, int32_t blocksize,

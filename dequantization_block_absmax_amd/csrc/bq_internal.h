@@ -105,6 +105,11 @@ namespace bq {
 // hipErrorInvalidConfiguration without calling HIP); the C ABI layer reads and clears it, so
 // that this refusal is told apart from the same error coming from the runtime.
 inline thread_local bool g_launch_refused_for_size = false;
+// Events (hipEvent_t) that the next kernel launch on this thread stamps with that kernel's own
+// start and end time (hipExtLaunchKernel), then forgets.  Set only by the measurement hook of
+// bq_debug.h.
+inline thread_local void* g_next_launch_start = nullptr;
+inline thread_local void* g_next_launch_stop = nullptr;
 
 // Fused dequantize + linear for M <= 4 (k_linear.hip): y (M x N, binary32) = x . deq(W)^T.
 int launch_linear(const void* x, int dtype, int64_t M, int64_t K, int64_t N, int blocksize, const DequantArgs& da,
@@ -114,8 +119,11 @@ int launch_linear(const void* x, int dtype, int64_t M, int64_t K, int64_t N, int
 int launch_gemm(const void* x, int dtype, int64_t M, int64_t K, int64_t N, int blocksize, const DequantArgs& da,
                 const float* absmax, const uint8_t* packed, float* y, void* stream);
 
+// With partials == nullptr: binary32 block maxima into absmax.  Otherwise (the data pass of a
+// nested quantize) also the per-wave partial sums, and the block maxima in the input's own
+// format (binary32 for fp32 input, the 16-bit pattern for fp16 / bf16 input).
 int launch_quantize(const void* in, int dtype, int64_t n, int blocksize, const PreparedTable& t,
-                    float* absmax, uint8_t* packed, double* partials, void* stream);
+                    void* absmax, uint8_t* packed, double* partials, void* stream);
 // Workgroups of a quantize launch over n elements.
 int quantize_grid(int64_t n);
 // Partial sums a quantize launch writes: one per wave of 2048 elements (one per pair of waves
@@ -124,7 +132,9 @@ int64_t quantize_partials(int64_t n, int blocksize);
 constexpr int64_t kQuantTileElems = 8192;  // elements per quantize tile
 int launch_dequantize(void* out, int dtype, int64_t n, int blocksize, const DequantArgs& a,
                       const float* absmax, const uint8_t* packed, void* stream);
-int launch_nested_stats(const float* absmax, int64_t nb, int blocksize2, const PreparedTable& t2,
+// absmax: the block maxima as the nested data pass stores them for `dtype` (binary32 for fp32
+// input, the 16-bit pattern for fp16 / bf16 input).
+int launch_nested_stats(const void* absmax, int dtype, int64_t nb, int blocksize2, const PreparedTable& t2,
                         double* partials, int64_t npart, uint8_t* q2, float* absmax2, float* mean,
                         void* stream);
 int launch_dequantize_nested(void* out, int dtype, int64_t n, int blocksize, int blocksize2,

@@ -7,15 +7,15 @@
 //   d_b   = fl32(a_b - mean);  per group of B2 blocks: a2_g = max |d_b|,
 //   q2_b  = nearest code of fl32(fl32(d_b * s) * fl32(1 / fl32(a2_g * s))) in the 256 table
 //
-// The data quantize kernel already writes, per wave of 2048 elements, the pairwise sum of its
-// blocks' maxima: an aligned subtree of 2^k leaves of the mean's tree (blocks past n hold +0, and
-// x + 0 = x, so padding never changes a sum).  Then:
+// The data quantize kernel already writes the block maxima (binary32, or the 16 bits of fp16 /
+// bf16 input, which hold them exactly) and, per wave of 2048 elements, the pairwise sum of its
+// blocks' maxima: an aligned subtree of 2^k leaves of the mean's tree (blocks past n hold +0,
+// and x + 0 = x, so padding never changes a sum).  Then:
 //   run_sum_kernel: sums runs of 2048 partials in place (more than 512 partials);
 //   mean_kernel:    finishes the tree (only when more than 512 run sums remain);
 //   stats_kernel:   finishes the tree itself otherwise (each workgroup, the same bits), then
-//                   one wave per 1024, 2048 or 4096 blocks (4 consecutive per lane per run of 256)
-//                   takes the same absmax / guard / LUT search as the data kernel and writes
-//                   q2 and the group maxima.
+//                   takes the same absmax / guard / LUT search as the data kernel over groups
+//                   of the block maxima and writes q2 and the group maxima.
 #include <hip/hip_runtime.h>
 
 #include "bq_device.h"
@@ -24,8 +24,6 @@
 namespace bq {
 namespace {
 
-constexpr int kThreads = 512;  // statistics workgroup: eight waves share one LUT
-constexpr int kWaves = kThreads / 64;
 constexpr int kMeanThreads = 1024;
 constexpr int kLeaves = 32;                 // sums per lane
 constexpr int kWaveLeaves = 64 * kLeaves;   // 2048: leaves per wave
@@ -82,13 +80,35 @@ __device__ __forceinline__ double wave_tree512(const double* __restrict__ leaves
 }
 constexpr int64_t kFusedLeaves = 512;  // leaves the statistics kernel sums itself
 
-// First level over many per-wave partial sums: wave w replaces leaf 2048w by the sum of
-// leaves [2048w, 2048w + 2048), an aligned subtree of the same tree (it reads its whole run
-// before lane 0 writes, and no other wave reads that run).
-__global__ __launch_bounds__(64) void run_sum_kernel(double* __restrict__ partials, int64_t npart) {
-  const int64_t i0 = (int64_t)blockIdx.x * kWaveLeaves;
-  const double s = wave_tree(partials, 1, i0, npart, threadIdx.x);
-  if (threadIdx.x == 0) partials[i0] = s;
+// First level over many per-wave partial sums: workgroup r replaces leaf 2048r by the sum of
+// leaves [2048r, 2048r + 2048), an aligned subtree of the same tree.  Thread t adds leaves
+// [8t, 8t + 8) of the run as a 3-level tree, the xor butterfly joins the aligned runs of 16 ..
+// 512 leaves inside each wave, and thread 0 joins the four waves as (w0 + w1) + (w2 + w3).  The
+// run is read in full before thread 0 writes (the barrier), and no other workgroup reads it.
+constexpr int kRunThreads = 256;
+__global__ __launch_bounds__(kRunThreads) void run_sum_kernel(double* __restrict__ partials, int64_t npart) {
+  __shared__ double s_w[kRunThreads / 64];
+  const int t = threadIdx.x;
+  const int64_t j0 = (int64_t)blockIdx.x * kWaveLeaves + (int64_t)t * 8;
+  double v[8];
+  if (j0 + 8 <= npart) {
+    const double2* p = reinterpret_cast<const double2*>(partials + j0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double2 d = p[i];
+      v[2 * i] = d.x;
+      v[2 * i + 1] = d.y;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = j0 + i < npart ? partials[j0 + i] : 0.0;
+  }
+  double s = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) s = s + __shfl_xor(s, m);
+  if ((t & 63) == 0) s_w[t >> 6] = s;
+  __syncthreads();
+  if (t == 0) partials[(int64_t)blockIdx.x * kWaveLeaves] = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
 }
 
 // Sum of `count` leaves leaves[i * stride]: 16 waves add a 32768-leaf chunk (wave sums
@@ -140,41 +160,95 @@ __global__ __launch_bounds__(kMeanThreads) void mean_kernel(const double* __rest
   }
 }
 
-// One wave covers KR runs of 256 consecutive blocks (lane l holds blocks 4l..4l+3 of each run);
-// a group of B2 blocks is ceil(B2 / 256) whole runs, or B2 / 4 lanes of one run.  All of a
-// wave's loads are issued before the LUT prologue.
-template <int MODE, int M, int KR, bool kRoundwise>
-__global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict__ absmax, int64_t nb,
-                                                         const double* __restrict__ leaves, int64_t stride,
-                                                         int64_t count, float* __restrict__ mean, int log2b2,
-                                                         int64_t ngroups, uint8_t* __restrict__ q2,
-                                                         float* __restrict__ absmax2, QuantArgs qa) {
+// Statistics of the groups.  A lane holds 16 consecutive blocks, so a group of B2 blocks is
+// g = B2 / 16 consecutive lanes; a wave holds 1024 blocks and a workgroup of 4 waves a tile of
+// 4096 (every group lies in one tile: B2 <= 4096).  The per-group work (maximum across lanes,
+// guard, reciprocal) is one wave instruction for every group the wave holds at once, so with
+// groups of 256 blocks it is shared by four groups.  Each workgroup takes kStatTiles
+// consecutive tiles, loading the next tile while it codes the current one, and builds the LUT
+// once for all of them.
+constexpr int kStatThreads = 256;
+constexpr int kBPL = 16;                           // blocks per lane
+constexpr int kStatTile = kStatThreads * kBPL;     // 4096 blocks
+constexpr int kStatTiles = 4;                      // tiles per workgroup
+
+// Block maxima as the data pass stores them: binary32, or the 16 bits of bf16 / fp16 input.
+enum AbsmaxStore : int { AS_F32 = 0, AS_BF16 = 1, AS_F16 = 2 };
+
+template <int AS>
+struct AbsmaxLoad {
+  static constexpr int kWords = AS == AS_F32 ? kBPL : kBPL / 2;  // 32-bit words per lane
+  uint32_t w[kWords];
+};
+
+// Loads the lane's 16 block maxima of tile `tile` (raw words; blocks past nb read as zero).
+template <int AS>
+__device__ __forceinline__ AbsmaxLoad<AS> load_absmax(const void* __restrict__ absmax, int64_t nb, int64_t b0) {
+  AbsmaxLoad<AS> r;
+  constexpr int kW = AbsmaxLoad<AS>::kWords;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(absmax) +
+                                                          b0 * (AS == AS_F32 ? 4 : 2));
+  if (b0 + kBPL <= nb) {
+    const uint4* p = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+    for (int i = 0; i < kW / 4; ++i) {
+      const uint4 v = p[i];
+      r.w[4 * i] = v.x;
+      r.w[4 * i + 1] = v.y;
+      r.w[4 * i + 2] = v.z;
+      r.w[4 * i + 3] = v.w;
+    }
+  } else {
+    const int nv = b0 < nb ? (int)(nb - b0) : 0;
+    if constexpr (AS == AS_F32) {
+#pragma unroll
+      for (int i = 0; i < kW; ++i) r.w[i] = i < nv ? src[i] : 0u;
+    } else {
+      const uint16_t* h = reinterpret_cast<const uint16_t*>(src);
+#pragma unroll
+      for (int i = 0; i < kW; ++i) {
+        const uint32_t lo = 2 * i < nv ? h[2 * i] : 0u;
+        const uint32_t hi = 2 * i + 1 < nv ? h[2 * i + 1] : 0u;
+        r.w[i] = lo | (hi << 16);
+      }
+    }
+  }
+  return r;
+}
+
+// Block maximum i of the lane (binary32).
+template <int AS>
+__device__ __forceinline__ float absmax_value(const AbsmaxLoad<AS>& r, int i) {
+  if constexpr (AS == AS_F32) {
+    return bits_f32(r.w[i]);
+  } else if constexpr (AS == AS_BF16) {
+    const uint32_t v = r.w[i >> 1];
+    return bits_f32((i & 1) ? (v & 0xffff0000u) : (v << 16));
+  } else {
+    const uint32_t v = r.w[i >> 1];
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)((i & 1) ? (v >> 16) : (v & 0xffffu)));
+  }
+}
+
+template <int AS, int MODE, int M>
+__global__ __launch_bounds__(kStatThreads) void stats_kernel(const void* __restrict__ absmax, int64_t nb,
+                                                             const double* __restrict__ leaves, int64_t stride,
+                                                             int64_t count, float* __restrict__ mean, int log2b2,
+                                                             int64_t ngroups, uint8_t* __restrict__ q2,
+                                                             float* __restrict__ absmax2, QuantArgs qa) {
   using E = typename Entry<M>::type;
   __shared__ float s_thr[260];
   __shared__ E s_lut[LutLayout<MODE, M>::kSize];
   __shared__ float s_mean;
+  __shared__ uint32_t s_red[2][kStatThreads / 64];  // groups wider than a wave: per-wave maxima
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int B2 = 1 << log2b2;
-  const int R = B2 > 256 ? B2 >> 8 : 1;       // runs per group
-  const int lg = B2 >= 256 ? 64 : (B2 >> 2);  // lanes per group inside a run
-  const int64_t b0 = ((int64_t)blockIdx.x * kWaves + (tid >> 6)) * 256 * KR + lane * 4;
-  const bool active = b0 - lane * 4 < nb;
+  const int g = 1 << (log2b2 - 4);  // lanes per group (2 .. 256)
+  const int64_t tile0 = (int64_t)blockIdx.x * kStatTiles;
+  const int64_t ntiles = (nb + kStatTile - 1) / kStatTile;
 
-  const auto lw = lut_fetch<MODE, M, kThreads>(qa, tid);  // table loads ahead of the data loads
-  float4 v[KR];
-#pragma unroll
-  for (int r = 0; r < KR; ++r) {
-    const int64_t b = b0 + r * 256;
-    v[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (b + 4 <= nb) {
-      v[r] = *reinterpret_cast<const float4*>(absmax + b);
-    } else if (b < nb) {
-      v[r].x = absmax[b];
-      if (b + 1 < nb) v[r].y = absmax[b + 1];
-      if (b + 2 < nb) v[r].z = absmax[b + 2];
-    }
-  }
+  const auto lw = lut_fetch<MODE, M, kStatThreads>(qa, tid);  // table loads ahead of the data loads
+  AbsmaxLoad<AS> cur = load_absmax<AS>(absmax, nb, tile0 * kStatTile + (int64_t)tid * kBPL);
   // With count > 0 every workgroup finishes the mean's tree itself (count <= 512 leaves, the
   // same bits in every workgroup); workgroup 0 stores it.  With count == 0 the mean is read.
   if (count > 0 && tid < 64) {
@@ -185,113 +259,111 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float* __restrict
       if (blockIdx.x == 0) *mean = mv;
     }
   }
-  lut_fill<MODE, M, kThreads>(qa, lw, s_lut, s_thr, tid);  // ends with a barrier: s_mean is visible
-  if (!active) return;  // whole waves
+  lut_fill<MODE, M, kStatThreads>(qa, lw, s_lut, s_thr, tid);  // ends with a barrier: s_mean is visible
   const float m = count > 0 ? s_mean : *mean;
 
-  // Codes and q2 of run r, given the group maximum key of its blocks.
-  auto emit = [&](int r, uint32_t key, const float* d) {
-    const int64_t b = b0 + r * 256;
+  for (int k = 0; k < kStatTiles; ++k) {
+    const int64_t tile = tile0 + k;
+    if (tile >= ntiles) break;  // uniform
+    const int64_t b0 = tile * kStatTile + (int64_t)tid * kBPL;
+    AbsmaxLoad<AS> next = cur;
+    if (k + 1 < kStatTiles && tile + 1 < ntiles)  // uniform
+      next = load_absmax<AS>(absmax, nb, b0 + kStatTile);
+    const bool whole = tile * kStatTile + kStatTile <= nb;  // uniform
+
+    // d = a - mean; blocks past nb contribute nothing to a group maximum (|d| of a zero pad is
+    // not used: those blocks are masked below).
+    float d[kBPL];
+#pragma unroll
+    for (int i = 0; i < kBPL; ++i) d[i] = absmax_value<AS>(cur, i) - m;
+    float amax = 0.0f;
+    if (whole) {
+#pragma unroll
+      for (int i = 0; i < kBPL; ++i) amax = fmaxf(amax, fabsf(d[i]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < kBPL; ++i)
+        if (b0 + i < nb) amax = fmaxf(amax, fabsf(d[i]));
+    }
+    // Group maximum: |d| is finite and not negative, so its bits order like its value.
+    uint32_t key = f32_bits(amax);
+    key = group_max_u32(key, g < 64 ? g : 64);
+    if (g > 64) {  // groups of 2048 or 4096 blocks span 2 or 4 waves
+      const int wave = tid >> 6;
+      if (lane == 0) s_red[k & 1][wave] = key;
+      __syncthreads();
+      const int w0 = wave & ~((g >> 6) - 1);
+      for (int w = 0; w < (g >> 6); ++w) key = max(key, s_red[k & 1][w0 + w]);
+    }
     const float a2 = bits_f32(key);
-    const int64_t g = b >> log2b2;
-    if ((lane & (lg - 1)) == 0 && (r & (R - 1)) == 0 && g < ngroups) absmax2[g] = a2;
+    const int64_t grp = b0 >> log2b2;
+    if ((tid & (g - 1)) == 0 && grp < ngroups) absmax2[grp] = a2;
     const float s = a2 < 0x1p-64f ? 0x1p64f : (a2 > 0x1p64f ? 0x1p-64f : 1.0f);
     const float rc = 1.0f / (a2 * s);
-    // (d * s) * rc is d * rc when s = 1; a wave-uniform test lets the common case skip the
-    // scaling instead of computing both and selecting.
-    uint32_t q[4];
+    uint32_t w[kBPL / 4];
     if (__builtin_expect(__all(s == 1.0f), 1)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) q[i] = nearest_code<MODE, M>(d[i] * rc, qa, s_lut, s_thr);
-    } else {
+      for (int j = 0; j < kBPL / 4; ++j) {
+        uint32_t q[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) q[i] = nearest_code<MODE, M>((d[i] * s) * rc, qa, s_lut, s_thr);
-    }
-    const uint32_t w = pack_word<8>(q);
-    if (b + 4 <= nb) {
-      *reinterpret_cast<uint32_t*>(q2 + b) = w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (b + i < nb) q2[b + i] = (uint8_t)(w >> (8 * i));
-    }
-  };
-
-  // d = a - mean; blocks past nb contribute nothing to a group maximum.
-  if constexpr (kRoundwise) {
-    // B2 <= 256: every group lies inside one run, so each run is finished as soon as its
-    // loads arrive, overlapping the codes of early runs with the loads of later ones.
-#pragma unroll
-    for (int r = 0; r < KR; ++r) {
-      const int64_t b = b0 + r * 256;
-      const float d[4] = {v[r].x - m, v[r].y - m, v[r].z - m, v[r].w - m};
-      uint32_t key = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (b + i < nb) key = max(key, f32_bits(d[i]) & 0x7fffffffu);
-      key = group_max_u32(key, lg);
-      if (b < nb) emit(r, key, d);
-    }
-  } else {
-    uint32_t key[KR];
-#pragma unroll
-    for (int r = 0; r < KR; ++r) {
-      const int64_t b = b0 + r * 256;
-      float d[4] = {v[r].x - m, v[r].y - m, v[r].z - m, v[r].w - m};
-      key[r] = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (b + i < nb) key[r] = max(key[r], f32_bits(d[i]) & 0x7fffffffu);
-      v[r] = make_float4(d[0], d[1], d[2], d[3]);
-    }
-#pragma unroll
-    for (int r = 0; r < KR; ++r)
-      key[r] = group_max_u32(key[r], lg);
-    // groups of R runs: an xor butterfly over run indices gives every run its group's maximum
-#pragma unroll
-    for (int st = 1; st < KR; st <<= 1)
-      if (st < R) {
-#pragma unroll
-        for (int r = 0; r < KR; ++r)
-          if ((r & st) == 0) {
-            const uint32_t k2 = max(key[r], key[r | st]);
-            key[r] = k2;
-            key[r | st] = k2;
-          }
+        for (int i = 0; i < 4; ++i) q[i] = nearest_code<MODE, M>(d[4 * j + i] * rc, qa, s_lut, s_thr);
+        w[j] = pack_word<8>(q);
       }
+    } else {
 #pragma unroll
-    for (int r = 0; r < KR; ++r) {
-      const float d[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
-      if (b0 + r * 256 < nb) emit(r, key[r], d);
+      for (int j = 0; j < kBPL / 4; ++j) {
+        uint32_t q[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = nearest_code<MODE, M>((d[4 * j + i] * s) * rc, qa, s_lut, s_thr);
+        w[j] = pack_word<8>(q);
+      }
     }
+    if (whole) {
+      *reinterpret_cast<uint4*>(q2 + b0) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else if (b0 < nb) {
+#pragma unroll
+      for (int i = 0; i < kBPL; ++i)
+        if (b0 + i < nb) q2[b0 + i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
+    }
+    cur = next;
   }
 }
 
-template <int MODE, int M>
-hipError_t launch_stats(const float* absmax, int64_t nb, const double* leaves, int64_t stride, int64_t count,
+template <int AS, int MODE, int M>
+hipError_t launch_stats(const void* absmax, int64_t nb, const double* leaves, int64_t stride, int64_t count,
                         float* mean, int log2b2, int64_t ngroups, uint8_t* q2, float* absmax2, const QuantArgs& qa,
                         hipStream_t s) {
-  // runs per wave: a group (B2 / 256 runs) fits in a wave; groups inside a run take 4 runs per
-  // wave (more waves in flight: 2^23 blocks, 245.6 against 249.1 us for the whole nested call)
-  const int kr = log2b2 > 11 ? 16 : (log2b2 > 8 ? 8 : 4);
-  const dim3 grid((unsigned)((nb + kWaves * 256 * kr - 1) / (kWaves * 256 * kr)));
-  if (log2b2 > 11)
-    return launch_kernel(stats_kernel<MODE, M, 16, false>, grid, dim3(kThreads), s, absmax, nb, leaves, stride,
-                         count, mean, log2b2, ngroups, q2, absmax2, qa);
-  if (log2b2 > 8)
-    return launch_kernel(stats_kernel<MODE, M, 8, false>, grid, dim3(kThreads), s, absmax, nb, leaves, stride,
-                         count, mean, log2b2, ngroups, q2, absmax2, qa);
-  return launch_kernel(stats_kernel<MODE, M, 4, true>, grid, dim3(kThreads), s, absmax, nb, leaves, stride, count,
+  const int64_t per = (int64_t)kStatTile * kStatTiles;
+  const dim3 grid((unsigned)((nb + per - 1) / per));
+  return launch_kernel(stats_kernel<AS, MODE, M>, grid, dim3(kStatThreads), s, absmax, nb, leaves, stride, count,
                        mean, log2b2, ngroups, q2, absmax2, qa);
+}
+
+template <int AS>
+hipError_t launch_stats_as(const void* absmax, int64_t nb, const double* leaves, int64_t stride, int64_t count,
+                           float* mean, int log2b2, int64_t ngroups, uint8_t* q2, float* absmax2,
+                           const PreparedTable& t2, hipStream_t s) {
+  const QuantArgs& qa = t2.qa;
+  if (t2.mode == LIN) {
+    if (t2.M <= 1) return launch_stats<AS, LIN, 1>(absmax, nb, leaves, stride, count, mean, log2b2, ngroups, q2, absmax2, qa, s);
+    if (t2.M == 2) return launch_stats<AS, LIN, 2>(absmax, nb, leaves, stride, count, mean, log2b2, ngroups, q2, absmax2, qa, s);
+    return launch_stats<AS, LIN, 3>(absmax, nb, leaves, stride, count, mean, log2b2, ngroups, q2, absmax2, qa, s);
+  }
+  if (t2.mode == LOG) {
+    if (t2.M <= 1) return launch_stats<AS, LOG, 1>(absmax, nb, leaves, stride, count, mean, log2b2, ngroups, q2, absmax2, qa, s);
+    if (t2.M == 2) return launch_stats<AS, LOG, 2>(absmax, nb, leaves, stride, count, mean, log2b2, ngroups, q2, absmax2, qa, s);
+    return launch_stats<AS, LOG, 3>(absmax, nb, leaves, stride, count, mean, log2b2, ngroups, q2, absmax2, qa, s);
+  }
+  return launch_stats<AS, SEARCH, 1>(absmax, nb, leaves, stride, count, mean, log2b2, ngroups, q2, absmax2, qa, s);
 }
 
 }  // namespace
 
-int launch_nested_stats(const float* absmax, int64_t nb, int blocksize2, const PreparedTable& t2,
+int launch_nested_stats(const void* absmax, int dtype, int64_t nb, int blocksize2, const PreparedTable& t2,
                         double* partials, int64_t npart, uint8_t* q2, float* absmax2, float* mean,
                         void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // Above 512 partial sums, runs of 2048 are first summed in place by one wave each (one
+  // Above 512 partial sums, runs of 2048 are first summed in place by one workgroup each (one
   // workgroup reading them all would be bound by a single CU's bandwidth).  Up to 512 leaves
   // remain, the statistics kernel finishes the tree itself; beyond, mean_kernel does.
   hipError_t e;
@@ -299,7 +371,7 @@ int launch_nested_stats(const float* absmax, int64_t nb, int blocksize2, const P
   int64_t stride = 1, count = npart;
   if (npart > kFusedLeaves) {
     const int64_t runs = (npart + kWaveLeaves - 1) / kWaveLeaves;
-    e = launch_kernel(run_sum_kernel, dim3((unsigned)runs), dim3(64), s, leaves, npart);
+    e = launch_kernel(run_sum_kernel, dim3((unsigned)runs), dim3(kRunThreads), s, leaves, npart);
     if (e != hipSuccess) return (int)e;
     stride = kWaveLeaves;
     count = runs;
@@ -312,21 +384,12 @@ int launch_nested_stats(const float* absmax, int64_t nb, int blocksize2, const P
   int log2b2 = 0;
   while ((1 << log2b2) < blocksize2) ++log2b2;
   const int64_t ngroups = (nb + blocksize2 - 1) / blocksize2;
-  const QuantArgs& qa = t2.qa;
-  auto go = [&](auto kernel_launcher) {
-    return kernel_launcher(absmax, nb, leaves, stride, count, mean, log2b2, ngroups, q2, absmax2, qa, s);
-  };
-  if (t2.mode == LIN) {
-    if (t2.M <= 1) e = go(launch_stats<LIN, 1>);
-    else if (t2.M == 2) e = go(launch_stats<LIN, 2>);
-    else e = go(launch_stats<LIN, 3>);
-  } else if (t2.mode == LOG) {
-    if (t2.M <= 1) e = go(launch_stats<LOG, 1>);
-    else if (t2.M == 2) e = go(launch_stats<LOG, 2>);
-    else e = go(launch_stats<LOG, 3>);
-  } else {
-    e = go(launch_stats<SEARCH, 1>);
-  }
+  if (dtype == F32)
+    e = launch_stats_as<AS_F32>(absmax, nb, leaves, stride, count, mean, log2b2, ngroups, q2, absmax2, t2, s);
+  else if (dtype == BF16)
+    e = launch_stats_as<AS_BF16>(absmax, nb, leaves, stride, count, mean, log2b2, ngroups, q2, absmax2, t2, s);
+  else
+    e = launch_stats_as<AS_F16>(absmax, nb, leaves, stride, count, mean, log2b2, ngroups, q2, absmax2, t2, s);
   return (int)e;
 }
 

@@ -112,6 +112,15 @@ __device__ __forceinline__ double read_lane(double x, int l) {
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
+// The block absmax in the input's own 16-bit format (fp16 / bf16 input), from the max key: the
+// maximum of |x| over elements of that format is itself a value of the format, so the 16 bits
+// hold it exactly.  +0 when the block has no finite element.
+template <int DT>
+__device__ __forceinline__ uint32_t key_to_bits16(uint32_t k) {
+  constexpr uint32_t off = DT == BF16 ? 0x0100u : 0x0800u;
+  return k >= off ? (k - off) >> 1 : 0u;
+}
+
 // Block absmax (binary32) from the max key; +0 when the block has no finite element.
 template <int DT>
 __device__ __forceinline__ float key_to_absmax(uint32_t k) {
@@ -234,11 +243,14 @@ struct QuantShared {
   uint32_t red[kThreads / 64];  // B = 4096: the two waves of a block exchange their keys
 };
 
-// Quantizes one lane chunk: block absmax, normalization, codes, packing and stores; with
-// `partials`, also the pairwise sum of the block maxima of this wave's 2048 elements.
-template <int DT, int KB, int MODE, int M>
+// Quantizes one lane chunk: block absmax, normalization, codes, packing and stores.  NESTED
+// (the data pass of a nested quantize) also writes the pairwise sum of the block maxima of this
+// wave's 2048 elements, and stores the block maxima in the input's own format (binary32 for
+// fp32 input, the 16 bits of fp16 / bf16 input, which hold them exactly); otherwise the block
+// maxima are binary32.
+template <int DT, int KB, int MODE, int M, bool NESTED>
 __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, int64_t elem0, int64_t n, int log2g,
-                                               float* __restrict__ absmax, uint8_t* __restrict__ packed,
+                                               void* __restrict__ absmax, uint8_t* __restrict__ packed,
                                                double* __restrict__ partials, const QuantArgs& qa,
                                                const typename Entry<M>::type* s_lut, const float* s_thr,
                                                QuantShared& sh, uint4* stage) {
@@ -265,9 +277,14 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, in
   }
   const float a = key_to_absmax<DT>(key);
   const int64_t blk = elem0 >> (5 + log2g);
-  if ((tid & (G - 1)) == 0 && blk < nb) absmax[blk] = a;
+  if ((tid & (G - 1)) == 0 && blk < nb) {
+    if (NESTED && DT != F32)
+      static_cast<uint16_t*>(absmax)[blk] = (uint16_t)key_to_bits16<DT>(key);
+    else
+      static_cast<float*>(absmax)[blk] = a;
+  }
 
-  if (partials != nullptr) {
+  if constexpr (NESTED) {
     // Pairwise sum of the block maxima of this wave's 2048 elements: an aligned subtree of the
     // nested mean's tree (blocks past n hold +0).  Lane i holds the sum of the subtree that
     // starts at its block; each level adds the right neighbour subtree (lane i + m) to the left
@@ -374,9 +391,9 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, in
 }
 
 // A workgroup quantizes one tile of 8192 elements, tile blockIdx.x.
-template <int DT, int KB, int MODE, int M>
+template <int DT, int KB, int MODE, int M, bool NESTED>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __restrict__ in, int64_t n, int log2g,
-                                                            float* __restrict__ absmax,
+                                                            void* __restrict__ absmax,
                                                             uint8_t* __restrict__ packed,
                                                             double* __restrict__ partials, QuantArgs qa) {
   using Tr = Traits<DT>;
@@ -412,8 +429,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __res
       load_chunk_full<DT>(in, elem0, w);
       lut_fill<MODE, M, kThreads>(qa, lw, s_lut, s_thr, tid);
     }
-    quantize_chunk<DT, KB, MODE, M>(w, kEPT, elem0, n, log2g, absmax, packed, partials, qa, s_lut, s_thr, sh,
-                                    stage);
+    quantize_chunk<DT, KB, MODE, M, NESTED>(w, kEPT, elem0, n, log2g, absmax, packed, partials, qa, s_lut, s_thr,
+                                            sh, stage);
   } else {
     const auto lw = lut_fetch<MODE, M, kThreads>(qa, tid);
     const int64_t wave0 = elem0 - (int64_t)(tid & 63) * kEPT;
@@ -425,20 +442,24 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __res
       nvalid = load_chunk<DT>(in, n, elem0, w);
     }
     lut_fill<MODE, M, kThreads>(qa, lw, s_lut, s_thr, tid);
-    quantize_chunk<DT, KB, MODE, M>(w, nvalid, elem0, n, log2g, absmax, packed, partials, qa, s_lut, s_thr, sh,
-                                    stage);
+    quantize_chunk<DT, KB, MODE, M, NESTED>(w, nvalid, elem0, n, log2g, absmax, packed, partials, qa, s_lut, s_thr,
+                                            sh, stage);
   }
 }
 
 template <int DT, int KB, int MODE, int M>
-hipError_t launch4(const void* in, int64_t n, int log2g, float* absmax, uint8_t* packed, double* partials,
+hipError_t launch4(const void* in, int64_t n, int log2g, void* absmax, uint8_t* packed, double* partials,
                    const QuantArgs& qa, hipStream_t stream) {
-  return launch_kernel(quantize_kernel<DT, KB, MODE, M>, dim3((unsigned)quantize_grid(n)), dim3(kThreads), stream,
+  const dim3 grid((unsigned)quantize_grid(n));
+  if (partials != nullptr)
+    return launch_kernel(quantize_kernel<DT, KB, MODE, M, true>, grid, dim3(kThreads), stream,
+                         static_cast<const uint8_t*>(in), n, log2g, absmax, packed, partials, qa);
+  return launch_kernel(quantize_kernel<DT, KB, MODE, M, false>, grid, dim3(kThreads), stream,
                        static_cast<const uint8_t*>(in), n, log2g, absmax, packed, partials, qa);
 }
 
 template <int DT, int KB>
-hipError_t launch_mode(const void* in, int64_t n, int log2g, float* absmax, uint8_t* packed,
+hipError_t launch_mode(const void* in, int64_t n, int log2g, void* absmax, uint8_t* packed,
                        double* partials, const PreparedTable& t, hipStream_t s) {
   if (t.mode == LIN) {
     if (t.M <= 1) return launch4<DT, KB, LIN, 1>(in, n, log2g, absmax, packed, partials, t.qa, s);
@@ -454,7 +475,7 @@ hipError_t launch_mode(const void* in, int64_t n, int log2g, float* absmax, uint
 }
 
 template <int DT>
-hipError_t launch_dt(const void* in, int64_t n, int log2g, float* absmax, uint8_t* packed,
+hipError_t launch_dt(const void* in, int64_t n, int log2g, void* absmax, uint8_t* packed,
                      double* partials, const PreparedTable& t, hipStream_t s) {
   return t.K == 16 ? launch_mode<DT, 4>(in, n, log2g, absmax, packed, partials, t, s)
                    : launch_mode<DT, 8>(in, n, log2g, absmax, packed, partials, t, s);
@@ -469,7 +490,7 @@ int64_t quantize_partials(int64_t n, int blocksize) {
   return blocksize == 4096 ? waves / 2 : waves;
 }
 
-int launch_quantize(const void* in, int dtype, int64_t n, int blocksize, const PreparedTable& t, float* absmax,
+int launch_quantize(const void* in, int dtype, int64_t n, int blocksize, const PreparedTable& t, void* absmax,
                     uint8_t* packed, double* partials, void* stream) {
   int log2g = 0;
   while ((kEPT << log2g) < blocksize) ++log2g;

@@ -105,7 +105,7 @@ bq_status bq_dequantize_blockwise(void* out, bq_dtype dtype, int64_t n, int32_t 
  *              `blocksize2` blocks by the same absmax / normalize / nearest rules;
  *   rebuilt  a'_b = fl32(fl32(c2[q2_b] * absmax2_g) + mean), used by the nested dequantize. */
 typedef struct {
-  uint8_t* qabsmax;            /* [device] nb codes q2_b (nb = ceil(n / blocksize)), 4-byte aligned */
+  uint8_t* qabsmax;            /* [device] nb codes q2_b (nb = ceil(n / blocksize)), 16-byte aligned */
   float* absmax2;              /* [device] ceil(nb / blocksize2) binary32 group maxima */
   float* mean;                 /* [device] 1 binary32 value */
   const bq_code_table* table;  /* [host] 256-entry statistics table */
@@ -114,14 +114,17 @@ typedef struct {
   size_t workspace_bytes;
 } bq_nested_stats;
 
-/* Bytes of device workspace bq_quantize_nested needs (0 for n <= 0).  After the call's
- * stream work completes, the first ceil(n / blocksize) * 4 bytes of the workspace hold the
- * binary32 block maxima a_b. */
+/* Bytes of device workspace bq_quantize_nested needs (0 for n <= 0), for any dtype.  After the
+ * call's stream work completes, the workspace starts with the nb = ceil(n / blocksize) block
+ * maxima a_b: nb binary32 values for BQ_F32 input; for BQ_F16 / BQ_BF16 input, nb 16-bit
+ * values of that type (the maximum of |x| over values of a format is itself a value of the
+ * format, so they are exact). */
 size_t bq_nested_workspace_bytes(int64_t n, int32_t blocksize, int32_t blocksize2);
 
 /* Blockwise quantization with nested statistics: packed data codes as bq_quantize_blockwise,
  * and the statistics of bq_nested_stats written to stats->qabsmax, ->absmax2 and ->mean.
- * Enqueues four kernels (data, partial sums, mean, statistics) on `stream`. */
+ * Enqueues up to four kernels on `stream`: the data pass, the partial-sum runs (inputs of more
+ * than 2^20 elements), the mean (more than 2^31 elements), then the statistics. */
 bq_status bq_quantize_nested(const void* in, bq_dtype dtype, int64_t n, int32_t blocksize,
                              const bq_code_table* code_table, bq_nested_stats* stats,
                              uint8_t* packed, hipStream_t stream);

@@ -1,7 +1,7 @@
 /*
  * bq_debug.h -- test and measurement hooks of libbq.  bq_debug_nearest_codes makes no HIP call
- * and works without a GPU; bq_debug_time_next_data_kernel only arms events that a later call
- * records.
+ * and works without a GPU; bq_debug_time_next_kernel only arms events that a later call
+ * fills.
  */
 #ifndef BQ_DEBUG_H
 #define BQ_DEBUG_H
@@ -27,14 +27,17 @@ extern "C" {
 bq_status bq_debug_nearest_codes(const bq_code_table* table, const float* y, int64_t count,
                                  int32_t* codes, int32_t* mode, int32_t* compares);
 
-/* Measurement hook: the next bq_quantize_nested call made on the calling thread records
- * `start` on its stream right before it enqueues its data kernel (the blockwise quantize of
- * the data, which also writes the workspace) and `stop` right after, then forgets both, so
- * that hipEventElapsedTime(start, stop) is that kernel's own duration as the call launches
- * it.  The events are the caller's (created with timing enabled) and must stay valid until
- * that call returns; a failed hipEventRecord makes that call return BQ_ERR_HIP.  Passing two
- * NULLs disarms the hook.  Returns BQ_OK, or BQ_ERR_NULL when exactly one event is NULL. */
-bq_status bq_debug_time_next_data_kernel(hipEvent_t start, hipEvent_t stop);
+/* Measurement hook: the next kernel the library launches on the calling thread goes through
+ * hipExtLaunchKernel, which stamps that kernel's own start and end times into `start` and
+ * `stop`; then the hook forgets both.  The next call's first kernel is the one timed: the data
+ * kernel of a nested quantize (bq_quantize_nested or bq_quantize_nested_noalloc; the blockwise
+ * quantize of the data, which also writes the workspace), or the only kernel of the other
+ * calls.  hipEventElapsedTime(start, stop) is then that kernel's duration as the call launches
+ * it, with no marker packets between the call's kernels.  The events are the caller's
+ * (created with timing enabled) and must stay valid until the work completes.  A call that
+ * fails validation launches nothing and leaves the hook armed.  Passing two NULLs disarms it.
+ * Returns BQ_OK, or BQ_ERR_NULL when exactly one event is NULL. */
+bq_status bq_debug_time_next_kernel(hipEvent_t start, hipEvent_t stop);
 
 #ifdef __cplusplus
 }

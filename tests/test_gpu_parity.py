@@ -246,8 +246,16 @@ def gpu_nested(x: torch.Tensor, dtype: str, B: int, t16, t256, B2=256, out_dtype
     bq.check(bq.bq_quantize_nested(x, BQ_DT[dtype], n, B, t16, stats, packed), "quantize_nested")
     out = torch.empty(max(n, 8), dtype=TORCH_DT[out_dtype or dtype], device=dev)
     bq.check(bq.bq_dequantize_nested(out, BQ_DT[out_dtype or dtype], n, B, t16, stats, packed), "dequantize_nested")
-    absmax = ws[:nb * 4].view(torch.float32)
-    return dict(absmax=absmax, q2=q2[:nb], absmax2=absmax2[:ng], mean=mean[0], packed=packed, out=out)
+    return dict(absmax=workspace_absmax(ws, nb, dtype), q2=q2[:nb], absmax2=absmax2[:ng], mean=mean[0],
+                packed=packed, out=out)
+
+
+def workspace_absmax(ws: torch.Tensor, nb: int, dtype: str) -> torch.Tensor:
+    """The block maxima the nested quantize leaves at the start of its workspace, widened to
+    binary32: stored as binary32 for fp32 input and as the input's 16-bit type otherwise."""
+    if dtype == "float32":
+        return ws[:nb * 4].view(torch.float32)
+    return ws[:nb * 2].view(TORCH_DT[dtype]).float()
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -514,17 +522,17 @@ def test_negative_zero_table_entry(dev, o):
 
 
 def test_data_kernel_timing_hook(dev, o):
-    """Events armed with bq_debug_time_next_data_kernel bracket the data kernel of the next
-    nested quantize only (a positive elapsed time, shorter than the whole call), are forgotten
-    after it, and leave the outputs unchanged."""
+    """Events armed with bq_debug_time_next_kernel take the start and end of the data kernel of
+    the next nested quantize only (a positive elapsed time, shorter than the whole call), are
+    forgotten after it, and leave the outputs unchanged."""
     n, B = 1 << 22, 64
     t16, t256 = synth.table16(), synth.table256()
     x = synth.blockwise_input(n, "bfloat16", 17, std=0.02, device=dev)
     r0 = gpu_nested(x, "bfloat16", B, t16, t256)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    assert bq.bq_debug_time_next_data_kernel(e0, None) == bq.BQ_ERR_NULL
-    bq.check(bq.bq_debug_time_next_data_kernel(e0, e1))
+    assert bq.bq_debug_time_next_kernel(e0, None) == bq.BQ_ERR_NULL
+    bq.check(bq.bq_debug_time_next_kernel(e0, e1))
     c0.record()
     r1 = gpu_nested(x, "bfloat16", B, t16, t256)
     c1.record()
