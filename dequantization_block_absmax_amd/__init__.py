@@ -24,7 +24,7 @@ BQ_Q32_Q4, BQ_Q32_Q8 = 0, 1
 EXPORTS = ("bq_quantize_blockwise", "bq_dequantize_blockwise", "bq_quantize_nested",
            "bq_dequantize_nested", "bq_dequant_q32", "bq_nested_workspace_bytes", "bq_status_string",
            "bq_debug_nearest_codes", "bq_last_hip_error", "bq_linear_blockwise", "bq_gemm_blockwise",
-           "bq_debug_time_next_kernel")
+           "bq_debug_time_next_kernel", "bq_quantize_nested_noalloc")
 
 
 class BQError(RuntimeError):
@@ -64,6 +64,7 @@ def _load() -> ctypes.CDLL:
         "bq_quantize_blockwise": [vp, st, i64, i32, tp, vp, vp, vp],
         "bq_dequantize_blockwise": [vp, st, i64, i32, tp, vp, vp, vp],
         "bq_quantize_nested": [vp, st, i64, i32, tp, sp, vp, vp],
+        "bq_quantize_nested_noalloc": [vp, st, i64, i32, tp, sp, vp, vp],
         "bq_dequantize_nested": [vp, st, i64, i32, tp, sp, vp, vp],
         "bq_dequant_q32": [vp, st, i64, i32, st, vp, vp],
         "bq_linear_blockwise": [vp, st, i64, i64, i64, i32, tp, vp, vp, vp, vp],
@@ -170,6 +171,13 @@ def bq_quantize_nested(inp, dtype, n: int, blocksize: int, table, stats: bq_nest
     return _lib.bq_quantize_nested(_addr(inp), dtype_code(dtype), int(n), int(blocksize), _table_ptr(table),
                                    ctypes.pointer(stats) if stats is not None else None, _addr(packed),
                                    _stream(stream))
+
+
+def bq_quantize_nested_noalloc(inp, dtype, n: int, blocksize: int, table, stats: bq_nested_stats | None, packed,
+                               stream=None) -> int:
+    return _lib.bq_quantize_nested_noalloc(_addr(inp), dtype_code(dtype), int(n), int(blocksize), _table_ptr(table),
+                                           ctypes.pointer(stats) if stats is not None else None, _addr(packed),
+                                           _stream(stream))
 
 
 def bq_dequantize_nested(out, dtype, n: int, blocksize: int, table, stats: bq_nested_stats | None, packed,

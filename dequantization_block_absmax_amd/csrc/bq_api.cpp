@@ -283,6 +283,19 @@ bq_status bq_quantize_nested(const void* in, bq_dtype dtype, int64_t n, int32_t 
   return launch_quantize_nested(in, dtype, n, blocksize, t, stats, packed, stats->workspace, stream);
 }
 
+bq_status bq_quantize_nested_noalloc(const void* in, bq_dtype dtype, int64_t n, int32_t blocksize,
+                                     const bq_code_table* code_table, bq_nested_stats* stats,
+                                     uint8_t* packed, hipStream_t stream) {
+  Tables t;
+  const bq_status st = check_quantize_nested(in, dtype, n, blocksize, code_table, stats, packed, false, &t);
+  if (st != BQ_OK || n == 0) return st;
+  if (ws_bytes(n, nblocks(n, blocksize)) > bq::kScratchBytes) return BQ_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  const int e = bq::scratch_buffer(&scratch);
+  if (e != 0) return hip_status(e);
+  return launch_quantize_nested(in, dtype, n, blocksize, t, stats, packed, scratch, stream);
+}
+
 bq_status bq_dequantize_nested(void* out, bq_dtype dtype, int64_t n, int32_t blocksize,
                                const bq_code_table* code_table, const bq_nested_stats* stats,
                                const uint8_t* packed, hipStream_t stream) {

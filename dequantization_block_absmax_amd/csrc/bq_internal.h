@@ -141,4 +141,10 @@ int launch_dequantize_nested(void* out, int dtype, int64_t n, int blocksize, int
                              const NestedDequantArgs& a, const uint8_t* q2, const float* absmax2,
                              const float* mean, const uint8_t* packed, void* stream);
 int launch_q32(const void* blocks, int dtype, int64_t n, int fmt, void* out, void* stream);
+
+// The library-owned scratch of bq_quantize_nested_noalloc (k_scratch.hip): kScratchBytes per
+// device, 256-byte aligned.  scratch_buffer sets *ptr to the current device's copy (its device
+// address, looked up once per device) and returns 0, or a hipError_t.
+constexpr size_t kScratchBytes = (size_t)36 << 20;
+int scratch_buffer(void** ptr);
 }  // namespace bq

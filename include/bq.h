@@ -129,6 +129,20 @@ bq_status bq_quantize_nested(const void* in, bq_dtype dtype, int64_t n, int32_t 
                              const bq_code_table* code_table, bq_nested_stats* stats,
                              uint8_t* packed, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): bq_quantize_nested with the library's own scratch
+ * memory in place of the caller's workspace.  stats->workspace and stats->workspace_bytes are
+ * ignored; everything else, the outputs and the errors are those of bq_quantize_nested.
+ * The scratch is a fixed 36 MiB array per GPU (37,748,736 bytes, held by every GPU the library
+ * runs on until the process ends), enough for any input whose bq_nested_workspace_bytes is at
+ * most that size, e.g. 2^29 elements at block size 64; a larger input returns
+ * BQ_ERR_WORKSPACE before anything is enqueued.  The call allocates nothing.  All calls on one
+ * GPU share its scratch, which keeps the last call's contents: calls that overlap on one GPU
+ * (two streams or host threads without ordering between them) race and give wrong results. */
+bq_status bq_quantize_nested_noalloc(const void* in, bq_dtype dtype, int64_t n, int32_t blocksize,
+                                     const bq_code_table* code_table, bq_nested_stats* stats,
+                                     uint8_t* packed, hipStream_t stream);
+
 /* Dequantization from nested statistics: rebuilds each a'_b from (q2_b, absmax2_g, mean) and
  * dequantizes with it, in one kernel.  stats->workspace is not used. */
 bq_status bq_dequantize_nested(void* out, bq_dtype dtype, int64_t n, int32_t blocksize,

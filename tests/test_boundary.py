@@ -143,6 +143,30 @@ def test_nested_validation():
         == bq.BQ_ERR_ALIGNMENT
 
 
+def test_noalloc_validation():
+    """The allocation-free nested quantize validates like bq_quantize_nested, needs no
+    workspace, and refuses inputs whose workspace would exceed its 36 MiB scratch before any
+    HIP call."""
+    def call(stats=None, **kw):
+        args = dict(inp=FAKE, dtype=bq.BQ_BF16, n=1000, blocksize=64, table=T16,
+                    stats=nstats(workspace=None, workspace_bytes=0) if stats is None else stats, packed=FAKE,
+                    stream=0)
+        args.update(kw)
+        return bq.bq_quantize_nested_noalloc(**args)
+
+    assert call(n=0) == bq.BQ_OK
+    assert call(dtype=9) == bq.BQ_ERR_DTYPE
+    assert call(blocksize=65) == bq.BQ_ERR_BLOCKSIZE
+    assert call(stats=nstats(table=T16)) == bq.BQ_ERR_TABLE
+    assert call(stats=nstats(qabsmax=FAKE + 4)) == bq.BQ_ERR_ALIGNMENT
+    assert call(inp=None) == bq.BQ_ERR_NULL
+    limit = 36 << 20
+    fits = 1 << 29  # 2^29 elements at block size 64: the largest power of two that fits
+    assert bq.bq_nested_workspace_bytes(fits, 64) <= limit < bq.bq_nested_workspace_bytes(2 * fits, 64)
+    assert call(n=2 * fits) == bq.BQ_ERR_WORKSPACE
+    assert call(n=(1 << 33), blocksize=4096) == bq.BQ_ERR_WORKSPACE
+
+
 def test_workspace_bytes():
     assert bq.bq_nested_workspace_bytes(0, 64, 256) == 0
     for n, B in ((2**29, 64), (1000, 32), (8192 * 3 + 1, 4096)):
