@@ -44,13 +44,12 @@ bq_status hip_status(int e) {
 int64_t nblocks(int64_t n, int32_t b) { return (n + b - 1) / b; }
 
 // Nested workspace: the block maxima (binary32 absmax[nb] for fp32 input, the 16-bit patterns
-// for fp16 / bf16 input, in the same region), then the binary64 partial sums of the quantize
-// launch (one per 2048-element wave).
-size_t ws_partials_offset(int64_t nb) { return ((size_t)nb * 4 + 255) & ~(size_t)255; }
+// for fp16 / bf16 input, in the same region), padded to 256 bytes, then one binary64 run sum
+// of the mean's tree per kRunBlocks blocks.
+size_t ws_runs_offset(int64_t nb) { return ((size_t)nb * 4 + 255) & ~(size_t)255; }
 
-// absmax[nb] (fp32), padded to 256 bytes, then the quantize launch's partial sums (fp64).
-size_t ws_bytes(int64_t n, int64_t nb) {
-  return ws_partials_offset(nb) + (size_t)bq::quantize_partials(n, 32) * 8;
+size_t ws_bytes(int64_t nb) {
+  return ws_runs_offset(nb) + (size_t)((nb + bq::kRunBlocks - 1) / bq::kRunBlocks) * 8;
 }
 
 // Preparing a table (validation, thresholds, bucket LUT) costs more host time than a small
@@ -147,8 +146,7 @@ bq_status bq_quantize_blockwise(const void* in, bq_dtype dtype, int64_t n, int32
   if (in == nullptr || absmax == nullptr || packed == nullptr) return BQ_ERR_NULL;
   if (nblocks(n, blocksize) > INT32_MAX) return BQ_ERR_SIZE;
   if (!aligned(in, 16) || !aligned(packed, 16) || !aligned(absmax, 4)) return BQ_ERR_ALIGNMENT;
-  return hip_status(bq::launch_quantize(in, dtype, n, blocksize, t.data, absmax, packed, nullptr,
-                                        stream));
+  return hip_status(bq::launch_quantize(in, dtype, n, blocksize, t.data, absmax, packed, false, stream));
 }
 
 bq_status bq_dequantize_blockwise(void* out, bq_dtype dtype, int64_t n, int32_t blocksize,
@@ -220,7 +218,7 @@ bq_status bq_gemm_blockwise(const void* x, bq_dtype dtype, int64_t M, int64_t K,
 size_t bq_nested_workspace_bytes(int64_t n, int32_t blocksize, int32_t blocksize2) {
   (void)blocksize2;
   if (n <= 0 || !valid_blocksize(blocksize)) return 0;
-  return ws_bytes(n, nblocks(n, blocksize));
+  return ws_bytes(nblocks(n, blocksize));
 }
 
 static bq_status check_nested(const bq_nested_stats* stats, bq::PreparedTable* t2, bool need_ws,
@@ -236,7 +234,7 @@ static bq_status check_nested(const bq_nested_stats* stats, bq::PreparedTable* t
   if (need_ws) {
     if (stats->workspace == nullptr) return BQ_ERR_WORKSPACE;
     if (!aligned(stats->workspace, 256)) return BQ_ERR_ALIGNMENT;
-    if (stats->workspace_bytes < ws_bytes(n, nblocks(n, blocksize))) return BQ_ERR_WORKSPACE;
+    if (stats->workspace_bytes < ws_bytes(nblocks(n, blocksize))) return BQ_ERR_WORKSPACE;
   }
   return BQ_OK;
 }
@@ -265,12 +263,11 @@ static bq_status launch_quantize_nested(const void* in, bq_dtype dtype, int64_t 
                                         hipStream_t stream) {
   const int64_t nb = nblocks(n, blocksize);
   void* ws_absmax = ws;
-  double* ws_partials = reinterpret_cast<double*>(static_cast<uint8_t*>(ws) + ws_partials_offset(nb));
-  int e = bq::launch_quantize(in, dtype, n, blocksize, t.data, ws_absmax, packed, ws_partials, stream);
+  double* ws_runs = reinterpret_cast<double*>(static_cast<uint8_t*>(ws) + ws_runs_offset(nb));
+  int e = bq::launch_quantize(in, dtype, n, blocksize, t.data, ws_absmax, packed, true, stream);
   if (e != 0) return hip_status(e);
-  e = bq::launch_nested_stats(ws_absmax, dtype, nb, stats->blocksize2, t.stats, ws_partials,
-                              bq::quantize_partials(n, blocksize),
-                              stats->qabsmax, stats->absmax2, stats->mean, stream);
+  e = bq::launch_nested_stats(ws_absmax, dtype, nb, stats->blocksize2, t.stats, ws_runs, stats->qabsmax,
+                              stats->absmax2, stats->mean, stream);
   return hip_status(e);
 }
 
@@ -289,7 +286,7 @@ bq_status bq_quantize_nested_noalloc(const void* in, bq_dtype dtype, int64_t n, 
   Tables t;
   const bq_status st = check_quantize_nested(in, dtype, n, blocksize, code_table, stats, packed, false, &t);
   if (st != BQ_OK || n == 0) return st;
-  if (ws_bytes(n, nblocks(n, blocksize)) > bq::kScratchBytes) return BQ_ERR_WORKSPACE;
+  if (ws_bytes(nblocks(n, blocksize)) > bq::kScratchBytes) return BQ_ERR_WORKSPACE;
   void* scratch = nullptr;
   const int e = bq::scratch_buffer(&scratch);
   if (e != 0) return hip_status(e);

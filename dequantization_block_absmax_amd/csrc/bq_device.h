@@ -20,7 +20,8 @@ struct LutLayout {
   static constexpr int kSize = MODE == LIN ? kLinLutMax : (MODE == LOG ? kLutMax : 1);
 };
 
-// Nearest code of y (see bq_internal.h for the bucket functions).
+// Nearest code of y (see bq_internal.h for the bucket functions).  y must be in [-1, 1] for
+// LIN; LOG and SEARCH also take a non-finite y, which gives z.
 template <int MODE, int M>
 __device__ __forceinline__ uint32_t nearest_code(float y, const QuantArgs& qa,
                                                  const typename Entry<M>::type* lut,
@@ -33,9 +34,12 @@ __device__ __forceinline__ uint32_t nearest_code(float y, const QuantArgs& qa,
   } else {
     typename Entry<M>::type e;
     if constexpr (MODE == LIN) {
-      float zz = __builtin_fmaf(y, kLinAlpha, kLinBeta);
-      zz = fminf(fmaxf(zz, 0.0f), 1.0f);
-      e = lut[__builtin_amdgcn_ubfe(f32_bits(zz), (uint32_t)qa.sh, (uint32_t)(24 - qa.sh))];
+      // zz is the integer 2^23 + bucket, so its bits give the entry's byte offset in one
+      // shift-and-add (lin_off removes the bits of 2^23).
+      constexpr int kLog2E = M == 1 ? 3 : 4;
+      const float zz = __builtin_fmaf(y, qa.lin_scale, qa.lin_bias);
+      const uint32_t off = (f32_bits(zz) << kLog2E) + qa.lin_off;
+      e = *reinterpret_cast<const typename Entry<M>::type*>(reinterpret_cast<const char*>(lut) + off);
     } else {
       // Byte offset of the entry, in five operations: LO and HI are multiples of 2^SH, so
       // clamping |y| bits >> SH to [LO >> SH, HI >> SH] gives j + (LO >> SH); the sign picks the
@@ -145,13 +149,15 @@ __device__ __forceinline__ void lut_fill(const QuantArgs& qa, const LutWords<MOD
     if (tid + k * NT < 260) s_thr[tid + k * NT] = l.th[k];
   __syncthreads();
   if constexpr (MODE != SEARCH) {
-    // All kSize entries are written (those past nbuckets from the zero bases are never read),
-    // so the threshold reads and entry writes form one batch instead of a chain of branches.
+    // Rounds of NT entries: a round that starts past nbuckets is skipped (a uniform test);
+    // inside a round every entry is written (those past nbuckets from the zero bases are never
+    // read), so the threshold reads and entry writes form one batch instead of a chain of
+    // branches.
     constexpr int kSize = LutLayout<MODE, M>::kSize;
 #pragma unroll
     for (int k = 0; k < L::kLutIt; ++k) {
       const int i = tid + k * NT;
-      if ((k + 1) * NT <= kSize || i < kSize) {
+      if (k * NT < qa.nbuckets && ((k + 1) * NT <= kSize || i < kSize)) {
         const uint32_t b = l.bs[k];  // <= 255, so b + 2 stays inside the 260 thresholds
         E e;
         e.x = b;
@@ -169,8 +175,8 @@ __device__ __forceinline__ void lut_fill(const QuantArgs& qa, const LutWords<MOD
     sp.x = (uint32_t)qa.z;
     sp.y = 0x7fc00000u;
     if constexpr (M >= 2) sp.z = sp.w = 0x7fc00000u;
-    if (tid == (qa.special0 & (NT - 1))) s_lut[qa.special0] = sp;
-    if (tid == (qa.special1 & (NT - 1))) s_lut[qa.special1] = sp;
+    if (qa.special0 >= 0 && tid == (qa.special0 & (NT - 1))) s_lut[qa.special0] = sp;
+    if (qa.special1 >= 0 && tid == (qa.special1 & (NT - 1))) s_lut[qa.special1] = sp;
     __syncthreads();
   }
 }

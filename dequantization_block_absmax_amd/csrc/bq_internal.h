@@ -18,11 +18,13 @@ namespace bq {
 
 enum Dtype : int { F32 = 0, F16 = 1, BF16 = 2 };
 
-// Bucket functions (MODE):
-//   LIN:    zz = clamp(fma(y, 31/128, 3/4), 0, 1);  idx = bits(zz)[23:SH]
-//           Finite y in [-1, 1] gives zz in [0.5078125, 0.9921875], so idx in (0, H) with
-//           H = 2^(23-SH); NaN and -inf clamp to 0 (idx 0), +inf to 1.0 (idx H).  Uniform
-//           buckets in y: right for tables of roughly even spacing.
+// Bucket functions (MODE), for y in [-1, 1] (the kernels bring a non-finite element, or the
+// elements of a zero block, to y = 0, whose code is z):
+//   LIN:    zz = fma(y, H/2, 2^23 + H/2), rounded to nearest, is an integer in [2^23, 2^23 + H]
+//           (the binary32 values of [2^23, 2^24) are the integers), so bits(zz) = 0x4B000000 +
+//           idx with idx in [0, H]: H + 1 uniform buckets of width 2/H in y, and the entry's
+//           byte offset is one shift-and-add of bits(zz).  Right for tables of roughly even
+//           spacing.
 //   LOG:    a = bits(y) & 0x7fffffff;  j = (min(max(a, LO), HI) - LO) >> SH;
 //           idx = j + (sign(y) ? NJ : 0).  2^(23-SH) buckets per octave of |y| between
 //           2^-E and 1; j = NJ-1 (a >= HI) only for non-finite y.  Right for tables that
@@ -30,10 +32,9 @@ enum Dtype : int { F32 = 0, F16 = 1, BF16 = 2 };
 //   SEARCH: no buckets; branchless binary search over T (any valid table).
 enum Mode : int { LIN = 0, LOG = 1, SEARCH = 2 };
 
-constexpr float kLinAlpha = 0.2421875f;  // 31/128
-constexpr float kLinBeta = 0.75f;
 constexpr int kLutMax = 2100;            // LUT entries carried in the kernel arguments
-constexpr int kLinLutMax = 513;          // uniform buckets: H <= 512, plus the +inf bucket
+constexpr int kLinLutMax = 513;          // uniform buckets: H <= 512, so at most 513 entries
+constexpr uint32_t kLinBits = 0x4B000000u;  // bits of 2^23
 
 struct QuantArgs {
   // Table-derived data (built on the host per call, passed by value).
@@ -44,7 +45,9 @@ struct QuantArgs {
   int32_t z;                // code of 0.0
   int32_t K;
   // Bucket parameters.
-  int32_t sh;               // LIN and LOG shift
+  float lin_scale, lin_bias;  // LIN: H / 2 and 2^23 + H / 2
+  uint32_t lin_off;         // LIN: LUT byte offset = (bits(zz) << log2 of the entry size) + lin_off
+  int32_t sh;               // LOG shift
   uint32_t lo, hi;          // LOG clamp bounds (bit patterns of |y|)
   int32_t nj;               // LOG buckets per sign
   // LOG, as the kernels evaluate it: LUT byte offset = (clamp(|y| bits >> SH, jlo, jhi) << log2
@@ -119,24 +122,24 @@ int launch_linear(const void* x, int dtype, int64_t M, int64_t K, int64_t N, int
 int launch_gemm(const void* x, int dtype, int64_t M, int64_t K, int64_t N, int blocksize, const DequantArgs& da,
                 const float* absmax, const uint8_t* packed, float* y, void* stream);
 
-// With partials == nullptr: binary32 block maxima into absmax.  Otherwise (the data pass of a
-// nested quantize) also the per-wave partial sums, and the block maxima in the input's own
-// format (binary32 for fp32 input, the 16-bit pattern for fp16 / bf16 input).
+// Quantize kernel launch.  nested == false: binary32 block maxima into absmax.  nested == true
+// (the data pass of a nested quantize): the block maxima in the input's own format (binary32
+// for fp32 input, the 16-bit pattern for fp16 / bf16 input).
 int launch_quantize(const void* in, int dtype, int64_t n, int blocksize, const PreparedTable& t,
-                    void* absmax, uint8_t* packed, double* partials, void* stream);
+                    void* absmax, uint8_t* packed, bool nested, void* stream);
 // Workgroups of a quantize launch over n elements.
 int quantize_grid(int64_t n);
-// Partial sums a quantize launch writes: one per wave of 2048 elements (one per pair of waves
-// for B = 4096, whose blocks span two waves), including waves past n, which write +0.
-int64_t quantize_partials(int64_t n, int blocksize);
 constexpr int64_t kQuantTileElems = 8192;  // elements per quantize tile
+// Blocks per run of the nested mean's first level: each run is an aligned subtree of the
+// pairwise tree, summed by one workgroup into one binary64 run sum.
+constexpr int64_t kRunBlocks = 16384;
 int launch_dequantize(void* out, int dtype, int64_t n, int blocksize, const DequantArgs& a,
                       const float* absmax, const uint8_t* packed, void* stream);
 // absmax: the block maxima as the nested data pass stores them for `dtype` (binary32 for fp32
-// input, the 16-bit pattern for fp16 / bf16 input).
+// input, the 16-bit pattern for fp16 / bf16 input); runs: ceil(nb / kRunBlocks) binary64 run
+// sums (workspace).
 int launch_nested_stats(const void* absmax, int dtype, int64_t nb, int blocksize2, const PreparedTable& t2,
-                        double* partials, int64_t npart, uint8_t* q2, float* absmax2, float* mean,
-                        void* stream);
+                        double* runs, uint8_t* q2, float* absmax2, float* mean, void* stream);
 int launch_dequantize_nested(void* out, int dtype, int64_t n, int blocksize, int blocksize2,
                              const NestedDequantArgs& a, const uint8_t* q2, const float* absmax2,
                              const float* mean, const uint8_t* packed, void* stream);

@@ -27,10 +27,11 @@ int count_le(const std::vector<float>& thr, float y) {
   return (int)(std::upper_bound(thr.begin(), thr.end(), y) - thr.begin());
 }
 
-uint32_t lin_bucket(float y, int sh) {
-  float zz = fmaf(y, kLinAlpha, kLinBeta);  // correctly rounded, as v_fma_f32
-  zz = fminf(fmaxf(zz, 0.0f), 1.0f);
-  return (f32_bits(zz) >> sh) & ((1u << (24 - sh)) - 1u);
+// LIN bucket of y in [-1, 1] with H buckets of width 2/H: fma(y, H/2, 2^23 + H/2) rounded to
+// nearest (correctly rounded, as v_fma_f32) is the integer 2^23 + idx.
+uint32_t lin_bucket(float y, int H) {
+  const float zz = fmaf(y, 0.5f * (float)H, 8388608.0f + 0.5f * (float)H);
+  return f32_bits(zz) - kLinBits;
 }
 
 struct LogParams {
@@ -111,17 +112,18 @@ bool prepare_table(const float* entries, int size, PreparedTable* out) {
   best.M = 0;
   int best_cost = 4 * (size == 16 ? 4 : 8) + 2;
 
-  for (int sh : {15, 14}) {
-    int H = 1 << (23 - sh);
+  // Uniform buckets, the fewest that keep the compares per element lowest (a smaller LUT is
+  // cheaper to build in every workgroup).  Thresholds lie in (-1, 1], in buckets 0..H.
+  for (int H : {64, 128, 256, 512}) {
     if (H + 1 > kLinLutMax) continue;
     std::vector<int> ranks(size - 1);
-    for (int k = 0; k + 1 < size; ++k) ranks[k] = (int)lin_bucket(thr[k], sh);
+    for (int k = 0; k + 1 < size; ++k) ranks[k] = (int)lin_bucket(thr[k], H);
     Choice ch;
     ch.mode = LIN;
-    ch.sh = sh;
+    ch.sh = H;
     ch.nidx = H + 1;
-    ch.M = fill_lut(ranks, H + 1, H + 1, [](int idx) { return idx; }, 0, H, qa.z, ch.base);
-    int cost = 3 + 2 * ch.M;
+    ch.M = fill_lut(ranks, H + 1, H + 1, [](int idx) { return idx; }, -1, -1, qa.z, ch.base);
+    int cost = 2 + 2 * ch.M;
     if (ch.M <= 3 && cost < best_cost) { best = ch; best_cost = cost; }
   }
   for (auto se : {std::pair<int, int>{17, 16}, std::pair<int, int>{18, 16}, std::pair<int, int>{18, 24},
@@ -146,11 +148,13 @@ bool prepare_table(const float* entries, int size, PreparedTable* out) {
   out->mode = best.mode;
   out->M = best.M;
   if (best.mode == LIN) {
-    int H = 1 << (23 - best.sh);
-    qa.sh = best.sh;
+    const int H = best.sh;
+    const int e = best.M <= 1 ? 3 : 4;  // log2 of the LUT entry size (uint2 or uint4)
+    qa.lin_scale = 0.5f * (float)H;
+    qa.lin_bias = 8388608.0f + 0.5f * (float)H;
+    qa.lin_off = 0u - (kLinBits << e);
     qa.nbuckets = H + 1;
-    qa.special0 = 0;
-    qa.special1 = H;
+    qa.special0 = qa.special1 = -1;  // y is always in [-1, 1]: no bucket for non-finite values
     memcpy(qa.base, best.base, (size_t)qa.nbuckets);
   } else if (best.mode == LOG) {
     qa.sh = best.lp.sh;
@@ -192,9 +196,13 @@ uint32_t host_nearest(const bq::PreparedTable& t, float y) {
   }
   uint32_t idx;
   if (t.mode == LIN) {
-    float zz = fmaf(y, kLinAlpha, kLinBeta);
-    zz = fminf(fmaxf(zz, 0.0f), 1.0f);
-    idx = (f32_bits(zz) >> qa.sh) & ((1u << (24 - qa.sh)) - 1u);
+    // The kernels bring a non-finite element to y = 0, whose code is z.
+    if (!(fabsf(y) <= 1.0f)) y = 0.0f;
+    const float zz = fmaf(y, qa.lin_scale, qa.lin_bias);
+    idx = f32_bits(zz) - kLinBits;
+    // The kernels' form: the entry's byte offset from bits(zz) in one shift-and-add.
+    const int e = t.M <= 1 ? 3 : 4;
+    if ((f32_bits(zz) << e) + qa.lin_off != idx << e || idx >= (uint32_t)qa.nbuckets) return 0xffffffffu;
   } else {
     uint32_t u = f32_bits(y);
     uint32_t a = std::min(std::max(u & 0x7fffffffu, qa.lo), qa.hi);

@@ -7,12 +7,12 @@
 //   d_b   = fl32(a_b - mean);  per group of B2 blocks: a2_g = max |d_b|,
 //   q2_b  = nearest code of fl32(fl32(d_b * s) * fl32(1 / fl32(a2_g * s))) in the 256 table
 //
-// The data quantize kernel already writes the block maxima (binary32, or the 16 bits of fp16 /
-// bf16 input, which hold them exactly) and, per wave of 2048 elements, the pairwise sum of its
-// blocks' maxima: an aligned subtree of 2^k leaves of the mean's tree (blocks past n hold +0,
-// and x + 0 = x, so padding never changes a sum).  Then:
-//   run_sum_kernel: sums runs of 2048 partials in place (more than 512 partials);
-//   mean_kernel:    finishes the tree (only when more than 512 run sums remain);
+// The data quantize kernel writes the block maxima (binary32, or the 16 bits of fp16 / bf16
+// input, which hold them exactly).  Then:
+//   run_sum_kernel: one workgroup per run of 16384 blocks sums the run's maxima as an aligned
+//                   subtree of the mean's tree (blocks past nb count as +0, and x + 0 = x, so
+//                   padding never changes a sum) into one binary64 run sum;
+//   mean_kernel:    finishes the tree over the run sums (only when more than 512 remain);
 //   stats_kernel:   finishes the tree itself otherwise (each workgroup, the same bits), then
 //                   takes the same absmax / guard / LUT search as the data kernel over groups
 //                   of the block maxima and writes q2 and the group maxima.
@@ -80,35 +80,74 @@ __device__ __forceinline__ double wave_tree512(const double* __restrict__ leaves
 }
 constexpr int64_t kFusedLeaves = 512;  // leaves the statistics kernel sums itself
 
-// First level over many per-wave partial sums: workgroup r replaces leaf 2048r by the sum of
-// leaves [2048r, 2048r + 2048), an aligned subtree of the same tree.  Thread t adds leaves
-// [8t, 8t + 8) of the run as a 3-level tree, the xor butterfly joins the aligned runs of 16 ..
-// 512 leaves inside each wave, and thread 0 joins the four waves as (w0 + w1) + (w2 + w3).  The
-// run is read in full before thread 0 writes (the barrier), and no other workgroup reads it.
+// Block maxima as the data pass stores them: binary32, or the 16 bits of bf16 / fp16 input.
+enum AbsmaxStore : int { AS_F32 = 0, AS_BF16 = 1, AS_F16 = 2 };
+
+// Block maximum as binary32 from its stored bits.
+template <int AS>
+__device__ __forceinline__ float stored_absmax(uint32_t bits16_or_32) {
+  if constexpr (AS == AS_F32) return bits_f32(bits16_or_32);
+  else if constexpr (AS == AS_BF16) return bits_f32(bits16_or_32 << 16);
+  else return (float)__builtin_bit_cast(_Float16, (unsigned short)bits16_or_32);
+}
+
+// First level of the mean's tree: workgroup r sums the maxima of blocks [16384r, 16384r +
+// 16384) into runs[r].  Thread t adds its 64 blocks [64t, 64t + 64) of the run as a 6-level
+// tree (eight 8-leaf trees, then a tree of their sums), the xor butterfly joins the aligned
+// runs of 128 .. 4096 blocks inside each wave, and thread 0 joins the four waves as
+// (w0 + w1) + (w2 + w3).  Every sum is an aligned subtree of the pairwise tree.
 constexpr int kRunThreads = 256;
-__global__ __launch_bounds__(kRunThreads) void run_sum_kernel(double* __restrict__ partials, int64_t npart) {
+constexpr int kRunPerThread = (int)(kRunBlocks / kRunThreads);  // 64
+static_assert(kRunPerThread == 64, "a thread sums 64 blocks");
+
+template <int AS>
+__global__ __launch_bounds__(kRunThreads) void run_sum_kernel(const void* __restrict__ absmax, int64_t nb,
+                                                              double* __restrict__ runs) {
   __shared__ double s_w[kRunThreads / 64];
   const int t = threadIdx.x;
-  const int64_t j0 = (int64_t)blockIdx.x * kWaveLeaves + (int64_t)t * 8;
-  double v[8];
-  if (j0 + 8 <= npart) {
-    const double2* p = reinterpret_cast<const double2*>(partials + j0);
+  const int64_t b0 = (int64_t)blockIdx.x * kRunBlocks + (int64_t)t * kRunPerThread;
+  constexpr int kBytes = AS == AS_F32 ? 4 : 2;
+  constexpr int kVec = kRunPerThread * kBytes / 16;  // 16-byte loads per thread
+  uint32_t raw[kRunPerThread * kBytes / 4];
+  const uint8_t* src = static_cast<const uint8_t*>(absmax) + b0 * kBytes;
+  if (b0 + kRunPerThread <= nb) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const double2 d = p[i];
-      v[2 * i] = d.x;
-      v[2 * i + 1] = d.y;
+    for (int i = 0; i < kVec; ++i) {
+      const uint4 v = reinterpret_cast<const uint4*>(src)[i];
+      raw[4 * i] = v.x;
+      raw[4 * i + 1] = v.y;
+      raw[4 * i + 2] = v.z;
+      raw[4 * i + 3] = v.w;
     }
   } else {
+    const int nv = b0 < nb ? (int)(nb - b0) : 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = j0 + i < npart ? partials[j0 + i] : 0.0;
+    for (int i = 0; i < kRunPerThread * kBytes / 4; ++i) raw[i] = 0u;
+    if constexpr (AS == AS_F32) {
+      for (int i = 0; i < nv; ++i) raw[i] = reinterpret_cast<const uint32_t*>(src)[i];
+    } else {
+      const uint16_t* h = reinterpret_cast<const uint16_t*>(src);
+      for (int i = 0; i < nv; ++i) raw[i >> 1] |= (uint32_t)h[i] << (16 * (i & 1));
+    }
   }
-  double s = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+  double s8[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    double v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = 8 * c + i;
+      const uint32_t bits = AS == AS_F32 ? raw[k] : (raw[k >> 1] >> (16 * (k & 1))) & 0xffffu;
+      v[i] = (double)stored_absmax<AS>(bits);
+    }
+    s8[c] = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+  }
+  double s = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) s = s + __shfl_xor(s, m);
   if ((t & 63) == 0) s_w[t >> 6] = s;
   __syncthreads();
-  if (t == 0) partials[(int64_t)blockIdx.x * kWaveLeaves] = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
+  if (t == 0) runs[blockIdx.x] = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
 }
 
 // Sum of `count` leaves leaves[i * stride]: 16 waves add a 32768-leaf chunk (wave sums
@@ -171,9 +210,6 @@ constexpr int kStatThreads = 256;
 constexpr int kBPL = 16;                           // blocks per lane
 constexpr int kStatTile = kStatThreads * kBPL;     // 4096 blocks
 constexpr int kStatTiles = 4;                      // tiles per workgroup
-
-// Block maxima as the data pass stores them: binary32, or the 16 bits of bf16 / fp16 input.
-enum AbsmaxStore : int { AS_F32 = 0, AS_BF16 = 1, AS_F16 = 2 };
 
 template <int AS>
 struct AbsmaxLoad {
@@ -299,7 +335,8 @@ __global__ __launch_bounds__(kStatThreads) void stats_kernel(const void* __restr
     const int64_t grp = b0 >> log2b2;
     if ((tid & (g - 1)) == 0 && grp < ngroups) absmax2[grp] = a2;
     const float s = a2 < 0x1p-64f ? 0x1p64f : (a2 > 0x1p64f ? 0x1p-64f : 1.0f);
-    const float rc = 1.0f / (a2 * s);
+    // a group whose d are all zero (a2 = 0) takes y = 0, code z, everywhere
+    const float rc = a2 > 0.0f ? 1.0f / (a2 * s) : 0.0f;
     uint32_t w[kBPL / 4];
     if (__builtin_expect(__all(s == 1.0f), 1)) {
 #pragma unroll
@@ -360,30 +397,29 @@ hipError_t launch_stats_as(const void* absmax, int64_t nb, const double* leaves,
 }  // namespace
 
 int launch_nested_stats(const void* absmax, int dtype, int64_t nb, int blocksize2, const PreparedTable& t2,
-                        double* partials, int64_t npart, uint8_t* q2, float* absmax2, float* mean,
-                        void* stream) {
+                        double* runs, uint8_t* q2, float* absmax2, float* mean, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // Above 512 partial sums, runs of 2048 are first summed in place by one workgroup each (one
-  // workgroup reading them all would be bound by a single CU's bandwidth).  Up to 512 leaves
-  // remain, the statistics kernel finishes the tree itself; beyond, mean_kernel does.
+  // Run sums of 16384 blocks; up to 512 of them, the statistics kernel finishes the tree
+  // itself; beyond (more than 2^23 blocks), mean_kernel does.
+  const int64_t nruns = (nb + kRunBlocks - 1) / kRunBlocks;
   hipError_t e;
-  double* leaves = partials;
-  int64_t stride = 1, count = npart;
-  if (npart > kFusedLeaves) {
-    const int64_t runs = (npart + kWaveLeaves - 1) / kWaveLeaves;
-    e = launch_kernel(run_sum_kernel, dim3((unsigned)runs), dim3(kRunThreads), s, leaves, npart);
-    if (e != hipSuccess) return (int)e;
-    stride = kWaveLeaves;
-    count = runs;
-  }
+  const dim3 rgrid((unsigned)nruns);
+  if (dtype == F32) e = launch_kernel(run_sum_kernel<AS_F32>, rgrid, dim3(kRunThreads), s, absmax, nb, runs);
+  else if (dtype == BF16) e = launch_kernel(run_sum_kernel<AS_BF16>, rgrid, dim3(kRunThreads), s, absmax, nb, runs);
+  else e = launch_kernel(run_sum_kernel<AS_F16>, rgrid, dim3(kRunThreads), s, absmax, nb, runs);
+  if (e != hipSuccess) return (int)e;
+  int64_t count = nruns;
   if (count > kFusedLeaves) {
-    e = launch_kernel(mean_kernel, dim3(1), dim3(kMeanThreads), s, (const double*)leaves, stride, count, nb, mean);
+    e = launch_kernel(mean_kernel, dim3(1), dim3(kMeanThreads), s, (const double*)runs, (int64_t)1, count, nb,
+                      mean);
     if (e != hipSuccess) return (int)e;
     count = 0;
   }
   int log2b2 = 0;
   while ((1 << log2b2) < blocksize2) ++log2b2;
   const int64_t ngroups = (nb + blocksize2 - 1) / blocksize2;
+  const double* leaves = runs;
+  const int64_t stride = 1;
   if (dtype == F32)
     e = launch_stats_as<AS_F32>(absmax, nb, leaves, stride, count, mean, log2b2, ngroups, q2, absmax2, t2, s);
   else if (dtype == BF16)

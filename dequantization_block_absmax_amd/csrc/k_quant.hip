@@ -63,18 +63,25 @@ __device__ __forceinline__ float widen(const uint32_t* w, int e) {
   }
 }
 
-// Max of the finite-|x| key over the lane chunk.
+// Max of the finite-|x| key over the lane chunk; *finite tells whether every element of the
+// chunk is finite.  Common case first: the max of 2|x| (the shift drops the sign), for 16-bit
+// input two packed operations per pair.  Only when a wave holds an Inf/NaN (exponent all ones)
+// is the key recomputed with the wrap that excludes non-finite elements; for finite elements
+// both give 2|x| + off.
 template <int DT>
-__device__ __forceinline__ uint32_t chunk_key(const uint32_t* w) {
+__device__ __forceinline__ uint32_t chunk_key(const uint32_t* w, bool* finite) {
   if constexpr (DT == F32) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) m = max(m, w[i] << 1);
+    *finite = m < 0xff000000u;
+    // wave-uniform, so the rare path is a branch the common case skips
+    if (__builtin_expect(__all(*finite), 1)) return m + 0x01000000u;
     uint32_t k = 0;
 #pragma unroll
     for (int i = 0; i < 32; ++i) k = max(k, (w[i] << 1) + 0x01000000u);
     return k;
   } else {
-    // Common case first: the max of 2|h| (the shift drops the sign), two packed operations per
-    // pair.  Only when that max is Inf/NaN (exponent all ones) is the key recomputed with the
-    // wrap that excludes non-finite elements; for finite elements both give 2|h| + off.
     constexpr unsigned short off = DT == BF16 ? 0x0100 : 0x0800;
     constexpr uint32_t kNonFinite = DT == BF16 ? 0xff00u : 0xf800u;  // 2 * (bits of +Inf)
     u16x2 acc = {0, 0};
@@ -82,8 +89,8 @@ __device__ __forceinline__ uint32_t chunk_key(const uint32_t* w) {
     for (int i = 0; i < 16; ++i)
       acc = __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2, w[i]) << (u16x2){1, 1});
     const uint32_t m = max((uint32_t)acc.x, (uint32_t)acc.y);
-    // wave-uniform, so the rare path is a branch the common case skips
-    if (__builtin_expect(__all(m < kNonFinite), 1)) return m + off;
+    *finite = m < kNonFinite;
+    if (__builtin_expect(__all(*finite), 1)) return m + off;
     acc = (u16x2){0, 0};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -92,24 +99,6 @@ __device__ __forceinline__ uint32_t chunk_key(const uint32_t* w) {
     }
     return max((uint32_t)acc.x, (uint32_t)acc.y);
   }
-}
-
-// Lane i receives lane i + M of its 16-lane row (M < 16; lanes past the row end get 0, and
-// their results are never used).
-template <int M>
-__device__ __forceinline__ double row_shl(double x) {
-  const uint64_t u = __builtin_bit_cast(uint64_t, x);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, 0x100 | M, 0xf, 0xf, true);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), 0x100 | M, 0xf, 0xf, true);
-  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
-}
-
-// The value of lane `l` (wave-uniform).
-__device__ __forceinline__ double read_lane(double x, int l) {
-  const uint64_t u = __builtin_bit_cast(uint64_t, x);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
 // The block absmax in the input's own 16-bit format (fp16 / bf16 input), from the max key: the
@@ -244,23 +233,22 @@ struct QuantShared {
 };
 
 // Quantizes one lane chunk: block absmax, normalization, codes, packing and stores.  NESTED
-// (the data pass of a nested quantize) also writes the pairwise sum of the block maxima of this
-// wave's 2048 elements, and stores the block maxima in the input's own format (binary32 for
-// fp32 input, the 16 bits of fp16 / bf16 input, which hold them exactly); otherwise the block
-// maxima are binary32.
+// (the data pass of a nested quantize) stores the block maxima in the input's own format
+// (binary32 for fp32 input, the 16 bits of fp16 / bf16 input, which hold them exactly);
+// otherwise they are binary32.
 template <int DT, int KB, int MODE, int M, bool NESTED>
 __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, int64_t elem0, int64_t n, int log2g,
                                                void* __restrict__ absmax, uint8_t* __restrict__ packed,
-                                               double* __restrict__ partials, const QuantArgs& qa,
-                                               const typename Entry<M>::type* s_lut, const float* s_thr,
-                                               QuantShared& sh, uint4* stage) {
+                                               const QuantArgs& qa, const typename Entry<M>::type* s_lut,
+                                               const float* s_thr, QuantShared& sh, uint4* stage) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int G = 1 << log2g;
   const int64_t nb = (n + (kEPT << log2g) - 1) >> (5 + log2g);
 
   // Block absmax over G lanes.
-  uint32_t key = chunk_key<DT>(w);
+  bool finite;
+  uint32_t key = chunk_key<DT>(w, &finite);
   // Blocks of a whole wave or more (B >= 2048): DPP steps and lane reads, no LDS round trips.
   // Smaller blocks: LDS shuffles (the DPP form of group_max_u32, with its steps chosen at run
   // time, measured slower here: 2^29 bf16 4-bit 221.1 against 218.5 us).
@@ -284,35 +272,6 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, in
       static_cast<float*>(absmax)[blk] = a;
   }
 
-  if constexpr (NESTED) {
-    // Pairwise sum of the block maxima of this wave's 2048 elements: an aligned subtree of the
-    // nested mean's tree (blocks past n hold +0).  Lane i holds the sum of the subtree that
-    // starts at its block; each level adds the right neighbour subtree (lane i + m) to the left
-    // one, inside 16-lane rows by DPP row shifts, then across the four rows by lane reads.
-    // (Cross-lane shuffles through LDS made this chain long enough to slow the kernel by 4%.)
-    // Wave k of the grid writes partial k; with B = 4096 a block spans two waves and the
-    // first of the pair writes the block's absmax.
-    double sum = (double)a;
-    if (G <= 1) sum = sum + row_shl<1>(sum);
-    if (G <= 2) sum = sum + row_shl<2>(sum);
-    if (G <= 4) sum = sum + row_shl<4>(sum);
-    if (G <= 8) sum = sum + row_shl<8>(sum);
-    const double r0 = read_lane(sum, 0);
-    double wsum = r0;
-    if (G <= 32) {
-      const double r32 = read_lane(sum, 32);
-      if (G <= 16) {
-        const double r16 = read_lane(sum, 16), r48 = read_lane(sum, 48);
-        wsum = (r0 + r16) + (r32 + r48);
-      } else {
-        wsum = r0 + r32;
-      }
-    }
-    const int64_t gw = elem0 >> 11;  // global wave index: 2048 elements per wave
-    const int lper = log2g > 6 ? log2g - 6 : 0;  // log2 of the waves per block
-    if (lane == 0 && (gw & ((1 << lper) - 1)) == 0) partials[gw >> lper] = wsum;
-  }
-
   // Normalize with the power-of-two guard; codes are packed into their output word as soon
   // as they are found (first element of a pair in the high nibble for 4-bit codes).
   const float s = a < 0x1p-64f ? 0x1p64f : (a > 0x1p64f ? 0x1p-64f : 1.0f);
@@ -320,7 +279,9 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, in
   constexpr int kOut = KB == 4 ? 4 : 8;  // output words per lane chunk
   constexpr int kPer = 32 / kOut;        // codes per output word
   uint32_t o[kOut];
-  if (s == 1.0f) {
+  if (__builtin_expect(__all(finite && s == 1.0f && a > 0.0f), 1)) {
+    // Every element of the wave is finite and every block maximum is nonzero and needs no
+    // scaling: y = fl32(x * r) lies in [-1, 1] as it is.
 #pragma unroll
     for (int i = 0; i < kOut; ++i) {
       uint32_t q[kPer];
@@ -330,12 +291,19 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, in
       o[i] = pack_word<KB>(q);
     }
   } else {
+    // y = fl32(fl32(x * s) * r) for finite x in a block whose maximum is nonzero; a non-finite
+    // x, and every element of a zero block, takes y = 0, whose code is z (the nearest code to
+    // 0.0).  (Past n, the chunk holds NaN: code z, masked to the zero pad below.)
+    const bool live = a > 0.0f;
 #pragma unroll
     for (int i = 0; i < kOut; ++i) {
       uint32_t q[kPer];
 #pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        q[j] = nearest_code<MODE, M>((widen<DT>(w, i * kPer + j) * s) * r, qa, s_lut, s_thr);
+      for (int j = 0; j < kPer; ++j) {
+        const float x = widen<DT>(w, i * kPer + j);
+        const float y = (x * s) * r;
+        q[j] = nearest_code<MODE, M>(live && fabsf(x) <= 0x1.fffffep127f ? y : 0.0f, qa, s_lut, s_thr);
+      }
       o[i] = pack_word<KB>(q);
     }
   }
@@ -394,8 +362,7 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, in
 template <int DT, int KB, int MODE, int M, bool NESTED>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __restrict__ in, int64_t n, int log2g,
                                                             void* __restrict__ absmax,
-                                                            uint8_t* __restrict__ packed,
-                                                            double* __restrict__ partials, QuantArgs qa) {
+                                                            uint8_t* __restrict__ packed, QuantArgs qa) {
   using Tr = Traits<DT>;
   using E = typename Entry<M>::type;
   __shared__ float s_thr[260];
@@ -429,8 +396,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __res
       load_chunk_full<DT>(in, elem0, w);
       lut_fill<MODE, M, kThreads>(qa, lw, s_lut, s_thr, tid);
     }
-    quantize_chunk<DT, KB, MODE, M, NESTED>(w, kEPT, elem0, n, log2g, absmax, packed, partials, qa, s_lut, s_thr,
-                                            sh, stage);
+    quantize_chunk<DT, KB, MODE, M, NESTED>(w, kEPT, elem0, n, log2g, absmax, packed, qa, s_lut, s_thr, sh,
+                                            stage);
   } else {
     const auto lw = lut_fetch<MODE, M, kThreads>(qa, tid);
     const int64_t wave0 = elem0 - (int64_t)(tid & 63) * kEPT;
@@ -442,63 +409,58 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __res
       nvalid = load_chunk<DT>(in, n, elem0, w);
     }
     lut_fill<MODE, M, kThreads>(qa, lw, s_lut, s_thr, tid);
-    quantize_chunk<DT, KB, MODE, M, NESTED>(w, nvalid, elem0, n, log2g, absmax, packed, partials, qa, s_lut, s_thr,
-                                            sh, stage);
+    quantize_chunk<DT, KB, MODE, M, NESTED>(w, nvalid, elem0, n, log2g, absmax, packed, qa, s_lut, s_thr, sh,
+                                            stage);
   }
 }
 
 template <int DT, int KB, int MODE, int M>
-hipError_t launch4(const void* in, int64_t n, int log2g, void* absmax, uint8_t* packed, double* partials,
+hipError_t launch4(const void* in, int64_t n, int log2g, void* absmax, uint8_t* packed, bool nested,
                    const QuantArgs& qa, hipStream_t stream) {
   const dim3 grid((unsigned)quantize_grid(n));
-  if (partials != nullptr)
+  if (nested)
     return launch_kernel(quantize_kernel<DT, KB, MODE, M, true>, grid, dim3(kThreads), stream,
-                         static_cast<const uint8_t*>(in), n, log2g, absmax, packed, partials, qa);
+                         static_cast<const uint8_t*>(in), n, log2g, absmax, packed, qa);
   return launch_kernel(quantize_kernel<DT, KB, MODE, M, false>, grid, dim3(kThreads), stream,
-                       static_cast<const uint8_t*>(in), n, log2g, absmax, packed, partials, qa);
+                       static_cast<const uint8_t*>(in), n, log2g, absmax, packed, qa);
 }
 
 template <int DT, int KB>
-hipError_t launch_mode(const void* in, int64_t n, int log2g, void* absmax, uint8_t* packed,
-                       double* partials, const PreparedTable& t, hipStream_t s) {
+hipError_t launch_mode(const void* in, int64_t n, int log2g, void* absmax, uint8_t* packed, bool nested,
+                       const PreparedTable& t, hipStream_t s) {
   if (t.mode == LIN) {
-    if (t.M <= 1) return launch4<DT, KB, LIN, 1>(in, n, log2g, absmax, packed, partials, t.qa, s);
-    if (t.M == 2) return launch4<DT, KB, LIN, 2>(in, n, log2g, absmax, packed, partials, t.qa, s);
-    return launch4<DT, KB, LIN, 3>(in, n, log2g, absmax, packed, partials, t.qa, s);
+    if (t.M <= 1) return launch4<DT, KB, LIN, 1>(in, n, log2g, absmax, packed, nested, t.qa, s);
+    if (t.M == 2) return launch4<DT, KB, LIN, 2>(in, n, log2g, absmax, packed, nested, t.qa, s);
+    return launch4<DT, KB, LIN, 3>(in, n, log2g, absmax, packed, nested, t.qa, s);
   }
   if (t.mode == LOG) {
-    if (t.M <= 1) return launch4<DT, KB, LOG, 1>(in, n, log2g, absmax, packed, partials, t.qa, s);
-    if (t.M == 2) return launch4<DT, KB, LOG, 2>(in, n, log2g, absmax, packed, partials, t.qa, s);
-    return launch4<DT, KB, LOG, 3>(in, n, log2g, absmax, packed, partials, t.qa, s);
+    if (t.M <= 1) return launch4<DT, KB, LOG, 1>(in, n, log2g, absmax, packed, nested, t.qa, s);
+    if (t.M == 2) return launch4<DT, KB, LOG, 2>(in, n, log2g, absmax, packed, nested, t.qa, s);
+    return launch4<DT, KB, LOG, 3>(in, n, log2g, absmax, packed, nested, t.qa, s);
   }
-  return launch4<DT, KB, SEARCH, 1>(in, n, log2g, absmax, packed, partials, t.qa, s);
+  return launch4<DT, KB, SEARCH, 1>(in, n, log2g, absmax, packed, nested, t.qa, s);
 }
 
 template <int DT>
-hipError_t launch_dt(const void* in, int64_t n, int log2g, void* absmax, uint8_t* packed,
-                     double* partials, const PreparedTable& t, hipStream_t s) {
-  return t.K == 16 ? launch_mode<DT, 4>(in, n, log2g, absmax, packed, partials, t, s)
-                   : launch_mode<DT, 8>(in, n, log2g, absmax, packed, partials, t, s);
+hipError_t launch_dt(const void* in, int64_t n, int log2g, void* absmax, uint8_t* packed, bool nested,
+                     const PreparedTable& t, hipStream_t s) {
+  return t.K == 16 ? launch_mode<DT, 4>(in, n, log2g, absmax, packed, nested, t, s)
+                   : launch_mode<DT, 8>(in, n, log2g, absmax, packed, nested, t, s);
 }
 
 }  // namespace
 
 int quantize_grid(int64_t n) { return (int)((n + kTile - 1) / kTile); }
 
-int64_t quantize_partials(int64_t n, int blocksize) {
-  const int64_t waves = (int64_t)quantize_grid(n) * (kThreads / 64);
-  return blocksize == 4096 ? waves / 2 : waves;
-}
-
 int launch_quantize(const void* in, int dtype, int64_t n, int blocksize, const PreparedTable& t, void* absmax,
-                    uint8_t* packed, double* partials, void* stream) {
+                    uint8_t* packed, bool nested, void* stream) {
   int log2g = 0;
   while ((kEPT << log2g) < blocksize) ++log2g;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (dtype == F32) e = launch_dt<F32>(in, n, log2g, absmax, packed, partials, t, s);
-  else if (dtype == F16) e = launch_dt<F16>(in, n, log2g, absmax, packed, partials, t, s);
-  else e = launch_dt<BF16>(in, n, log2g, absmax, packed, partials, t, s);
+  if (dtype == F32) e = launch_dt<F32>(in, n, log2g, absmax, packed, nested, t, s);
+  else if (dtype == F16) e = launch_dt<F16>(in, n, log2g, absmax, packed, nested, t, s);
+  else e = launch_dt<BF16>(in, n, log2g, absmax, packed, nested, t, s);
   return (int)e;
 }
 

@@ -164,14 +164,14 @@ def test_noalloc_validation():
     fits = 1 << 29  # 2^29 elements at block size 64: the largest power of two that fits
     assert bq.bq_nested_workspace_bytes(fits, 64) <= limit < bq.bq_nested_workspace_bytes(2 * fits, 64)
     assert call(n=2 * fits) == bq.BQ_ERR_WORKSPACE
-    assert call(n=(1 << 33), blocksize=4096) == bq.BQ_ERR_WORKSPACE
+    assert call(n=(1 << 33), blocksize=32) == bq.BQ_ERR_WORKSPACE
 
 
 def test_workspace_bytes():
     assert bq.bq_nested_workspace_bytes(0, 64, 256) == 0
     for n, B in ((2**29, 64), (1000, 32), (8192 * 3 + 1, 4096)):
         nb = -(-n // B)
-        need = nb * 4 + (-(-n // 2048)) * 8  # fp32 block maxima + one fp64 partial sum per wave
+        need = nb * 4 + (-(-nb // 16384)) * 8  # fp32 block maxima + one fp64 sum per run of 16384 blocks
         ws = bq.bq_nested_workspace_bytes(n, B, 256)
         assert need <= ws < need + 512
 
