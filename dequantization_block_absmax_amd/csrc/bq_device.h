@@ -17,7 +17,7 @@ struct Entry<1> { typedef uint2 type; };
 // LDS size of the LUT, in entries.
 template <int MODE, int M>
 struct LutLayout {
-  static constexpr int kSize = MODE == LIN ? kLinLutMax : (MODE == LOG ? kLutMax : 1);
+  static constexpr int kSize = MODE == LIN ? kLinLutMax : MODE == LOG ? kLutMax : MODE == F16B ? kF16Size : 1;
 };
 
 // Nearest code of y (see bq_internal.h for the bucket functions).  y must be in [-1, 1] for
@@ -40,6 +40,12 @@ __device__ __forceinline__ uint32_t nearest_code(float y, const QuantArgs& qa,
       const float zz = __builtin_fmaf(y, qa.lin_scale, qa.lin_bias);
       const uint32_t off = (f32_bits(zz) << kLog2E) + qa.lin_off;
       e = *reinterpret_cast<const typename Entry<M>::type*>(reinterpret_cast<const char*>(lut) + off);
+    } else if constexpr (MODE == F16B) {
+      static_assert(M == 1, "F16B entries are 8 bytes");
+      typedef __fp16 h2 __attribute__((ext_vector_type(2)));
+      const uint32_t d = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(y, 0.0f));
+      const uint32_t m = (d & 0x3ff0u) | ((d >> 1) & 0x4000u);
+      e = *reinterpret_cast<const typename Entry<M>::type*>(reinterpret_cast<const char*>(lut) + (m >> 1));
     } else {
       // Byte offset of the entry, in five operations: LO and HI are multiples of 2^SH, so
       // clamping |y| bits >> SH to [LO >> SH, HI >> SH] gives j + (LO >> SH); the sign picks the
@@ -57,6 +63,46 @@ __device__ __forceinline__ uint32_t nearest_code(float y, const QuantArgs& qa,
     if constexpr (M >= 2) q += (y >= bits_f32(e.z) ? 1u : 0u);
     if constexpr (M >= 3) q += (y >= bits_f32(e.w) ? 1u : 0u);
     return q;
+  }
+}
+
+// Code from a fetched LUT entry (base, then up to three thresholds).
+template <int M>
+__device__ __forceinline__ uint32_t entry_code(float y, const typename Entry<M>::type& e) {
+  uint32_t q = e.x + (y >= bits_f32(e.y) ? 1u : 0u);
+  if constexpr (M >= 2) q += (y >= bits_f32(e.z) ? 1u : 0u);
+  if constexpr (M >= 3) q += (y >= bits_f32(e.w) ? 1u : 0u);
+  return q;
+}
+
+// Nearest codes of two values y0, y1 in [-1, 1].  F16B converts both in one instruction and
+// works on the pair h0 | h1 << 16: a mask keeps bits 4..13 of each half, the sign bits
+// shifted right by one land in the cleared bits 14 and 30 (one and-or), and the
+// 8-byte entries' offsets are (h0' >> 4) * 8 = bits 1..15 and (h1' >> 4) * 8 = the word >> 17.
+// Other modes take the values one at a time.
+template <int MODE, int M>
+__device__ __forceinline__ void nearest_pair(float y0, float y1, const QuantArgs& qa,
+                                             const typename Entry<M>::type* lut, const float* s_thr,
+                                             uint32_t& q0, uint32_t& q1) {
+  if constexpr (MODE == F16B) {
+    static_assert(M == 1, "F16B entries are 8 bytes");
+    typedef __fp16 h2 __attribute__((ext_vector_type(2)));
+    const uint32_t d = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(y0, y1));
+    uint32_t m = d & 0x3ff03ff0u;
+    uint32_t t = d >> 1;
+    asm("" : "+v"(m), "+v"(t));  // one mask and one shift for both halves (the compiler would
+                                 // otherwise split them per half)
+    const uint32_t p = (t & 0x40004000u) | m;  // bits 14 and 30 of m are clear: one v_and_or
+    const uint32_t off0 = __builtin_amdgcn_ubfe(p, 1u, 15u);
+    const uint32_t off1 = p >> 17;
+    const char* base = reinterpret_cast<const char*>(lut);
+    const typename Entry<M>::type e0 = *reinterpret_cast<const typename Entry<M>::type*>(base + off0);
+    const typename Entry<M>::type e1 = *reinterpret_cast<const typename Entry<M>::type*>(base + off1);
+    q0 = entry_code<M>(y0, e0);
+    q1 = entry_code<M>(y1, e1);
+  } else {
+    q0 = nearest_code<MODE, M>(y0, qa, lut, s_thr);
+    q1 = nearest_code<MODE, M>(y1, qa, lut, s_thr);
   }
 }
 
@@ -125,12 +171,18 @@ __device__ __forceinline__ LutWords<MODE, M, NT> lut_fetch(const QuantArgs& qa, 
     l.th[k] = i < 260 ? qa.thr[i] : 0.0f;
   }
   // Every entry of the base array is read, not just the nbuckets in use: the host zero-fills
-  // the rest, and a bound known at compile time leaves no branch between the loads.
+  // the rest, and a bound known at compile time leaves no branch between the loads.  F16B
+  // entries of negative y take their base from index - 1087, and the hole reads a valid index.
   constexpr int kSize = LutLayout<MODE, M>::kSize;
 #pragma unroll
   for (int k = 0; k < L::kLutIt; ++k) {
     const int i = tid + k * NT;
-    l.bs[k] = (k + 1) * NT <= kSize || i < kSize ? qa.base[i] : 0u;
+    if constexpr (MODE == F16B) {
+      const int j = i >= kF16NegLo ? i - kF16NegBase : min(i, kF16Pos - 1);
+      l.bs[k] = (k + 1) * NT <= kSize || i < kSize ? qa.base[j] : 0u;
+    } else {
+      l.bs[k] = (k + 1) * NT <= kSize || i < kSize ? qa.base[i] : 0u;
+    }
   }
   return l;
 }
@@ -157,7 +209,9 @@ __device__ __forceinline__ void lut_fill(const QuantArgs& qa, const LutWords<MOD
 #pragma unroll
     for (int k = 0; k < L::kLutIt; ++k) {
       const int i = tid + k * NT;
-      if (k * NT < qa.nbuckets && ((k + 1) * NT <= kSize || i < kSize)) {
+      // F16B: rounds wholly inside the hole (never read) are skipped too
+      const bool hole = MODE == F16B && k * NT >= kF16Pos && (k + 1) * NT <= kF16NegLo;
+      if (!hole && k * NT < qa.nbuckets && ((k + 1) * NT <= kSize || i < kSize)) {
         const uint32_t b = l.bs[k];  // <= 255, so b + 2 stays inside the 260 thresholds
         E e;
         e.x = b;

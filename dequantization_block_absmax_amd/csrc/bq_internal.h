@@ -29,8 +29,21 @@ enum Dtype : int { F32 = 0, F16 = 1, BF16 = 2 };
 //           idx = j + (sign(y) ? NJ : 0).  2^(23-SH) buckets per octave of |y| between
 //           2^-E and 1; j = NJ-1 (a >= HI) only for non-finite y.  Right for tables that
 //           are dense near 0.
+//   F16B:   h = the binary16 bits of y rounded toward zero (v_cvt_pkrtz_f16_f32, two elements
+//           per instruction); for |y| <= 1 bit 14 of h is clear, so moving the sign (bit 15)
+//           there, h' = (h & 0x3ff0) | ((h & 0x8000) >> 1), and idx = h' >> 4 give 64 buckets
+//           per octave of |y| from 2^-14 to 1, linear ones below, and every |y| < 2^-24 in the
+//           bucket of its signed zero.  Positive y give idx 0..960, negative y 1024..1984, so
+//           the LUT has 1985 entries with a small hole at 961..1023, and two elements' byte
+//           offsets take six operations.  The host keeps the bases of the two halves side by
+//           side (base index idx, or idx - 63 for negative y).  Right for tables that are dense
+//           near 0, with one compare.
 //   SEARCH: no buckets; branchless binary search over T (any valid table).
-enum Mode : int { LIN = 0, LOG = 1, SEARCH = 2 };
+enum Mode : int { LIN = 0, LOG = 1, SEARCH = 2, F16B = 3 };
+constexpr int kF16Pos = 961;       // F16B buckets of positive y: 0 .. 960
+constexpr int kF16NegLo = 1024;    // F16B buckets of negative y: 1024 .. 1984
+constexpr int kF16Size = 1985;     // F16B LUT entries, the hole 961 .. 1023 included
+constexpr int kF16NegBase = kF16NegLo - kF16Pos;  // 63: base index of negative bucket idx is idx - 63
 
 constexpr int kLutMax = 2100;            // LUT entries carried in the kernel arguments
 constexpr int kLinLutMax = 513;          // uniform buckets: H <= 512, so at most 513 entries

@@ -34,6 +34,25 @@ uint32_t lin_bucket(float y, int H) {
   return f32_bits(zz) - kLinBits;
 }
 
+// Bits of binary16(y) rounded toward zero, as v_cvt_pkrtz_f16_f32 (finite |y| < 65520; the
+// kernels only convert y in [-1, 1]).  Subnormal binary16 results are kept.
+uint32_t f16_rtz_bits(float y) {
+  const uint32_t u = f32_bits(y);
+  const uint32_t sign = (u >> 16) & 0x8000u;
+  const int e = (int)((u >> 23) & 0xff) - 127;  // exponent of a normal binary32 value
+  const uint32_t mant = u & 0x7fffffu;
+  if (((u >> 23) & 0xff) == 0) return sign;     // zero or binary32 subnormal: below 2^-126
+  if (e >= -14) return sign | ((uint32_t)(e + 15) << 10) | (mant >> 13);
+  const int sh = -1 - e;                          // subnormal binary16: (2^23 + mant) * 2^(e + 1) / 2^23 * 2^24
+  return sign | (sh >= 24 ? 0u : ((0x800000u | mant) >> sh));
+}
+
+// F16B bucket of y (see bq_internal.h): the sign moved from bit 15 to bit 14, then >> 4.
+int f16b_bucket(float y) {
+  const uint32_t h = f16_rtz_bits(y);
+  return (int)((((h & 0x3ff0u) | ((h & 0x8000u) >> 1))) >> 4);
+}
+
 struct LogParams {
   int sh;
   uint32_t lo, hi;
@@ -145,6 +164,41 @@ bool prepare_table(const float* entries, int size, PreparedTable* out) {
     if (ch.M <= 3 && cost < best_cost) { best = ch; best_cost = cost; }
   }
 
+  // binary16 buckets: one compare per element and a three-operation offset per pair.
+  {
+    std::vector<int> ranks(size - 1);
+    // rank in y order: negative buckets (largest index = most negative) first, then positive
+    auto rank_of_idx = [](int idx) { return idx >= kF16NegLo ? kF16Size - 1 - idx : kF16Pos + idx; };
+    bool ok = true;
+    for (int k = 0; k + 1 < size; ++k) {
+      const int idx = f16b_bucket(thr[k]);
+      if (!(idx < kF16Pos || (idx >= kF16NegLo && idx < kF16Size))) ok = false;
+      ranks[k] = ok ? rank_of_idx(idx) : 0;
+    }
+    if (ok) {
+      std::vector<uint8_t> full(kF16Size, 0);
+      const int nr = 2 * kF16Pos;
+      std::vector<int> cnt(nr + 1, 0), below(nr + 1, 0);
+      for (int r : ranks) cnt[r]++;
+      for (int r = 1; r <= nr; ++r) below[r] = below[r - 1] + cnt[r - 1];
+      int M = 0;
+      for (int r = 0; r < nr; ++r) M = std::max(M, cnt[r]);
+      const int cost = 2 + 2 * M;
+      if (M == 1 && cost < best_cost) {
+        Choice ch;
+        ch.mode = F16B;
+        ch.M = 1;
+        ch.sh = 4;
+        ch.nidx = kF16Size;
+        memset(ch.base, 0, sizeof(ch.base));
+        for (int idx = 0; idx < kF16Pos; ++idx) ch.base[idx] = (uint8_t)below[rank_of_idx(idx)];
+        for (int idx = kF16NegLo; idx < kF16Size; ++idx) ch.base[idx - kF16NegBase] = (uint8_t)below[rank_of_idx(idx)];
+        best = ch;
+        best_cost = cost;
+      }
+    }
+  }
+
   out->mode = best.mode;
   out->M = best.M;
   if (best.mode == LIN) {
@@ -170,6 +224,10 @@ bool prepare_table(const float* entries, int size, PreparedTable* out) {
     qa.special0 = best.lp.nj - 1;
     qa.special1 = 2 * best.lp.nj - 1;
     memcpy(qa.base, best.base, (size_t)qa.nbuckets);
+  } else if (best.mode == F16B) {
+    qa.nbuckets = kF16Size;
+    qa.special0 = qa.special1 = -1;  // y is always in [-1, 1]
+    memcpy(qa.base, best.base, (size_t)(2 * kF16Pos));
   } else {
     qa.nbuckets = 0;
     qa.special0 = qa.special1 = -1;
@@ -193,6 +251,20 @@ uint32_t host_nearest(const bq::PreparedTable& t, float y) {
     int q = 0;
     for (int step = qa.K >> 1; step >= 1; step >>= 1) q += (y >= qa.thr[q + step - 1]) ? step : 0;
     return (uint32_t)q;
+  }
+  if (t.mode == F16B) {
+    // The kernels bring a non-finite element to y = 0, whose code is z.
+    if (!(fabsf(y) <= 1.0f)) y = 0.0f;
+    const uint32_t h = f16_rtz_bits(y);
+    const uint32_t idx = (uint32_t)f16b_bucket(y);
+    // The kernels' form on a pair word h | 0 << 16: mask, shifted sign inserted into bit 14,
+    // byte offset of an 8-byte entry = bits 1..15.
+    const uint32_t m = h & 0x3ff03ff0u, t = h >> 1;
+    const uint32_t p = (0x40004000u & t) | (~0x40004000u & m);
+    if (((p >> 1) & 0x7fffu) != idx << 3) return 0xffffffffu;
+    if (!(idx < (uint32_t)kF16Pos || (idx >= (uint32_t)kF16NegLo && idx < (uint32_t)kF16Size))) return 0xffffffffu;
+    const uint32_t b = qa.base[idx >= (uint32_t)kF16NegLo ? idx - kF16NegBase : idx];
+    return b + ((y >= qa.thr[b]) ? 1u : 0u);
   }
   uint32_t idx;
   if (t.mode == LIN) {

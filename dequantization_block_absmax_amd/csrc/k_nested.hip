@@ -343,7 +343,8 @@ __global__ __launch_bounds__(kStatThreads) void stats_kernel(const void* __restr
       for (int j = 0; j < kBPL / 4; ++j) {
         uint32_t q[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) q[i] = nearest_code<MODE, M>(d[4 * j + i] * rc, qa, s_lut, s_thr);
+        for (int i = 0; i < 4; i += 2)
+          nearest_pair<MODE, M>(d[4 * j + i] * rc, d[4 * j + i + 1] * rc, qa, s_lut, s_thr, q[i], q[i + 1]);
         w[j] = pack_word<8>(q);
       }
     } else {
@@ -351,7 +352,9 @@ __global__ __launch_bounds__(kStatThreads) void stats_kernel(const void* __restr
       for (int j = 0; j < kBPL / 4; ++j) {
         uint32_t q[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) q[i] = nearest_code<MODE, M>((d[4 * j + i] * s) * rc, qa, s_lut, s_thr);
+        for (int i = 0; i < 4; i += 2)
+          nearest_pair<MODE, M>((d[4 * j + i] * s) * rc, (d[4 * j + i + 1] * s) * rc, qa, s_lut, s_thr, q[i],
+                                q[i + 1]);
         w[j] = pack_word<8>(q);
       }
     }
@@ -386,6 +389,8 @@ hipError_t launch_stats_as(const void* absmax, int64_t nb, const double* leaves,
     if (t2.M == 2) return launch_stats<AS, LIN, 2>(absmax, nb, leaves, stride, count, mean, log2b2, ngroups, q2, absmax2, qa, s);
     return launch_stats<AS, LIN, 3>(absmax, nb, leaves, stride, count, mean, log2b2, ngroups, q2, absmax2, qa, s);
   }
+  if (t2.mode == F16B)
+    return launch_stats<AS, F16B, 1>(absmax, nb, leaves, stride, count, mean, log2b2, ngroups, q2, absmax2, qa, s);
   if (t2.mode == LOG) {
     if (t2.M <= 1) return launch_stats<AS, LOG, 1>(absmax, nb, leaves, stride, count, mean, log2b2, ngroups, q2, absmax2, qa, s);
     if (t2.M == 2) return launch_stats<AS, LOG, 2>(absmax, nb, leaves, stride, count, mean, log2b2, ngroups, q2, absmax2, qa, s);

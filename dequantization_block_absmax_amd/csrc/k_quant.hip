@@ -286,14 +286,16 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, in
     for (int i = 0; i < kOut; ++i) {
       uint32_t q[kPer];
 #pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        q[j] = nearest_code<MODE, M>(widen<DT>(w, i * kPer + j) * r, qa, s_lut, s_thr);
+      for (int j = 0; j < kPer; j += 2)
+        nearest_pair<MODE, M>(widen<DT>(w, i * kPer + j) * r, widen<DT>(w, i * kPer + j + 1) * r, qa, s_lut, s_thr,
+                              q[j], q[j + 1]);
       o[i] = pack_word<KB>(q);
     }
   } else {
     // y = fl32(fl32(x * s) * r) for finite x in a block whose maximum is nonzero; a non-finite
     // x, and every element of a zero block, takes y = 0, whose code is z (the nearest code to
-    // 0.0).  (Past n, the chunk holds NaN: code z, masked to the zero pad below.)
+    // 0.0).  (Past n, the chunk holds NaN: code z, masked to the zero pad below.)  One element
+    // at a time: taking pairs here as the fast path does doubled the kernel's registers.
     const bool live = a > 0.0f;
 #pragma unroll
     for (int i = 0; i < kOut; ++i) {
@@ -433,6 +435,7 @@ hipError_t launch_mode(const void* in, int64_t n, int log2g, void* absmax, uint8
     if (t.M == 2) return launch4<DT, KB, LIN, 2>(in, n, log2g, absmax, packed, nested, t.qa, s);
     return launch4<DT, KB, LIN, 3>(in, n, log2g, absmax, packed, nested, t.qa, s);
   }
+  if (t.mode == F16B) return launch4<DT, KB, F16B, 1>(in, n, log2g, absmax, packed, nested, t.qa, s);
   if (t.mode == LOG) {
     if (t.M <= 1) return launch4<DT, KB, LOG, 1>(in, n, log2g, absmax, packed, nested, t.qa, s);
     if (t.M == 2) return launch4<DT, KB, LOG, 2>(in, n, log2g, absmax, packed, nested, t.qa, s);

@@ -249,6 +249,8 @@ def test_gemm_validation():
 # ---- host table preparation vs the oracle ------------------------------------------------
 
 def _search_probes(table, rng):
+    """Values next to every midpoint, the entries, random and log-spread values, special
+    values, and values around the binary16 subnormal and normal ranges."""
     t = np.asarray(table, np.float64)
     mids = ((t[:-1] + t[1:]) / 2).astype(np.float32)
     near = [mids]
@@ -262,7 +264,9 @@ def _search_probes(table, rng):
     logs = (rng.choice([-1, 1], 5000) * 2.0 ** rng.uniform(-30, 0, 5000)).astype(np.float32)
     special = np.float32([0.0, -0.0, 1.0, -1.0, 2.0**-149, -2.0**-149, 2.0**-126, 1 - 2.0**-24,
                           -(1 - 2.0**-24), np.nan, np.inf, -np.inf])
-    return np.concatenate(near + up + [entries, rand, logs, special])
+    f16 = np.float32([s * m * 2.0**e for s in (-1, 1) for e in (-26, -25, -24, -20, -15, -14, -13)
+                      for m in (1.0, 1.0 + 2.0**-23, 1.5, 2.0 - 2.0**-23)])
+    return np.concatenate(near + up + [entries, rand, logs, special, f16])
 
 
 def _oracle_codes(o, y, table):
@@ -278,6 +282,10 @@ TABLES = {
     "nf4_like": np.float32(np.sort(np.concatenate([[-1, 0, 1], np.linspace(-0.7, 0.72, 13)]))),
     "tiny_entries": np.float32(np.sort(np.concatenate([[-1, 0, 1, 2.0**-20, -2.0**-20, 2.0**-19],
                                                        np.linspace(0.1, 0.9, 10)]))),
+    # symmetric, 16 entries per side spaced 2^-19 apart below 2^-14 (thresholds in the binary16
+    # subnormal range), geometric above: binary16 buckets, one compare
+    "subnormal16": np.float32(np.sort(np.concatenate([
+        s * np.concatenate([np.arange(1, 17) * 2.0**-19, np.geomspace(2.0**-14, 1.0, 112)]) for s in (-1, 1)]))),
     # 200 entries packed into [0.5, 0.5 + 2e-4]: no bucketing keeps <= 3 compares -> search
     "clustered256": np.float32(np.sort(np.concatenate([np.linspace(-1, 0.45, 56),
                                                        0.5 + np.arange(200) * 2.0**-23 * 8]))),
@@ -299,6 +307,8 @@ def test_host_search_matches_oracle(name):
         assert mode == 2
     if name in ("table16", "hand16"):
         assert mode == 0 and cmp == 1
+    if name in ("table256", "subnormal16"):
+        assert mode == 3 and cmp == 1
 
 
 def test_launch_size_limit():

@@ -174,6 +174,9 @@ SEARCH_TABLES = {
     "clustered256": np.float32(np.sort(np.concatenate([np.linspace(-1, 0.45, 56),
                                                        0.5 + np.arange(200) * 2.0**-23 * 8]))),
     "dense_top16": np.float32(np.concatenate([np.linspace(-1, 0.9, 12), [0.93, 0.96, 0.98, 1.0]])),
+    # binary16 buckets with thresholds in the binary16 subnormal range
+    "subnormal16": np.float32(np.sort(np.concatenate([
+        s * np.concatenate([np.arange(1, 17) * 2.0**-19, np.geomspace(2.0**-14, 1.0, 112)]) for s in (-1, 1)]))),
 }
 
 
@@ -186,9 +189,16 @@ def test_search_modes(dev, o, name):
     # values clustered around the dense region hit the many-threshold buckets
     xc = x.clone()
     xc[::3] = 0.5 + (xc[::3] * 1e-4)
+    # blocks whose maximum is 1 and whose other values are tiny: y down to the binary16
+    # subnormal range and below
+    xt = x.clone()
+    xt[::64] = 1.0
+    xt[1::2] = xt[1::2] * (2.0 ** -18)
+    xt[3::4] = xt[3::4] * (2.0 ** -6)
     for B in (64, 4096):
         check_blockwise(o, x, "float32", B, table, "%s mode=%d cmp=%d B=%d" % (name, mode, cmp, B))
         check_blockwise(o, xc, "float32", B, table, "%s clustered B=%d" % (name, B))
+        check_blockwise(o, xt, "float32", B, table, "%s tiny B=%d" % (name, B))
 
 
 # ---- determinism and stream semantics ------------------------------------------------------
