@@ -67,6 +67,10 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
         "bqo_prepare_table": (ctypes.c_int, [fp, ctypes.c_int, fp]),
         "bqo_nested_groups": (ctypes.c_int, [fp, i64, ctypes.c_float, fp, ctypes.c_int, i32, i64, i64, u8p, fp]),
         "bqo_nested_stats": (ctypes.c_int, [fp, i64, fp, ctypes.c_int, i32, u8p, fp, fp]),
+        "iqo_vector_error": (ctypes.c_float, [ctypes.c_float] * 4),
+        "iqo_iq2xs_encode_block": (ctypes.c_int, [fp, ctypes.c_uint16, u8p, u8p]),
+        "iqo_iq2xs_quantize": (ctypes.c_int64, [vp, ctypes.c_int, i64, u8p, vp, u8p, i64, i64]),
+        "iqo_iq2xs_dequantize": (ctypes.c_int, [u8p, u8p, i64, ctypes.c_int, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -256,6 +260,52 @@ class Oracle:
             raise ValueError("oracle dequant_q32 rejected its arguments (%d)" % rc)
         return out[:n]
 
+    # IQ2_XS-style superblocks ------------------------------------------------------------
+    IQ2XS_BLOCK, IQ2XS_BYTES = 256, 74
+
+    @staticmethod
+    def _iq_grid(grid: np.ndarray) -> np.ndarray:
+        g = np.ascontiguousarray(grid, dtype=np.uint8).reshape(-1)
+        if g.size != 512 * 8:
+            raise ValueError("the grid holds 512 entries of 8 bytes")
+        return g
+
+    def iq2xs_vector_error(self, xn: float, dot: float, qn: float, s: float) -> np.float32:
+        return np.float32(self.lib.iqo_vector_error(*(float(np.float32(v)) for v in (xn, dot, qn, s))))
+
+    def iq2xs_encode_block(self, x: np.ndarray, d_bits: int, grid: np.ndarray):
+        """One superblock of 256 binary32 values -> (74 payload bytes, rejected flag)."""
+        xx = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+        if xx.size != 256:
+            raise ValueError("a superblock holds 256 values")
+        g = self._iq_grid(grid)
+        out = np.zeros(self.IQ2XS_BYTES, np.uint8)
+        rej = self.lib.iqo_iq2xs_encode_block(_ptr(xx), int(d_bits), _ptr(g), _ptr(out))
+        return out, rej
+
+    def iq2xs_quantize(self, x: np.ndarray, dtype: int, grid: np.ndarray, scales: np.ndarray):
+        """x: n raw elements of `dtype` (n a multiple of 256); scales: n/256 binary16 bit
+        patterns.  Returns (payload bytes, number of rejected scales)."""
+        xx = np.ascontiguousarray(x).reshape(-1)
+        n, nb = xx.size, xx.size // self.IQ2XS_BLOCK
+        g = self._iq_grid(grid)
+        sc = np.ascontiguousarray(scales, dtype=np.uint16).reshape(-1)
+        if sc.size != nb:
+            raise ValueError("one scale per superblock")
+        out = np.zeros(max(nb * self.IQ2XS_BYTES, 1), np.uint8)
+        rej = self.lib.iqo_iq2xs_quantize(_ptr(xx), dtype, n, _ptr(g), _ptr(sc), _ptr(out), 0, nb)
+        if rej < 0:
+            raise ValueError("oracle iq2xs_quantize rejected its arguments")
+        return out[:nb * self.IQ2XS_BYTES], int(rej)
+
+    def iq2xs_dequantize(self, blocks: np.ndarray, grid: np.ndarray, n: int, dtype: int = F32) -> np.ndarray:
+        b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(-1)
+        g = self._iq_grid(grid)
+        out = np.zeros(max(n, 1), np.float32 if dtype == F32 else np.uint16)
+        if self.lib.iqo_iq2xs_dequantize(_ptr(b), _ptr(g), n, dtype, _ptr(out)) != 0:
+            raise ValueError("oracle iq2xs_dequantize rejected its arguments")
+        return out[:n]
+
 
 def default_threads() -> int:
     """Host threads for the range-split entry points: the CPU count, at most 16."""
@@ -329,6 +379,26 @@ class ParallelOracle(Oracle):
                                                         _ptr(t), K, _ptr(a) + 4 * b0, _ptr(p) + p0)
         _run_all([job(b0, b1) for b0, b1 in self._parts(nb)], self.threads)
         return out[:n]
+
+    def iq2xs_quantize(self, x: np.ndarray, dtype: int, grid: np.ndarray, scales: np.ndarray):
+        xx = np.ascontiguousarray(x).reshape(-1)
+        n, nb = xx.size, xx.size // self.IQ2XS_BLOCK
+        g = self._iq_grid(grid)
+        sc = np.ascontiguousarray(scales, dtype=np.uint16).reshape(-1)
+        if sc.size != nb:
+            raise ValueError("one scale per superblock")
+        out = np.zeros(max(nb * self.IQ2XS_BYTES, 1), np.uint8)
+        lib, counts = self.lib, []
+
+        def job(b0, b1):
+            def run():
+                counts.append(lib.iqo_iq2xs_quantize(_ptr(xx), dtype, n, _ptr(g), _ptr(sc), _ptr(out), b0, b1))
+                return 0 if counts[-1] >= 0 else -1
+            return run
+        _run_all([job(b0, b1) for b0, b1 in self._parts(nb)], self.threads)
+        if any(c < 0 for c in counts):
+            raise ValueError("oracle iq2xs_quantize rejected its arguments")
+        return out[:nb * self.IQ2XS_BYTES], int(sum(counts))
 
     def nested_stats(self, absmax: np.ndarray, table2: np.ndarray, blocksize2: int = 256):
         """mean (one call over the whole array), then q2 / absmax2 over ranges of groups."""

@@ -7,7 +7,8 @@
  * table or constant generator with the GPU path.
  *
  * Build: gcc -std=c11 -O2 -ffp-contract=off -fno-fast-math -fPIC -shared
- * (binary32 operations round once each, round-to-nearest-even; no fused multiply-add).
+ * (binary32 operations round once each, round-to-nearest-even; no multiply-add is fused
+ * unless written as fmaf, which only the IQ2_XS error form of that section does).
  *
  * Sources (page title, then the section or passage followed):
  *  - "Respect the current CUDA stream in blockwise quantization" (bitsandbytes PR 2052):
@@ -449,6 +450,190 @@ int bqo_dequant_q32(const uint8_t* blocks, int dtype, int64_t n, int32_t row_len
       for (int j = 0; j < 32; ++j) {
         int q = (int8_t)blk[2 + j];
         store_elem(out, dtype, b * 32 + j, (float)q * d);
+      }
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* IQ2_XS-style search encoding and its decoding ("[OMNIML-5899] Add CUDA kernels for IQ  */
+/* packing", Model-Optimizer PR 2448: the Summary, "Dependency behavior", and the review   */
+/* items "Wire format", "Scale anchors", "Even-parity sign field", "Search equivalence";   */
+/* the later review's "IQ2_XS grouping" and "Negative scales" replies).                    */
+/*                                                                                        */
+/* Superblock: 256 consecutive elements, 74 bytes:                                        */
+/*   bytes 0-1   the caller's binary16 scale d (little-endian);                           */
+/*   bytes 2-65  32 little-endian 16-bit words, one per 8-element vector v (elements        */
+/*               8v .. 8v+7): bits 0-8 the grid entry e, bits 9-15 the signs of elements    */
+/*               0-6 (bit set = negative); element 7's sign makes the count even;          */
+/*   bytes 66-73 byte i = ls[2i] | ls[2i+1] << 4, ls[g] the 4-bit local scale of group g    */
+/*               (elements 16g .. 16g+15, vectors 2g and 2g+1).                             */
+/* Decoded element j of vector v: d * (2*ls + 1) / 8 * grid[e][j] * (-1 if its sign bit).   */
+/* The grid (512 entries of 8 magnitude bytes) is the caller's: the pages do not hold it.   */
+/*                                                                                        */
+/* Readings (restated where used):                                                        */
+/*  I1 a non-finite element is read as +0.0 (the Summary normalizes non-finite inputs);    */
+/*     -0.0 counts as non-negative.                                                        */
+/*  I2 d with no magnitude bits (+0.0 or -0.0) gives the all-zero payload; a NaN, infinite  */
+/*     or negative d is rejected (counted) and also gets the all-zero payload.             */
+/*  I3 a vector's error for entry e at scale s is the pages' clamped form                   */
+/*     max(fma(s*s, qn, fma(-2s, dot, xn)), 0) in binary32: xn = fma-chain sum of a_j^2,     */
+/*     dot = fma-chain sum of a_j*q_j (j ascending, from +0), qn = sum of q_j^2 (exact),    */
+/*     a_j = |x_j|; with an odd count of negative elements, dot becomes fma(-2, w, dot),    */
+/*     w = min_j fl(a_j*q_j), and the sign of the first element reaching w is flipped.     */
+/*  I4 s = d*(2*ls+1)/8 (exact in binary32).  Each group takes the local scale whose       */
+/*     summed error fl(E(v0) + E(v1)) is least, E(v) = min over entries of the error;       */
+/*     equal sums go to the lower ls.  Each vector then takes the entry of least error at   */
+/*     that scale, equal errors to the lower entry index.                                   */
+/* ------------------------------------------------------------------------------------ */
+
+enum { IQ_BLOCK = 256, IQ_VEC = 8, IQ_ENTRIES = 512, IQ_BYTES = 74 };
+
+typedef struct {
+  float a[IQ_VEC]; /* |x_j| (I1) */
+  int neg;         /* bit j set: x_j < 0 */
+  int odd;         /* odd count of negative elements */
+  float xn;        /* fma-chain sum of a_j^2 */
+} iq_vector;
+
+static void iq_load_vector(const float* x, iq_vector* v) {
+  v->neg = 0;
+  v->xn = 0.0f;
+  int count = 0;
+  for (int j = 0; j < IQ_VEC; ++j) {
+    float t = isfinite(x[j]) ? x[j] : 0.0f; /* I1 */
+    if (t < 0.0f) {
+      v->neg |= 1 << j;
+      ++count;
+    }
+    v->a[j] = fabsf(t);
+  }
+  v->odd = count & 1;
+  for (int j = 0; j < IQ_VEC; ++j) v->xn = fmaf(v->a[j], v->a[j], v->xn);
+}
+
+/* dot of |x| with the entry's magnitudes, after the even-parity correction (I3); *flip is
+ * the element whose sign the correction flips, or -1. */
+static float iq_entry_dot(const iq_vector* v, const uint8_t* q, int* flip) {
+  float dot = 0.0f;
+  for (int j = 0; j < IQ_VEC; ++j) dot = fmaf(v->a[j], (float)q[j], dot);
+  *flip = -1;
+  if (v->odd) {
+    int k = 0;
+    float w = v->a[0] * (float)q[0];
+    for (int j = 1; j < IQ_VEC; ++j) {
+      float p = v->a[j] * (float)q[j];
+      if (p < w) {
+        w = p;
+        k = j;
+      }
+    }
+    dot = fmaf(-2.0f, w, dot);
+    *flip = k;
+  }
+  return dot;
+}
+
+static float iq_entry_qnorm(const uint8_t* q) {
+  float s = 0.0f;
+  for (int j = 0; j < IQ_VEC; ++j) s += (float)q[j] * (float)q[j]; /* integers, exact */
+  return s;
+}
+
+/* The clamped error of I3 at scale s. */
+float iqo_vector_error(float xn, float dot, float qn, float s) {
+  return fmaxf(fmaf(s * s, qn, fmaf(-2.0f * s, dot, xn)), 0.0f);
+}
+
+/* Least error over the grid at scale s (I4); *entry gets the lowest index reaching it. */
+static float iq_best_entry(const iq_vector* v, const uint8_t* grid, float s, int* entry) {
+  float best = 0.0f;
+  for (int e = 0; e < IQ_ENTRIES; ++e) {
+    int flip;
+    const uint8_t* q = grid + IQ_VEC * e;
+    float err = iqo_vector_error(v->xn, iq_entry_dot(v, q, &flip), iq_entry_qnorm(q), s);
+    if (e == 0 || err < best) {
+      best = err;
+      *entry = e;
+    }
+  }
+  return best;
+}
+
+/* Encodes one superblock of 256 binary32 values; returns 1 when d is rejected (I2). */
+int iqo_iq2xs_encode_block(const float* x, uint16_t d_bits, const uint8_t* grid, uint8_t* out) {
+  memset(out, 0, IQ_BYTES);
+  if ((d_bits & 0x7fff) == 0) return 0;                             /* I2: zero scale */
+  if ((d_bits & 0x7c00) == 0x7c00 || (d_bits & 0x8000)) return 1;   /* I2: NaN, inf, negative */
+  float d = bqo_f16_to_f32(d_bits);
+  out[0] = (uint8_t)(d_bits & 0xff);
+  out[1] = (uint8_t)(d_bits >> 8);
+  iq_vector vec[IQ_BLOCK / IQ_VEC];
+  for (int v = 0; v < IQ_BLOCK / IQ_VEC; ++v) iq_load_vector(x + IQ_VEC * v, &vec[v]);
+  int ls[16];
+  for (int g = 0; g < 16; ++g) {
+    int best_l = 0;
+    float best_sum = 0.0f;
+    for (int l = 0; l < 16; ++l) {
+      float s = d * (float)(2 * l + 1) * 0.125f; /* I4 */
+      int e0, e1;
+      float sum = iq_best_entry(&vec[2 * g], grid, s, &e0) + iq_best_entry(&vec[2 * g + 1], grid, s, &e1);
+      if (l == 0 || sum < best_sum) {
+        best_sum = sum;
+        best_l = l;
+      }
+    }
+    ls[g] = best_l;
+    float s = d * (float)(2 * best_l + 1) * 0.125f;
+    for (int v = 2 * g; v < 2 * g + 2; ++v) {
+      int e = 0, flip;
+      iq_best_entry(&vec[v], grid, s, &e);
+      iq_entry_dot(&vec[v], grid + IQ_VEC * e, &flip);
+      int signs = vec[v].neg ^ (flip >= 0 ? 1 << flip : 0); /* even count of set bits */
+      uint16_t word = (uint16_t)(e | ((signs & 0x7f) << 9));
+      out[2 + 2 * v] = (uint8_t)(word & 0xff);
+      out[3 + 2 * v] = (uint8_t)(word >> 8);
+    }
+  }
+  for (int i = 0; i < 8; ++i) out[66 + i] = (uint8_t)(ls[2 * i] | (ls[2 * i + 1] << 4));
+  return 0;
+}
+
+/* Superblocks [b_lo, b_hi) of an n-element input of `dtype` (n a multiple of 256); returns
+ * the number of rejected scales, or -1 for invalid arguments. */
+int64_t iqo_iq2xs_quantize(const void* in, int dtype, int64_t n, const uint8_t* grid,
+                           const uint16_t* scales, uint8_t* out, int64_t b_lo, int64_t b_hi) {
+  if (dtype != BQO_F32 && dtype != BQO_F16 && dtype != BQO_BF16) return -1;
+  if (n < 0 || n % IQ_BLOCK != 0 || b_lo < 0 || b_hi > n / IQ_BLOCK) return -1;
+  int64_t rejected = 0;
+  float x[IQ_BLOCK];
+  for (int64_t b = b_lo; b < b_hi; ++b) {
+    for (int i = 0; i < IQ_BLOCK; ++i) x[i] = load_elem(in, dtype, b * IQ_BLOCK + i);
+    rejected += iqo_iq2xs_encode_block(x, scales[b], grid, out + b * IQ_BYTES);
+  }
+  return rejected;
+}
+
+/* Decodes n/256 superblocks to `dtype`: the binary32 value d*(2*ls+1)/8*q is exact (11, 5
+ * and 8 significant bits), then rounded once (R10); the sign is a negation. */
+int iqo_iq2xs_dequantize(const uint8_t* blocks, const uint8_t* grid, int64_t n, int dtype, void* out) {
+  if (dtype != BQO_F32 && dtype != BQO_F16 && dtype != BQO_BF16) return -1;
+  if (n < 0 || n % IQ_BLOCK != 0) return -1;
+  for (int64_t b = 0; b < n / IQ_BLOCK; ++b) {
+    const uint8_t* blk = blocks + b * IQ_BYTES;
+    float d = bqo_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));
+    for (int v = 0; v < IQ_BLOCK / IQ_VEC; ++v) {
+      int g = v / 2;
+      int ls = (blk[66 + g / 2] >> (4 * (g % 2))) & 0xf;
+      float dl = d * (float)(2 * ls + 1) * 0.125f;
+      int word = blk[2 + 2 * v] | (blk[3 + 2 * v] << 8);
+      int e = word & 0x1ff, signs = word >> 9, parity = 0;
+      for (int j = 0; j < 7; ++j) parity ^= (signs >> j) & 1;
+      signs |= parity << 7;
+      for (int j = 0; j < IQ_VEC; ++j) {
+        float val = dl * (float)grid[IQ_VEC * e + j];
+        store_elem(out, dtype, b * IQ_BLOCK + IQ_VEC * v + j, ((signs >> j) & 1) ? -val : val);
       }
     }
   }

@@ -754,4 +754,253 @@ def pin_gemm_exact_rational(o):
                 assert abs(Fraction(float(y[m, n])) - exact) <= bound, (K, m, n, float(y[m, n]), float(exact))
 
 
+# ------------------------------------------------------------------------------------------
+# IQ2_XS-style search encoding ('[OMNIML-5899] Add CUDA kernels for IQ packing')
+# ------------------------------------------------------------------------------------------
+
+def _iq_grid(rng) -> np.ndarray:
+    """512 distinct entries of 8 magnitudes from {8, 25, 43}, the byte alphabet the pages give
+    for the IQ2_XS grid (the grid itself is not on the pages)."""
+    rows = set()
+    out = []
+    while len(out) < 512:
+        r = tuple(int(v) for v in rng.choice([8, 25, 43], size=8))
+        if r not in rows:
+            rows.add(r)
+            out.append(r)
+    return np.array(out, np.uint8)
+
+
+def _even_patterns() -> np.ndarray:
+    """The 128 sign patterns (+1 / -1 over 8 elements) with an even number of -1."""
+    pats = [[-1 if (m >> j) & 1 else 1 for j in range(8)] for m in range(256) if bin(m).count("1") % 2 == 0]
+    return np.array(pats, np.int64)
+
+
+def _iq_fields(block: np.ndarray):
+    """(d bits, entry per vector, 8-bit sign mask per vector, local scale per group) of a
+    74-byte superblock, read from the byte layout of the pages' 'Wire format' item."""
+    b = [int(v) for v in block]
+    words = [b[2 + 2 * v] | (b[3 + 2 * v] << 8) for v in range(32)]
+    entries = [w & 511 for w in words]
+    masks = []
+    for w in words:
+        s7 = w >> 9
+        masks.append(s7 | ((bin(s7).count("1") & 1) << 7))
+    ls = [(b[66 + g // 2] >> (4 * (g % 2))) & 15 for g in range(16)]
+    return b[0] | (b[1] << 8), entries, masks, ls
+
+
+def _iq_block_bytes(d_bits, entries, masks, ls) -> np.ndarray:
+    out = np.zeros(74, np.uint8)
+    out[0], out[1] = d_bits & 0xFF, d_bits >> 8
+    for v in range(32):
+        assert bin(masks[v]).count("1") % 2 == 0
+        w = entries[v] | ((masks[v] & 0x7F) << 9)
+        out[2 + 2 * v], out[3 + 2 * v] = w & 0xFF, w >> 8
+    for i in range(8):
+        out[66 + i] = ls[2 * i] | (ls[2 * i + 1] << 4)
+    return out
+
+
+def _iq_decode64(block: np.ndarray, grid: np.ndarray) -> np.ndarray:
+    """binary64 decode with the GGML element scale d * (0.5 + ls) * 0.25 (exact here)."""
+    d_bits, entries, masks, ls = _iq_fields(block)
+    d = float(np.uint16(d_bits).view(np.float16))
+    out = np.zeros(256)
+    for v in range(32):
+        db = d * (0.5 + ls[v // 2]) * 0.25
+        for j in range(8):
+            out[8 * v + j] = db * int(grid[entries[v], j]) * (-1.0 if (masks[v] >> j) & 1 else 1.0)
+    return out
+
+
+def pin_iq2xs_exact_search(o):
+    """d = 8 and integer inputs of magnitude <= 215: every binary32 step of the search is exact
+    (all values are integers below 2^24), so the oracle must return the exact optimum.  It is
+    found here by decoding every candidate -- 16 local scales x 512 entries x all 128 even sign
+    patterns -- and summing squared differences: the least group error picks the local scale
+    (lower one on equal sums), then each vector the lowest entry of least error.  A duplicate
+    grid entry (400 = 17) and a vector that entry reproduces exactly check the tie rule."""
+    rng = _rng(71)
+    grid = _iq_grid(rng)
+    grid[400] = grid[17]
+    x = np.zeros(256, np.float32)
+    groups = [0, 3, 5, 7, 12, 15]  # group 5 stays zero
+    for g in (0, 3, 7, 12, 15):
+        x[16 * g:16 * g + 16] = rng.integers(-200, 201, size=16)
+    x[16 * 3:16 * 3 + 8] = rng.integers(-12, 13, size=8)  # one small and one large vector
+    x[16 * 7 + 3] = 0.0
+    signs = np.array([1, -1, -1, 1, 1, 1, -1, -1])
+    x[16 * 12 + 8:16 * 12 + 16] = 5 * grid[17].astype(np.int64) * signs  # ls 2 (2*ls+1 = 5)
+    block, rej = o.iq2xs_encode_block(x, 0x4800, grid)  # d = 8
+    assert rej == 0
+    d_bits, entries, masks, ls = _iq_fields(block)
+    assert d_bits == 0x4800
+    P = _even_patterns()
+    Q = grid.astype(np.int64)
+    xi = x.astype(np.int64)
+    for g in groups:
+        E = np.zeros((2, 16), np.int64)
+        first = np.zeros((2, 16), np.int64)
+        for k in range(2):
+            X = xi[16 * g + 8 * k:16 * g + 8 * k + 8]
+            for l in range(16):
+                dec = (2 * l + 1) * Q[:, None, :] * P[None, :, :]  # d * (2l+1)/8 * q * sign, d = 8
+                err = ((X[None, None, :] - dec) ** 2).sum(axis=2).min(axis=1)
+                E[k, l] = err.min()
+                first[k, l] = int(np.argmax(err == err.min()))
+        total = E[0] + E[1]
+        lstar = int(np.argmax(total == total.min()))
+        assert ls[g] == lstar, (g, ls[g], lstar, total)
+        for k in range(2):
+            v = 2 * g + k
+            assert entries[v] == first[k, lstar], (g, k, entries[v], first[k, lstar])
+            sgn = np.array([-1 if (masks[v] >> j) & 1 else 1 for j in range(8)])
+            dec = (2 * lstar + 1) * Q[entries[v]] * sgn
+            X = xi[8 * v:8 * v + 8]
+            assert int(((X - dec) ** 2).sum()) == E[k, lstar], (g, k)
+    assert entries[2 * 12 + 1] == 17 and ls[12] == 2  # the exact fit, lowest of the two equal entries
+
+
+def pin_iq2xs_tie_rules(o):
+    """A caller grid built for exact ties (entry 0 = (1, 0, ..., 0), entry 9 the same, every other
+    entry eight 255s) and d = 8, so a candidate's decoded vector is (2*ls+1) * entry * signs.
+    Group 0 = (4, 0, ..., 0) and zeros: at ls 0 the errors are (4-1)^2 + 1^2 = 10, at ls 1
+    (4-3)^2 + 3^2 = 10, more above, so the lower local scale 0 wins (the first vector alone would
+    pick ls 1); every vector takes entry 0 over its duplicate 9.  Group 1 = (-4, 0, ..., 0) and
+    zeros: one negative element, so the sign of the first element of least |x_j| * q_j (element
+    1, product 0) is flipped: sign bits 0 and 1, the same errors.  The payload is therefore all
+    zero past d except the word of vector 2, 3 << 9."""
+    grid = np.full((512, 8), 255, np.uint8)
+    grid[0] = grid[9] = [1, 0, 0, 0, 0, 0, 0, 0]
+    x = np.zeros(256, np.float32)
+    x[0], x[16] = 4.0, -4.0
+    block, rej = o.iq2xs_encode_block(x, 0x4800, grid)
+    want = np.zeros(74, np.uint8)
+    want[1] = 0x48
+    want[2 + 2 * 2 + 1] = (3 << 9) >> 8
+    assert rej == 0 and np.array_equal(block, want), np.nonzero(block != want)
+
+
+def pin_iq2xs_round_trip(o):
+    """Blocks that the format represents exactly (random d, local scales, distinct entries and
+    even sign patterns) encode back to the very bytes they were built from: their error is 0,
+    and no other candidate reaches 0 with the {8, 25, 43} alphabet and odd multipliers."""
+    rng = _rng(72)
+    grid = _iq_grid(rng)
+    for trial in range(3):
+        d = np.float16(2.0 ** rng.uniform(-12, 6))
+        d_bits = int(d.view(np.uint16))
+        ls = [int(v) for v in rng.integers(0, 16, 16)]
+        entries = [int(v) for v in rng.integers(0, 512, 32)]
+        masks = []
+        for _ in range(32):
+            m = int(rng.integers(0, 128))
+            masks.append(m | ((bin(m).count("1") & 1) << 7))
+        block = _iq_block_bytes(d_bits, entries, masks, ls)
+        x = _iq_decode64(block, grid).astype(np.float32)
+        assert np.array_equal(x.astype(np.float64), _iq_decode64(block, grid))  # exact in binary32
+        enc, rej = o.iq2xs_encode_block(x, d_bits, grid)
+        assert rej == 0
+        assert np.array_equal(enc, block), (trial, np.nonzero(enc != block))
+
+
+def pin_iq2xs_special_scales(o):
+    """d = +0.0 or -0.0: the all-zero payload, not rejected; NaN, infinite or negative d: the
+    all-zero payload, rejected (the pages' boundary refuses such scales and masks -0.0 into the
+    zero-payload branch); the smallest subnormal d is an ordinary scale."""
+    rng = _rng(73)
+    grid = _iq_grid(rng)
+    x = rng.standard_normal(256).astype(np.float32)
+    for bits, rejected in ((0x0000, 0), (0x8000, 0), (0x7E00, 1), (0x7C00, 1), (0xFC00, 1), (0xBC00, 1),
+                           (0x8001, 1), (0xFE00, 1)):
+        enc, rej = o.iq2xs_encode_block(x, bits, grid)
+        assert rej == rejected and not enc.any(), hex(bits)
+    enc, rej = o.iq2xs_encode_block(x * np.float32(2.0 ** -22), 0x0001, grid)
+    assert rej == 0 and enc[0] == 1 and enc[1] == 0 and enc[2:].any()
+
+
+def pin_iq2xs_nonfinite_elements_read_as_zero(o):
+    """NaN and infinite elements encode as 0.0 would: the payload is that of the same block with
+    zeros in their places."""
+    rng = _rng(74)
+    grid = _iq_grid(rng)
+    x = rng.standard_normal(256).astype(np.float32)
+    y = x.copy()
+    for i, v in ((3, np.nan), (17, np.inf), (18, -np.inf), (200, -np.nan), (255, np.inf)):
+        y[i] = v
+        x[i] = 0.0
+    d_bits = int(np.float16(0.02).view(np.uint16))
+    a, _ = o.iq2xs_encode_block(x, d_bits, grid)
+    b, _ = o.iq2xs_encode_block(y, d_bits, grid)
+    assert np.array_equal(a, b)
+    x[100] = -0.0  # -0.0 is not a negative element
+    c, _ = o.iq2xs_encode_block(x, d_bits, grid)
+    x[100] = 0.0
+    e, _ = o.iq2xs_encode_block(x, d_bits, grid)
+    assert np.array_equal(c, e)
+
+
+def pin_iq2xs_dtype_equivalence(o):
+    """The same values given as fp32, fp16 and bf16 (all exactly representable) encode to the
+    same payload."""
+    rng = _rng(75)
+    grid = _iq_grid(rng)
+    x = (rng.integers(-64, 65, size=512) / 8.0).astype(np.float32)
+    scales = np.array([int(np.float16(v).view(np.uint16)) for v in (0.05, 0.0625)], np.uint16)
+    ref, _ = o.iq2xs_quantize(x, oracle.F32, grid, scales)
+    h = x.astype(np.float16).view(np.uint16)
+    bf = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(o.iq2xs_quantize(h, oracle.F16, grid, scales)[0], ref)
+    assert np.array_equal(o.iq2xs_quantize(bf, oracle.BF16, grid, scales)[0], ref)
+
+
+def pin_iq2xs_decode_golden(o):
+    """The hand-worked superblock of tests/golden/iq2xs_decode.json decodes to its printed
+    values (binary32 and fp16 exact, bf16 with the one round-to-nearest-even case)."""
+    gd = _golden("iq2xs_decode.json")
+    grid = np.array([gd["grid_default"]] * 512, np.uint8)
+    for e, row in gd["grid_entries"].items():
+        grid[int(e)] = row
+    block = np.zeros(74, np.uint8)
+    d_bits = int(gd["d_bits"], 16)
+    block[0], block[1] = d_bits & 0xFF, d_bits >> 8
+    for v, w in gd["words"].items():
+        w = int(w, 16)
+        block[2 + 2 * int(v)], block[3 + 2 * int(v)] = w & 0xFF, w >> 8
+    for i, sb in enumerate(gd["scale_bytes"]):
+        block[66 + i] = int(sb, 16)
+    want = np.full(256, gd["vector_default"], np.float32)
+    for v, vals in gd["vectors"].items():
+        want[8 * int(v):8 * int(v) + 8] = vals
+    got = o.iq2xs_dequantize(block, grid, 256, oracle.F32)
+    assert np.array_equal(got, want)
+    h = o.iq2xs_dequantize(block, grid, 256, oracle.F16)
+    assert np.array_equal(h.view(np.float16).astype(np.float32), want)
+    want_bf = want.copy()
+    for v, vals in gd["bf16_vectors"].items():
+        want_bf[8 * int(v):8 * int(v) + 8] = vals
+    b = o.iq2xs_dequantize(block, grid, 256, oracle.BF16)
+    assert np.array_equal((b.astype(np.uint32) << 16).view(np.float32), want_bf)
+
+
+def pin_iq2xs_decode_random(o):
+    """Random payloads (finite d) decode to the binary64 GGML form, exactly in binary32, and to
+    torch's round-to-nearest-even of it in fp16 and bf16."""
+    rng = _rng(76)
+    grid = rng.integers(0, 256, size=(512, 8)).astype(np.uint8)
+    blocks = rng.integers(0, 256, size=(6, 74)).astype(np.uint8)
+    for k in range(6):
+        blocks[k, 1] &= 0x7B  # keep d finite
+    want = np.concatenate([_iq_decode64(blocks[k], grid) for k in range(6)])
+    got = o.iq2xs_dequantize(blocks, grid, 6 * 256, oracle.F32)
+    assert np.array_equal(got.astype(np.float64), want)
+    t = torch.from_numpy(want.astype(np.float32))
+    assert np.array_equal(o.iq2xs_dequantize(blocks, grid, 6 * 256, oracle.F16),
+                          t.to(torch.float16).view(torch.int16).numpy().view(np.uint16))
+    assert np.array_equal(o.iq2xs_dequantize(blocks, grid, 6 * 256, oracle.BF16),
+                          t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

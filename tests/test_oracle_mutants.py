@@ -51,6 +51,21 @@ MUTANTS = {
     "gemm_rounds_to_the_other_type": ("const float w16 = dtype == BQO_F16 ?", "const float w16 = dtype != BQO_F16 ?"),
     "gemm_transposed_weight": ("const int64_t f = n * K + k;", "const int64_t f = k * N + n;"),
     "gemm_binary32_sum": ("double acc = 0.0;", "float acc = 0.0f;"),
+    "iq_flip_strongest": ("      if (p < w) {", "      if (p > w) {"),
+    "iq_no_parity_correction": ("    dot = fmaf(-2.0f, w, dot);\n", ""),
+    "iq_scale_ties_to_higher": ("if (l == 0 || sum < best_sum)", "if (l == 0 || sum <= best_sum)"),
+    "iq_entry_ties_to_higher": ("if (e == 0 || err < best)", "if (e == 0 || err <= best)"),
+    "iq_sign_bits_at_8": ("(uint16_t)(e | ((signs & 0x7f) << 9))", "(uint16_t)(e | ((signs & 0x7f) << 8))"),
+    "iq_scale_nibbles_swapped": ("(uint8_t)(ls[2 * i] | (ls[2 * i + 1] << 4))", "(uint8_t)(ls[2 * i + 1] | (ls[2 * i] << 4))"),
+    "iq_local_scale_even": ("float s = d * (float)(2 * l + 1) * 0.125f; /* I4 */", "float s = d * (float)(2 * l + 2) * 0.125f; /* I4 */"),
+    "iq_decode_quarter": ("float dl = d * (float)(2 * ls + 1) * 0.125f;", "float dl = d * (float)(2 * ls + 1) * 0.25f;"),
+    "iq_decode_parity_dropped": ("      signs |= parity << 7;\n", ""),
+    "iq_nonfinite_kept": ("float t = isfinite(x[j]) ? x[j] : 0.0f; /* I1 */", "float t = x[j];"),
+    "iq_negative_scale_accepted": ("if ((d_bits & 0x7c00) == 0x7c00 || (d_bits & 0x8000)) return 1;",
+                                   "if ((d_bits & 0x7c00) == 0x7c00) return 1;"),
+    "iq_negative_zero_rejected": ("if ((d_bits & 0x7fff) == 0) return 0;", "if (d_bits == 0) return 0;"),
+    "iq_group_of_one_vector": ("+ iq_best_entry(&vec[2 * g + 1], grid, s, &e1);", "; (void)e1;"),
+    "iq_error_sign_flipped": ("fmaf(-2.0f * s, dot, xn)", "fmaf(2.0f * s, dot, xn)"),
 }
 
 
