@@ -111,7 +111,6 @@ extern "C" {
 int bq_last_hip_error(void) { return g_last_hip_error; }
 
 bq_status bq_debug_time_next_kernel(hipEvent_t start, hipEvent_t stop) {
-  if ((start == nullptr) != (stop == nullptr)) return BQ_ERR_NULL;
   bq::g_next_launch_start = start;
   bq::g_next_launch_stop = stop;
   return BQ_OK;
@@ -328,6 +327,33 @@ bq_status bq_dequant_q32(const void* blocks, bq_dtype dtype, int64_t n, int32_t 
   if (n / 32 > INT32_MAX) return BQ_ERR_SIZE;
   if (!aligned(blocks, 2) || !aligned(out, 16)) return BQ_ERR_ALIGNMENT;
   return hip_status(bq::launch_q32(blocks, dtype, n, (int)format, out, stream));
+}
+
+static bq_status check_iq2xs_shape(bq_dtype dtype, int64_t n, int64_t row_len) {
+  if (!valid_dtype(dtype)) return BQ_ERR_DTYPE;
+  if (row_len <= 0 || row_len % 256 != 0) return BQ_ERR_FORMAT;
+  if (n < 0 || n % row_len != 0 || n / 256 > INT32_MAX) return BQ_ERR_SIZE;
+  return BQ_OK;
+}
+
+bq_status bq_iq2xs_quantize(const void* in, bq_dtype dtype, int64_t n, int64_t row_len, const uint8_t* grid,
+                            const uint16_t* scales, uint8_t* blocks, uint32_t* rejected, hipStream_t stream) {
+  const bq_status st = check_iq2xs_shape(dtype, n, row_len);
+  if (st != BQ_OK || n == 0) return st;
+  if (in == nullptr || grid == nullptr || scales == nullptr || blocks == nullptr || rejected == nullptr)
+    return BQ_ERR_NULL;
+  if (!aligned(in, 16) || !aligned(grid, 16) || !aligned(scales, 2) || !aligned(blocks, 2) || !aligned(rejected, 4))
+    return BQ_ERR_ALIGNMENT;
+  return hip_status(bq::launch_iq2xs_quantize(in, dtype, n, grid, scales, blocks, rejected, stream));
+}
+
+bq_status bq_iq2xs_dequantize(const uint8_t* blocks, const uint8_t* grid, int64_t n, int64_t row_len,
+                              bq_dtype dtype, void* out, hipStream_t stream) {
+  const bq_status st = check_iq2xs_shape(dtype, n, row_len);
+  if (st != BQ_OK || n == 0) return st;
+  if (blocks == nullptr || grid == nullptr || out == nullptr) return BQ_ERR_NULL;
+  if (!aligned(blocks, 2) || !aligned(grid, 8) || !aligned(out, 16)) return BQ_ERR_ALIGNMENT;
+  return hip_status(bq::launch_iq2xs_dequantize(blocks, grid, n, dtype, out, stream));
 }
 
 }  // extern "C"

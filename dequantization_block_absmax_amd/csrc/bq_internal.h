@@ -157,6 +157,10 @@ int launch_dequantize_nested(void* out, int dtype, int64_t n, int blocksize, int
                              const NestedDequantArgs& a, const uint8_t* q2, const float* absmax2,
                              const float* mean, const uint8_t* packed, void* stream);
 int launch_q32(const void* blocks, int dtype, int64_t n, int fmt, void* out, void* stream);
+int launch_iq2xs_quantize(const void* in, int dtype, int64_t n, const uint8_t* grid, const uint16_t* scales,
+                          uint8_t* blocks, uint32_t* rejected, void* stream);
+int launch_iq2xs_dequantize(const uint8_t* blocks, const uint8_t* grid, int64_t n, int dtype, void* out,
+                            void* stream);
 
 // The library-owned scratch of bq_quantize_nested_noalloc (k_scratch.hip): kScratchBytes per
 // device, 256-byte aligned.  scratch_buffer sets *ptr to the current device's copy (its device

@@ -64,7 +64,8 @@ typedef enum {
   BQ_ERR_BLOCKSIZE = 4, /* blocksize not a power of two in [32, 4096] */
   BQ_ERR_TABLE = 5,     /* code table: size, order, range or spacing (see bq_code_table) */
   BQ_ERR_ALIGNMENT = 6, /* a device pointer is not aligned as required */
-  BQ_ERR_FORMAT = 7,    /* unknown bq_q32_format, or row_len not a multiple of 32 */
+  BQ_ERR_FORMAT = 7,    /* unknown bq_q32_format, or row_len not a multiple of 32 (of 256 for
+                           the IQ2_XS-style calls) */
   BQ_ERR_WORKSPACE = 8, /* nested workspace missing or smaller than bq_nested_workspace_bytes */
   BQ_ERR_HIP = 9        /* the HIP runtime rejected a launch */
 } bq_status;
@@ -211,6 +212,58 @@ bq_status bq_linear_blockwise(const void* x, bq_dtype dtype, int64_t M, int64_t 
 bq_status bq_gemm_blockwise(const void* x, bq_dtype dtype, int64_t M, int64_t K, int64_t N, int32_t blocksize,
                             const bq_code_table* code_table, const float* absmax, const uint8_t* packed,
                             float* y, hipStream_t stream);
+
+/* IQ2_XS-style search encoding ("[OMNIML-5899] Add CUDA kernels for IQ packing", Model-
+ * Optimizer PR 2448: the Summary's caller-computed fp16 superblock scales, the review items
+ * "Wire format", "Scale anchors", "Even-parity sign field" and "Search equivalence", and the
+ * round-3 "IQ2_XS grouping" item).  A superblock is 256 consecutive elements, stored in 74
+ * bytes:
+ *   bytes 0-1   the caller's binary16 scale d (little-endian);
+ *   bytes 2-65  32 little-endian 16-bit words, one per 8-element vector v: bits 0-8 the grid
+ *               entry e, bits 9-15 the signs of the vector's elements 0-6 (bit set =
+ *               negative); element 7's sign is the parity of those seven bits, so every
+ *               vector holds an even number of negative elements;
+ *   bytes 66-73 byte i = ls[2i] | ls[2i+1] << 4, the 4-bit local scale of each 16-element
+ *               group g (vectors 2g and 2g+1).
+ * Element j of vector v decodes to d * (2 * ls + 1) / 8 * grid[e][j], negated if its sign is
+ * set (exact in binary32, then rounded once to the output type).
+ * The grid is the caller's: 512 entries of 8 magnitude bytes (entry e, element j at byte
+ * 8e + j), for the IQ2_XS format those of the GGML grid (bytes 0x08, 0x19, 0x2b).
+ *
+ * The search, per superblock with a valid d (binary32 throughout, fused multiply-adds where
+ * written fma, every other operation rounded once):
+ *   a_j = |x_j| (a NaN or infinite element reads as +0; -0 is not negative);
+ *   xn = fma-chain sum of a_j^2 and dot_e = fma-chain sum of a_j * q_j (j = 0..7, from +0);
+ *   with an odd count of negative elements, dot_e = fma(-2, w_e, dot_e), w_e the least
+ *   fl(a_j * q_j), and the first element reaching w_e has its sign flipped;
+ *   s = d * (2 * ls + 1) / 8; error(e, s) = max(fma(s*s, qn_e, fma(-2s, dot_e, xn)), 0),
+ *   qn_e = sum of q_j^2;
+ *   each group takes the ls whose fl(E(v0) + E(v1)) is least (E(v) = least error of vector v
+ *   over the grid; equal sums: the lower ls), then each vector the entry of least error at
+ *   that ls (equal errors: the lower entry).
+ * Scales: d = +0 or -0 gives an all-zero superblock.  A NaN, infinite or negative d is
+ * rejected: the superblock is written as zeros and *rejected is incremented (atomically, on
+ * the device: the caller sets it beforehand and reads it after the stream work completes).
+ *   in        [device] n elements of `dtype`, 16-byte aligned.
+ *   n, row_len  row_len a positive multiple of 256 dividing n (n = 0: nothing enqueued), so no
+ *             superblock straddles a row (the per-row check of that page's round-3 review).
+ *   grid      [device] 4096 bytes, 16-byte aligned.
+ *   scales    [device] n / 256 binary16 bit patterns, 2-byte aligned.
+ *   blocks    [device] out: (n / 256) * 74 bytes, 2-byte aligned.
+ *   rejected  [device] one uint32 counter, 4-byte aligned.
+ * Errors: BQ_ERR_DTYPE, BQ_ERR_FORMAT (row_len), BQ_ERR_SIZE (n negative or not a multiple of
+ * row_len, more than INT32_MAX superblocks), BQ_ERR_NULL, BQ_ERR_ALIGNMENT, BQ_ERR_HIP. */
+bq_status bq_iq2xs_quantize(const void* in, bq_dtype dtype, int64_t n, int64_t row_len, const uint8_t* grid,
+                            const uint16_t* scales, uint8_t* blocks, uint32_t* rejected, hipStream_t stream);
+
+/* Decodes n / 256 superblocks laid out as bq_iq2xs_quantize writes them (any bytes: d is read
+ * as binary16 whatever it holds) to n elements of `dtype`.
+ *   blocks    [device] (n / 256) * 74 bytes, 2-byte aligned.
+ *   grid      [device] 4096 bytes, 8-byte aligned.
+ *   out       [device] out: n elements of `dtype`, 16-byte aligned.
+ * Errors: as bq_iq2xs_quantize. */
+bq_status bq_iq2xs_dequantize(const uint8_t* blocks, const uint8_t* grid, int64_t n, int64_t row_len,
+                              bq_dtype dtype, void* out, hipStream_t stream);
 
 /* The hipError_t (as int) of the most recent launch that failed on the calling thread with
  * BQ_ERR_HIP, or 0 if none has. */

@@ -159,6 +159,30 @@ def q32_blocks(nblocks: int, fmt: str, seed: int, device="cpu") -> torch.Tensor:
     return out.reshape(-1)
 
 
+def iq2xs_grid(seed: int = 512, alphabet=(8, 25, 43)) -> np.ndarray:
+    """512 distinct grid entries of 8 magnitude bytes drawn from `alphabet` (the byte values the
+    IQ2_XS grid uses; the grid itself is the caller's), as a (512, 8) uint8 array."""
+    rows, out, start = set(), [], 0
+    k = len(alphabet)
+    while len(out) < 512:
+        idx = (_srl(u64(seed, 7, start, 8), 33) % k).numpy()
+        start += 8
+        r = tuple(int(alphabet[i]) for i in idx)
+        if r not in rows:
+            rows.add(r)
+            out.append(r)
+    return np.array(out, np.uint8)
+
+
+def iq2xs_scales(x: torch.Tensor, ratio: float = 0.8) -> torch.Tensor:
+    """A caller's binary16 superblock scales for x (n a multiple of 256): ratio * (largest
+    finite |x| of the superblock) / 166.625, 166.625 being the largest decoded magnitude per
+    unit scale (15.5 / 4 * 43).  Returned as int16 bit patterns on x's device."""
+    a = x.to(torch.float32).reshape(-1, 256).abs()
+    a = torch.where(torch.isfinite(a), a, torch.zeros_like(a)).amax(dim=1)
+    return (a * (ratio / 166.625)).to(torch.float16).view(torch.int16)
+
+
 def to_bits16(t: torch.Tensor) -> np.ndarray:
     """uint16 bit patterns of a 16-bit tensor (for the oracle's numpy interface)."""
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
