@@ -10,10 +10,11 @@ One step is one pass of the whole hot path over one batch of synthetic input:
 Inputs are generated on the device before timing (they are resident in HBM when the timed
 region starts).  `value` is input bytes of the step / step time (the metric's "effective
 GB/s (input bytes)"); every call's algorithmic read+write bytes against the 8 TB/s HBM peak
-is in `detail`.  `roofline` is the slower of the two 1 GiB kernels, each timed per launch
-with HIP events on the stream it runs on, over as many steps again right after the timed
-region: the data kernel of bq_quantize_nested and the one kernel of bq_dequantize_nested
-(bq_debug_time_next_kernel: the launch stamps its own start and end into two events).  `cpu_baseline` is
+is in `detail`.  `roofline` is the slower of the two 1 GiB kernels as the step launches them,
+the data kernel of bq_quantize_nested and the one kernel of bq_dequantize_nested, each timed
+with HIP events on the stream it runs on over further steps right after the timed region: a
+launch armed with a start and a stop event, minus the span of a pair of back-to-back markers
+(the lead of the start marker over its kernel; see kernel_step_loop).  `cpu_baseline` is
 the CPU oracle on the whole step input from as many host threads as the oracle may use (at
 most 16), plus the same oracle on one thread over a sixteenth of the step; the threaded
 oracle's outputs are also this run's parity reference (`parity`: every output byte of the
@@ -166,6 +167,10 @@ class TimingEvents:
         self.made.append(ev.value)
         return ev.value
 
+    def record(self, ev: int, stream: int):
+        if self.hip.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
     def ms(self, a: int, b: int) -> float:
         out = self.ctypes.c_float()
         if self.hip.hipEventElapsedTime(self.ctypes.byref(out), a, b) != 0:
@@ -198,24 +203,40 @@ def timed_step_loop(w: Workload, torch, steps: int):
     return a.elapsed_time(b), (time.perf_counter() - t0) * 1e3
 
 
-def kernel_step_loop(w: Workload, bq, torch, steps: int, tev: TimingEvents):
-    """The same steps again, right after the timed region, with the launches of the
-    nested-quantize data kernel and of the nested-dequantize kernel stamping their own start
-    and end into events (bq_debug_time_next_kernel).  Each stamped launch idles the GPU for a
-    few microseconds on each side, so the stamped steps are kept out of the timed region.
-    Returns the per-launch ms of the two kernels."""
-    qk = [(tev.new(), tev.new()) for _ in range(steps)]
-    dk = [(tev.new(), tev.new()) for _ in range(steps)]
+def kernel_step_loop(w: Workload, bq, torch, cycles: int, tev: TimingEvents):
+    """Steps again, right after the timed region, in cycles of two, timing the in-step launches
+    of the nested-quantize data kernel Q and of the nested-dequantize kernel D with HIP events
+    on the stream they run on.  In the first step of a cycle both launches are armed with
+    bq_debug_time_next_kernel: the stop event takes the kernel's end; the start event is a
+    marker enqueued before it, whose timestamp leads the kernel's start by the latency of a
+    marker (on MI355X about 4-5 us, near constant).  In the second step a pair of markers is
+    recorded back to back before each of the two calls: the pair's span is that latency alone.
+    Returns (Q spans, D spans, pair spans) in ms; a kernel's time is the mean of its spans minus
+    the mean pair span.  Armed launches idle the GPU for a few microseconds around them, so
+    these steps stay out of the timed region."""
+    q, d, pairs = [], [], []
+    arm = bq.bq_debug_time_next_kernel
+    stream = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
-    for i in range(steps):
-        bq.check(bq.bq_debug_time_next_kernel(*qk[i]), "arm data-kernel events")
+    for _ in range(cycles):
+        a, b, c, e = tev.new(), tev.new(), tev.new(), tev.new()
+        bq.check(arm(a, b), "arm")
         w.run("quantize_nested")
-        bq.check(bq.bq_debug_time_next_kernel(*dk[i]), "arm dequantize-kernel events")
+        bq.check(arm(c, e), "arm")
         w.run("dequantize_nested")
         w.run("dequant_q32_q4")
         w.run("dequant_q32_q8")
+        q.append((a, b))
+        d.append((c, e))
+        for name in STEP:
+            if name in ("quantize_nested", "dequantize_nested"):
+                m0, m1 = tev.new(), tev.new()
+                tev.record(m0, stream)
+                tev.record(m1, stream)
+                pairs.append((m0, m1))
+            w.run(name)
     torch.cuda.synchronize()
-    return [tev.ms(e0, e1) for e0, e1 in qk], [tev.ms(e0, e1) for e0, e1 in dk]
+    return tuple([tev.ms(x, y) for x, y in v] for v in (q, d, pairs))
 
 
 def time_calls(fn, torch, reps: int) -> float:
@@ -595,7 +616,7 @@ def main():
     ms_per_step = total_ms / args.steps
     gpu_out = None if args.no_cpu_baseline else step_outputs(w, torch)  # the last timed step's outputs
     tev = TimingEvents(torch)
-    qk_ms, dk_ms = kernel_step_loop(w, bq, torch, args.steps, tev)
+    q_sp, d_sp, pair_sp = kernel_step_loop(w, bq, torch, args.steps, tev)
     tev.close()
     # Per-call breakdown: each call back to back between two events (an event between calls
     # adds a few microseconds of its own), REPS calls per round.  The GGUF calls rotate over
@@ -624,28 +645,31 @@ def main():
         detail[name] = dict(us=round(ms * 1e3, 2), input_gbs=round(c["inp"] / ms / 1e6, 1),
                             rw_gbs=round(c["rw"] / ms / 1e6, 1), pct_hbm_peak=round(100 * c["rw"] / ms / 1e6 / PEAK_GBS, 1))
 
-    # Roofline of the dominant kernel: the slower (by mean launch time over the stamped steps) of
-    # the data kernel inside bq_quantize_nested and the kernel of bq_dequantize_nested.  The data
-    # kernel's algorithmic bytes are the method's: 2 B of bf16 read and 0.5 B of codes written per
-    # element; what it also writes for the statistics (the block maxima and per-wave partial sums
-    # in the workspace, read back by the statistics kernels) is reported as intermediate bytes.
+    # Roofline of the dominant kernel: the slower (by its in-step launch time, from the event
+    # spans of kernel_step_loop) of the data kernel inside bq_quantize_nested and the kernel of
+    # bq_dequantize_nested.  The data kernel's algorithmic bytes are the method's: 2 B of bf16
+    # read and 0.5 B of codes written per element; the 16-bit block maxima it also writes for
+    # the statistics kernels (2 B per block) are reported as intermediate bytes.
     n = w.N5
-    qk_mean, dk_mean = statistics.fmean(qk_ms), statistics.fmean(dk_ms)
+    mean = statistics.fmean
+    lead = mean(pair_sp)
+    qk_mean, dk_mean = mean(q_sp) - lead, mean(d_sp) - lead
     q_bytes = 2 * n + n // 2
-    q_inter = w.ws_bytes
+    q_inter = 2 * w.nb
     dq_bytes = w.calls["dequantize_nested"]["rw"]
-    detail["quantize_nested data kernel (stamped launches)"] = dict(
-        us_mean=round(qk_mean * 1e3, 2), us_median=round(statistics.median(qk_ms) * 1e3, 2),
+    us = lambda v: round(v * 1e3, 2)  # noqa: E731
+    detail["quantize_nested data kernel (in-step, event spans)"] = dict(
+        us=us(qk_mean), span_us=us(mean(q_sp)), marker_pair_us=us(lead),
         pct_hbm_peak=round(100 * q_bytes / qk_mean / 1e6 / PEAK_GBS, 1),
         pct_hbm_peak_with_intermediate=round(100 * (q_bytes + q_inter) / qk_mean / 1e6 / PEAK_GBS, 1))
-    detail["dequantize_nested kernel (stamped launches)"] = dict(
-        us_mean=round(dk_mean * 1e3, 2), us_median=round(statistics.median(dk_ms) * 1e3, 2),
+    detail["dequantize_nested kernel (in-step, event spans)"] = dict(
+        us=us(dk_mean), span_us=us(mean(d_sp)), marker_pair_us=us(lead),
         pct_hbm_peak=round(100 * dq_bytes / dk_mean / 1e6 / PEAK_GBS, 1))
     detail["quantize_blockwise of the same tensor (no statistics)"] = dict(
         us=round(per["quantize_kernel"] * 1e3, 2),
         pct_hbm_peak=round(100 * (q_bytes + 4 * w.nb) / per["quantize_kernel"] / 1e6 / PEAK_GBS, 1))
     if qk_mean >= dk_mean:
-        roofline = dict(kernel="quantize_kernel<2, 4, 0, 1>, the data kernel of bq_quantize_nested",
+        roofline = dict(kernel="quantize_kernel<2, 4, 0, 1, true>, the data kernel of bq_quantize_nested",
                         bytes_per_launch=q_bytes, intermediate_bytes_per_launch=q_inter, ms=qk_mean,
                         traffic=traffic_for("quantize_kernel"))
     else:
@@ -655,7 +679,7 @@ def main():
     achieved = roofline["bytes_per_launch"] / kms / 1e6
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_GBS, 4), traffic=roofline.pop("traffic"),
-                    us_per_launch=round(kms * 1e3, 2), launches=len(qk_ms), **roofline)
+                    us_per_launch=round(kms * 1e3, 2), launches=len(q_sp), **roofline)
 
     if not args.no_detail:
         log("timing the individual workloads")

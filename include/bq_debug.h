@@ -28,15 +28,18 @@ bq_status bq_debug_nearest_codes(const bq_code_table* table, const float* y, int
                                  int32_t* codes, int32_t* mode, int32_t* compares);
 
 /* Measurement hook: the next kernel the library launches on the calling thread goes through
- * hipExtLaunchKernel, which stamps that kernel's own start and end times into `start` and
- * `stop`; then the hook forgets both.  The next call's first kernel is the one timed: the data
- * kernel of a nested quantize (bq_quantize_nested or bq_quantize_nested_noalloc; the blockwise
- * quantize of the data, which also writes the workspace), or the only kernel of the other
- * calls.  hipEventElapsedTime(start, stop) is then that kernel's duration as the call launches
- * it, with no marker packets between the call's kernels.  The events are the caller's
- * (created with timing enabled) and must stay valid until the work completes.  A call that
- * fails validation launches nothing and leaves the hook armed.  Passing two NULLs disarms it.
- * Returns BQ_OK, or BQ_ERR_NULL when exactly one event is NULL. */
+ * hipExtLaunchKernel with these events; then the hook forgets both.  The next call's first
+ * kernel is the one armed: the data kernel of a nested quantize (bq_quantize_nested or
+ * bq_quantize_nested_noalloc), or the only kernel of the other calls.  `stop` (if not NULL) is
+ * bound to that kernel and takes its end time, adding nothing to the kernel.  `start` (if not
+ * NULL) becomes a marker enqueued just before the kernel: on MI355X with ROCm 7.2 its
+ * timestamp leads the kernel's own start by a near-constant 4.4-5.4 us, so
+ * hipEventElapsedTime(start, stop) over one launch overstates it by that lead (two markers
+ * recorded back to back span about the same time, 4.1 us, and measure it).  Any armed
+ * launch also leaves the GPU idle for about 4.5 us after the kernel.  The events
+ * are the caller's (created with timing enabled) and must stay valid until the work completes.
+ * A call that fails validation launches nothing and leaves the hook armed.  Two NULLs disarm
+ * it.  Returns BQ_OK. */
 bq_status bq_debug_time_next_kernel(hipEvent_t start, hipEvent_t stop);
 
 #ifdef __cplusplus

@@ -532,16 +532,16 @@ def test_negative_zero_table_entry(dev, o):
 
 
 def test_data_kernel_timing_hook(dev, o):
-    """Events armed with bq_debug_time_next_kernel take the start and end of the data kernel of
-    the next nested quantize only (a positive elapsed time, shorter than the whole call), are
-    forgotten after it, and leave the outputs unchanged."""
+    """Events armed with bq_debug_time_next_kernel bracket the data kernel of the next nested
+    quantize only (a positive elapsed time, shorter than the whole call), are forgotten after
+    it, and leave the outputs unchanged; a start armed on one call and a stop on the next span
+    both calls' armed kernels."""
     n, B = 1 << 22, 64
     t16, t256 = synth.table16(), synth.table256()
     x = synth.blockwise_input(n, "bfloat16", 17, std=0.02, device=dev)
     r0 = gpu_nested(x, "bfloat16", B, t16, t256)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    assert bq.bq_debug_time_next_kernel(e0, None) == bq.BQ_ERR_NULL
     bq.check(bq.bq_debug_time_next_kernel(e0, e1))
     c0.record()
     r1 = gpu_nested(x, "bfloat16", B, t16, t256)
@@ -557,3 +557,12 @@ def test_data_kernel_timing_hook(dev, o):
     gpu_nested(x, "bfloat16", B, t16, t256)
     torch.cuda.synchronize()
     assert e0.elapsed_time(e1) >= k_ms
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    bq.check(bq.bq_debug_time_next_kernel(s0, None))
+    gpu_nested(x, "bfloat16", B, t16, t256)
+    bq.check(bq.bq_debug_time_next_kernel(None, s1))
+    r2 = gpu_nested(x, "bfloat16", B, t16, t256)
+    torch.cuda.synchronize()
+    assert s0.elapsed_time(s1) > k_ms
+    for k in ("absmax", "q2", "absmax2", "packed", "out"):
+        assert torch.equal(r0[k].view(torch.uint8), r2[k].view(torch.uint8)), k
