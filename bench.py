@@ -12,15 +12,14 @@ region starts).  `value` is input bytes of the step / step time (the metric's "e
 GB/s (input bytes)"); every call's algorithmic read+write bytes against the 8 TB/s HBM peak
 is in `detail`.  `roofline` is the slower of the two 1 GiB kernels as the step launches them,
 the data kernel of bq_quantize_nested and the one kernel of bq_dequantize_nested, each timed
-with HIP events on the stream it runs on over further steps right after the timed region: a
-launch armed with a start and a stop event, minus the span of a pair of back-to-back markers
-(the lead of the start marker over its kernel; see kernel_step_loop).  `cpu_baseline` is
+with HIP events on the stream it runs on over further steps right after the timed region, as
+the difference of two event spans that share a marker's lead (see kernel_step_loop).  `cpu_baseline` is
 the CPU oracle on the whole step input from as many host threads as the oracle may use (at
 most 16), plus the same oracle on one thread over a sixteenth of the step; the threaded
 oracle's outputs are also this run's parity reference (`parity`: every output byte of the
 step's calls against the oracle's).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-detail] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 40] [--no-detail] [--no-cpu-baseline]
     python bench.py --profile     (a few launches of each kernel plus a 1 GiB copy, for rocprofv3)
 """
 from __future__ import annotations
@@ -53,7 +52,9 @@ def parse_args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    # 40 warm-up steps (about 22 ms): the first ~15 ms of back-to-back steps run 3-5% slower
+    # while the GPU's clocks settle; the timed steps measure the sustained rate after that.
+    p.add_argument("--warmup", type=int, default=40)
     p.add_argument("--no-detail", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--profile", action="store_true")
@@ -204,39 +205,56 @@ def timed_step_loop(w: Workload, torch, steps: int):
 
 
 def kernel_step_loop(w: Workload, bq, torch, cycles: int, tev: TimingEvents):
-    """Steps again, right after the timed region, in cycles of two, timing the in-step launches
-    of the nested-quantize data kernel Q and of the nested-dequantize kernel D with HIP events
-    on the stream they run on.  In the first step of a cycle both launches are armed with
-    bq_debug_time_next_kernel: the stop event takes the kernel's end; the start event is a
-    marker enqueued before it, whose timestamp leads the kernel's start by the latency of a
-    marker (on MI355X about 4-5 us, near constant).  In the second step a pair of markers is
-    recorded back to back before each of the two calls: the pair's span is that latency alone.
-    Returns (Q spans, D spans, pair spans) in ms; a kernel's time is the mean of its spans minus
-    the mean pair span.  Armed launches idle the GPU for a few microseconds around them, so
-    these steps stay out of the timed region."""
-    q, d, pairs = [], [], []
+    """Steps again, right after the timed region, in cycles of four, timing the in-step
+    launches of the nested-quantize data kernel Q and of the nested-dequantize kernel D with
+    HIP events on the stream they run on.  A marker recorded before a launch leads it by a
+    near-constant few microseconds of idle GPU (a marker's latency), and a stop event bound to
+    a launch (bq_debug_time_next_kernel) takes the kernel's end, then idles the GPU for a few
+    microseconds after it.  So each kernel's time is the difference of two spans that open
+    with the same kind of marker:
+      step 2: marker before the previous step's Q8 dequant, stop bound to Q   (lead + Q8 + Q)
+      step 3: marker before Q8, stop bound to Q8                              (lead + Q8)
+      step 2: marker before D, stop bound to the Q4 dequant after it          (lead + D + Q4)
+      step 3: marker before Q4, stop bound to Q4                              (lead + Q4)
+    Inside a span nothing idles: Q runs right after Q8 and Q4 right after D, as in the timed
+    steps.  Returns (Q spans, Q8 spans, D spans, Q4 spans) in ms."""
+    spans = {k: [] for k in ("q", "q8", "d", "q4")}
     arm = bq.bq_debug_time_next_kernel
     stream = torch.cuda.current_stream().cuda_stream
+
+    def marker():
+        ev = tev.new()
+        tev.record(ev, stream)
+        return ev
+
+    def stop_on(name):
+        ev = tev.new()
+        bq.check(arm(None, ev), "arm")
+        w.run(name)
+        return ev
+
     torch.cuda.synchronize()
     for _ in range(cycles):
-        a, b, c, e = tev.new(), tev.new(), tev.new(), tev.new()
-        bq.check(arm(a, b), "arm")
-        w.run("quantize_nested")
-        bq.check(arm(c, e), "arm")
+        w.run("quantize_nested")                       # step 1
         w.run("dequantize_nested")
         w.run("dequant_q32_q4")
+        m = marker()
         w.run("dequant_q32_q8")
-        q.append((a, b))
-        d.append((c, e))
-        for name in STEP:
-            if name in ("quantize_nested", "dequantize_nested"):
-                m0, m1 = tev.new(), tev.new()
-                tev.record(m0, stream)
-                tev.record(m1, stream)
-                pairs.append((m0, m1))
+        spans["q"].append((m, stop_on("quantize_nested")))  # step 2
+        m = marker()
+        w.run("dequantize_nested")
+        spans["d"].append((m, stop_on("dequant_q32_q4")))
+        w.run("dequant_q32_q8")
+        w.run("quantize_nested")                       # step 3
+        w.run("dequantize_nested")
+        m = marker()
+        spans["q4"].append((m, stop_on("dequant_q32_q4")))
+        m = marker()
+        spans["q8"].append((m, stop_on("dequant_q32_q8")))
+        for name in STEP:                              # step 4
             w.run(name)
     torch.cuda.synchronize()
-    return tuple([tev.ms(x, y) for x, y in v] for v in (q, d, pairs))
+    return tuple([tev.ms(x, y) for x, y in spans[k]] for k in ("q", "q8", "d", "q4"))
 
 
 def time_calls(fn, torch, reps: int) -> float:
@@ -350,6 +368,7 @@ def detail_configs(bq, synth, torch, dev, peak):
     blockwise("bf16 n=2^26 8-bit B=4096", 1 << 26, "bfloat16", 4096, t256, 3, 0.02, reps=50)
     out.update(loading_pipeline(bq, synth, torch, dev, t16))
     out.update(fused_linear(bq, synth, torch, dev, t16, t256, peak))
+    out.update(iq2xs(bq, synth, torch, dev))
     return out
 
 
@@ -435,6 +454,46 @@ def fused_linear(bq, synth, torch, dev, t16, t256, peak, N=14336, K=4096, B=64, 
                 unfused_us=round(u_ms * 1e3, 2), speedup_vs_unfused=round(u_ms / f_ms, 2))
         del ws, wbf
     return out
+
+
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak (FMA = 2 flops, dual-issue / packed)
+
+
+def iq2xs(bq, synth, torch, dev, rows=4096, cols=14336, sets=4):
+    """The IQ2_XS-style encoder and decoder on a 4096 x 14336 bf16 weight (229,376
+    superblocks).  The encoder is a search bound by VALU issue: its algorithmic work per
+    superblock is 32 vectors x 512 entries x (an 8-term dot, 8 FMA, plus 2 FMA of the error
+    for each of the 16 local scales), 1,310,720 flops counting an FMA as two, reported against
+    the fp32 vector peak.  The decoder is bound by HBM (74 bytes in, 512 out per superblock)."""
+    n = rows * cols
+    nb = n // 256
+    x = synth.blockwise_input(n, "bfloat16", 40, std=0.02, p_out=0.01, device=dev)
+    scales = synth.iq2xs_scales(x)
+    grid = torch.from_numpy(synth.iq2xs_grid().reshape(-1)).to(dev)
+    blocks = torch.empty(nb * 74, dtype=torch.uint8, device=dev)
+    rejected = torch.zeros(1, dtype=torch.int32, device=dev)
+    outs = [torch.empty(n, dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+
+    def enc():
+        bq.check(bq.bq_iq2xs_quantize(x, bq.BQ_BF16, n, cols, grid, scales, blocks, rejected), "iq2xs quantize")
+    i = [0]
+
+    def dec():
+        out = outs[i[0] % sets]
+        i[0] += 1
+        bq.check(bq.bq_iq2xs_dequantize(blocks, grid, n, cols, bq.BQ_BF16, out), "iq2xs dequantize")
+    enc()
+    e_ms = statistics.median(time_calls(enc, torch, 3) for _ in range(ROUNDS))
+    d_ms = statistics.median(time_calls(dec, torch, 8) for _ in range(ROUNDS))
+    flops = nb * 32 * 512 * (16 + 16 * 4)
+    dec_bytes = nb * 74 + 2 * n
+    return {"iq2xs encode bf16 4096x14336 (search over a 512-entry grid)": dict(
+                us=round(e_ms * 1e3, 1), superblocks_per_s=round(nb / e_ms * 1e3, 1),
+                tflops=round(flops / e_ms / 1e9, 1),
+                pct_fp32_vector_peak=round(100 * flops / e_ms / 1e9 / FP32_VECTOR_PEAK_TFLOPS, 1)),
+            "iq2xs decode to bf16 4096x14336": dict(
+                us=round(d_ms * 1e3, 2), rw_gbs=round(dec_bytes / d_ms / 1e6, 1),
+                pct_hbm_peak=round(100 * dec_bytes / d_ms / 1e6 / PEAK_GBS, 1))}
 
 
 def loading_pipeline(bq, synth, torch, dev, table, chunks=8, chunk=1 << 25, B=64):
@@ -616,7 +675,7 @@ def main():
     ms_per_step = total_ms / args.steps
     gpu_out = None if args.no_cpu_baseline else step_outputs(w, torch)  # the last timed step's outputs
     tev = TimingEvents(torch)
-    q_sp, d_sp, pair_sp = kernel_step_loop(w, bq, torch, args.steps, tev)
+    q_sp, q8_sp, d_sp, q4_sp = kernel_step_loop(w, bq, torch, args.steps, tev)
     tev.close()
     # Per-call breakdown: each call back to back between two events (an event between calls
     # adds a few microseconds of its own), REPS calls per round.  The GGUF calls rotate over
@@ -652,18 +711,17 @@ def main():
     # the statistics kernels (2 B per block) are reported as intermediate bytes.
     n = w.N5
     mean = statistics.fmean
-    lead = mean(pair_sp)
-    qk_mean, dk_mean = mean(q_sp) - lead, mean(d_sp) - lead
+    qk_mean, dk_mean = mean(q_sp) - mean(q8_sp), mean(d_sp) - mean(q4_sp)
     q_bytes = 2 * n + n // 2
     q_inter = 2 * w.nb
     dq_bytes = w.calls["dequantize_nested"]["rw"]
     us = lambda v: round(v * 1e3, 2)  # noqa: E731
     detail["quantize_nested data kernel (in-step, event spans)"] = dict(
-        us=us(qk_mean), span_us=us(mean(q_sp)), marker_pair_us=us(lead),
+        us=us(qk_mean), span_q8_q_us=us(mean(q_sp)), span_q8_us=us(mean(q8_sp)),
         pct_hbm_peak=round(100 * q_bytes / qk_mean / 1e6 / PEAK_GBS, 1),
         pct_hbm_peak_with_intermediate=round(100 * (q_bytes + q_inter) / qk_mean / 1e6 / PEAK_GBS, 1))
     detail["dequantize_nested kernel (in-step, event spans)"] = dict(
-        us=us(dk_mean), span_us=us(mean(d_sp)), marker_pair_us=us(lead),
+        us=us(dk_mean), span_d_q4_us=us(mean(d_sp)), span_q4_us=us(mean(q4_sp)),
         pct_hbm_peak=round(100 * dq_bytes / dk_mean / 1e6 / PEAK_GBS, 1))
     detail["quantize_blockwise of the same tensor (no statistics)"] = dict(
         us=round(per["quantize_kernel"] * 1e3, 2),

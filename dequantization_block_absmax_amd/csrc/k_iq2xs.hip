@@ -10,8 +10,11 @@
 // The grid sits in LDS as binary32 magnitudes with their squared norms (18 KB).
 //   Pass 1: for each of its 64 entries a lane forms the corrected dot (fma chain, then the
 //           parity correction) and keeps it in a register, and updates the 16 running minima
-//           of the error over its entries, one per local scale (the scales' s*s and -2s are
-//           wave-uniform).  A min over the slices gives E(v) per local scale; a DPP add with
+//           of the error over its entries, one per local scale (s and s*s are wave-uniform,
+//           in scalar registers; fma(s, -2 dot, xn) equals fma(-2s, dot, xn) bit for bit, the
+//           doubling being exact, so -2 dot is formed once per entry; two entries per
+//           v_min3).  The lane's entries sit at fixed LDS offsets from a per-lane base
+//           (without it the address arithmetic cost 2 VALU and ~60 VGPRs per entry stream).  A min over the slices gives E(v) per local scale; a DPP add with
 //           the partner vector gives the group sums, whose first least entry is the ls.
 //   Pass 2: the lanes re-evaluate their 64 stored dots at that ls only, and a min over the
 //           slices of (error, entry) gives the lowest entry of least error.
@@ -31,14 +34,20 @@
 namespace bq {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kEntries = 512;
-constexpr int kSlices = 8;
-constexpr int kPerSlice = kEntries / kSlices;
 constexpr int kBlockElems = 256;
 constexpr int kBlockBytes = 74;
-static_assert(kThreads == (kBlockElems / 8) * kSlices, "one lane per (vector, slice)");
-static_assert(kEntries == 2 * kThreads, "each lane stages two grid entries");
+constexpr int kDecodeThreads = 256;
+
+// Grid slices per vector: 8 lanes share one vector, so a workgroup of 256 lanes holds a
+// superblock's 32 vectors and each lane keeps 64 corrected dots (117 VGPRs, 4 waves per SIMD).
+// 16 slices (512 lanes, 124 VGPRs, also 4 waves per SIMD) measured 18% slower at 4096 x 14336:
+// the per-lane reductions and set-up double while the search work per lane halves.
+constexpr int kSlices = 8;
+constexpr int kThreads = (kBlockElems / 8) * kSlices;
+constexpr int kPerSlice = kEntries / kSlices;
+static_assert(kSlices == 8 || kSlices == 16, "slices are the lanes of a half-row or of a row");
+static_assert(kEntries % kThreads == 0, "each lane stages whole grid entries");
 
 constexpr float kMaxFinite = 0x1.fffffep127f;
 
@@ -52,13 +61,45 @@ __device__ __forceinline__ int dpp_i(int v) {
 }
 
 // DPP controls: quad_perm [1,0,3,2], quad_perm [2,3,0,1], half-row mirror (lane i <-> 7 - i of
-// each 8), row rotate by 8 (the other half of the 16-lane row).
-constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kRor8 = 0x128;
+// each 8), row mirror (lane i <-> 15 - i of each 16), row rotate by 8.
+constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140, kRor8 = 0x128;
 
-__device__ __forceinline__ float min8(float v) {
+// Min over the kSlices lanes of a vector.
+__device__ __forceinline__ float min_slices(float v) {
   v = fminf(v, dpp_f<kXor1>(v));
   v = fminf(v, dpp_f<kXor2>(v));
-  return fminf(v, dpp_f<kHalfMirror>(v));
+  v = fminf(v, dpp_f<kHalfMirror>(v));
+  if constexpr (kSlices == 16) v = fminf(v, dpp_f<kMirror>(v));
+  return v;
+}
+
+__device__ __forceinline__ int or_slices(int v) {
+  v |= dpp_i<kXor1>(v);
+  v |= dpp_i<kXor2>(v);
+  v |= dpp_i<kHalfMirror>(v);
+  if constexpr (kSlices == 16) v |= dpp_i<kMirror>(v);
+  return v;
+}
+
+// The value of the other vector of the group (the lanes kSlices away).
+__device__ __forceinline__ float partner(float v) {
+  if constexpr (kSlices == 8) {
+    return dpp_f<kRor8>(v);
+  } else {
+    // ds_swizzle bit mode inside 32 lanes: and 0x1F, or 0, xor 0x10
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+  }
+}
+
+// Lexicographic min of (error, entry) over the kSlices lanes of a vector.
+template <int CTRL>
+__device__ __forceinline__ void key_step(float& be, int& bi) {
+  const float oe = dpp_f<CTRL>(be);
+  const int oi = dpp_i<CTRL>(bi);
+  if (oe < be || (oe == be && oi < bi)) {
+    be = oe;
+    bi = oi;
+  }
 }
 
 // The 8 elements of vector `vec` (elements 8 vec .. 8 vec + 7), widened exactly.
@@ -106,18 +147,26 @@ __global__ __launch_bounds__(kThreads) void iq2xs_encode_kernel(const uint8_t* _
     return;
   }
 
-  {  // stage the grid: lane t converts entries 2t and 2t + 1
-    const uint4 g = reinterpret_cast<const uint4*>(grid)[tid];
-    const uint32_t w[4] = {g.x, g.y, g.z, g.w};
+  // Stage the grid: lane t converts entries t * kStage .. t * kStage + kStage - 1.
+  constexpr int kStage = kEntries / kThreads;
+  {
+    uint32_t w[2 * kStage];
+    if constexpr (kStage == 2) {
+      const uint4 g = reinterpret_cast<const uint4*>(grid)[tid];
+      w[0] = g.x; w[1] = g.y; w[2] = g.z; w[3] = g.w;
+    } else {
+      const uint2 g = reinterpret_cast<const uint2*>(grid)[tid];
+      w[0] = g.x; w[1] = g.y;
+    }
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < kStage; ++k) {
       float q[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) q[j] = (float)((w[2 * k + j / 4] >> (8 * (j % 4))) & 0xffu);
       float qn = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) qn += q[j] * q[j];
-      const int e = 2 * tid + k;
+      const int e = kStage * tid + k;
       s_q[2 * e] = make_float4(q[0], q[1], q[2], q[3]);
       s_q[2 * e + 1] = make_float4(q[4], q[5], q[6], q[7]);
       s_qn[e] = qn;
@@ -125,8 +174,8 @@ __global__ __launch_bounds__(kThreads) void iq2xs_encode_kernel(const uint8_t* _
   }
 
   const int lane = tid & 63;
-  const int v = (tid >> 6) * 8 + (lane >> 3);
-  const int slice = lane & 7;
+  const int v = (tid >> 6) * (64 / kSlices) + lane / kSlices;
+  const int slice = lane % kSlices;
   float a[8];
   uint32_t neg = 0;
   {
@@ -144,16 +193,20 @@ __global__ __launch_bounds__(kThreads) void iq2xs_encode_kernel(const uint8_t* _
 #pragma unroll
   for (int j = 0; j < 8; ++j) xn = __builtin_fmaf(a[j], a[j], xn);
 
-  // Per local scale l: s = d (2l + 1) / 8 (exact), its square and -2s, wave-uniform.
+  // Per local scale l: s = d (2l + 1) / 8 (exact) and its square, wave-uniform.
   const float d = (float)__builtin_bit_cast(_Float16, dbits);
-  float s2[16], m2s[16];
+  float s2[16], sl[16];
 #pragma unroll
   for (int l = 0; l < 16; ++l) {
     const float s = d * (float)(2 * l + 1) * 0.125f;
     s2[l] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, s * s)));
-    m2s[l] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, -2.0f * s)));
+    sl[l] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, s)));
   }
   __syncthreads();
+
+  // The lane's entries are slice + kSlices * i: fixed LDS offsets from a per-lane base.
+  const float4* qb = s_q + 2 * slice;
+  const float* qnb = s_qn + slice;
 
   // Pass 1.
   float E[16];
@@ -165,8 +218,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_encode_kernel(const uint8_t* _
     float dd[2], qq[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int e = slice + kSlices * (i + k);
-      const float4 lo = s_q[2 * e], hi = s_q[2 * e + 1];
+      const float4 lo = qb[2 * kSlices * (i + k)], hi = qb[2 * kSlices * (i + k) + 1];
       const float q[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       float dot = 0.0f;
 #pragma unroll
@@ -176,26 +228,24 @@ __global__ __launch_bounds__(kThreads) void iq2xs_encode_kernel(const uint8_t* _
       for (int j = 0; j < 8; ++j) p[j] = a[j] * q[j];
       const float w = fminf(fminf(fminf(p[0], p[1]), fminf(p[2], p[3])), fminf(fminf(p[4], p[5]), fminf(p[6], p[7])));
       const float fixed = __builtin_fmaf(-2.0f, w, dot);
-      dd[k] = odd ? fixed : dot;
-      qq[k] = s_qn[e];
-      dots[i + k] = dd[k];
+      dots[i + k] = odd ? fixed : dot;
+      dd[k] = -2.0f * dots[i + k];  // exact: fma(s, -2 dot, xn) = fma(-2s, dot, xn)
+      qq[k] = qnb[kSlices * (i + k)];
     }
 #pragma unroll
     for (int l = 0; l < 16; ++l) {
-      const float r0 = __builtin_fmaf(s2[l], qq[0], __builtin_fmaf(m2s[l], dd[0], xn));
-      const float r1 = __builtin_fmaf(s2[l], qq[1], __builtin_fmaf(m2s[l], dd[1], xn));
-      E[l] = fminf(E[l], fminf(r0, r1));
+      const float r0 = __builtin_fmaf(s2[l], qq[0], __builtin_fmaf(sl[l], dd[0], xn));
+      const float r1 = __builtin_fmaf(s2[l], qq[1], __builtin_fmaf(sl[l], dd[1], xn));
+      E[l] = fminf(fminf(E[l], r0), r1);
     }
   }
 #pragma unroll
-  for (int l = 0; l < 16; ++l) E[l] = min8(E[l]);
-  if (!(xn <= kMaxFinite)) {  // the same in the 8 lanes of a vector
+  for (int l = 0; l < 16; ++l) E[l] = min_slices(E[l]);
+  if (!(xn <= kMaxFinite)) {  // the same in all lanes of a vector
     int nonfinite = 0;
 #pragma unroll
     for (int i = 0; i < kPerSlice; ++i) nonfinite |= (dots[i] <= kMaxFinite) ? 0 : 1;
-    nonfinite |= dpp_i<kXor1>(nonfinite);
-    nonfinite |= dpp_i<kXor2>(nonfinite);
-    nonfinite |= dpp_i<kHalfMirror>(nonfinite);
+    nonfinite = or_slices(nonfinite);
 #pragma unroll
     for (int l = 0; l < 16; ++l) E[l] = nonfinite ? 0.0f : __builtin_inff();
   }
@@ -204,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_encode_kernel(const uint8_t* _
 #pragma unroll
   for (int l = 0; l < 16; ++l) {
     const float e = fmaxf(E[l], 0.0f);
-    const float g = e + dpp_f<kRor8>(e);  // fl(E(v0) + E(v1)), the same in both vectors' lanes
+    const float g = e + partner(e);  // fl(E(v0) + E(v1)), the same in both vectors' lanes
     if (l == 0 || g < bg) {
       bg = g;
       bl = l;
@@ -218,24 +268,17 @@ __global__ __launch_bounds__(kThreads) void iq2xs_encode_kernel(const uint8_t* _
   int bi = 0;
 #pragma unroll
   for (int i = 0; i < kPerSlice; ++i) {
-    const int e = slice + kSlices * i;
-    const float r = fmaxf(__builtin_fmaf(ss, s_qn[e], __builtin_fmaf(m2, dots[i], xn)), 0.0f);
+    const float r = fmaxf(__builtin_fmaf(ss, qnb[kSlices * i], __builtin_fmaf(m2, dots[i], xn)), 0.0f);
     if (i == 0 || r < be) {
       be = r;
-      bi = e;
+      bi = i;
     }
   }
-  {
-    float oe = dpp_f<kXor1>(be);
-    int oi = dpp_i<kXor1>(bi);
-    if (oe < be || (oe == be && oi < bi)) { be = oe; bi = oi; }
-    oe = dpp_f<kXor2>(be);
-    oi = dpp_i<kXor2>(bi);
-    if (oe < be || (oe == be && oi < bi)) { be = oe; bi = oi; }
-    oe = dpp_f<kHalfMirror>(be);
-    oi = dpp_i<kHalfMirror>(bi);
-    if (oe < be || (oe == be && oi < bi)) { be = oe; bi = oi; }
-  }
+  bi = slice + kSlices * bi;
+  key_step<kXor1>(be, bi);
+  key_step<kXor2>(be, bi);
+  key_step<kHalfMirror>(be, bi);
+  if constexpr (kSlices == 16) key_step<kMirror>(be, bi);
 
   if (slice == 0) {
     uint32_t mask = neg;
@@ -288,10 +331,10 @@ __device__ __forceinline__ void store_vector(uint8_t* out, int64_t vec, float* v
 }
 
 template <int DT>
-__global__ __launch_bounds__(kThreads) void iq2xs_decode_kernel(const uint8_t* __restrict__ blocks,
+__global__ __launch_bounds__(kDecodeThreads) void iq2xs_decode_kernel(const uint8_t* __restrict__ blocks,
                                                                 const uint8_t* __restrict__ grid, int64_t nvec,
                                                                 uint8_t* __restrict__ out) {
-  const int64_t vec = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t vec = (int64_t)blockIdx.x * kDecodeThreads + threadIdx.x;
   if (vec >= nvec) return;
   const uint8_t* blk = blocks + (vec >> 5) * kBlockBytes;
   const int v = (int)(vec & 31);
@@ -322,7 +365,8 @@ hipError_t launch_encode_dt(const void* in, int64_t n, const uint8_t* grid, cons
 template <int DT>
 hipError_t launch_decode_dt(const uint8_t* blocks, const uint8_t* grid, int64_t n, void* out, hipStream_t s) {
   const int64_t nvec = n / 8;
-  return launch_kernel(iq2xs_decode_kernel<DT>, dim3((unsigned)((nvec + kThreads - 1) / kThreads)), dim3(kThreads),
+  return launch_kernel(iq2xs_decode_kernel<DT>, dim3((unsigned)((nvec + kDecodeThreads - 1) / kDecodeThreads)),
+                       dim3(kDecodeThreads),
                        s, blocks, grid, nvec, static_cast<uint8_t*>(out));
 }
 
