@@ -20,7 +20,8 @@ oracle's outputs are also this run's parity reference (`parity`: every output by
 step's calls against the oracle's).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 40] [--no-detail] [--no-cpu-baseline]
-    python bench.py --profile     (a few launches of each kernel plus a 1 GiB copy, for rocprofv3)
+    python bench.py --profile     (a few launches of each kernel, the bf16 2^26 8-bit calls and the
+                                   IQ2_XS encode / decode, then a 1 GiB copy, for rocprofv3)
 """
 from __future__ import annotations
 
@@ -656,6 +657,19 @@ def main():
             bq.check(bq.bq_quantize_blockwise(x3, bq.BQ_BF16, n3, 4096, w.t256, a3, p3), "bf16 2^26 8-bit quantize")
         for _ in range(3):
             bq.check(bq.bq_dequantize_blockwise(o3, bq.BQ_BF16, n3, 4096, w.t256, a3, p3), "bf16 2^26 8-bit dequantize")
+        # the IQ2_XS-style encoder and decoder on a 4096 x 14336 bf16 weight
+        n6, cols6 = 4096 * 14336, 14336
+        x6 = synth.blockwise_input(n6, "bfloat16", 40, std=0.02, p_out=0.01, device=dev)
+        s6 = synth.iq2xs_scales(x6)
+        g6 = torch.from_numpy(synth.iq2xs_grid().reshape(-1)).to(dev)
+        b6 = torch.empty(n6 // 256 * 74, dtype=torch.uint8, device=dev)
+        r6 = torch.zeros(1, dtype=torch.int32, device=dev)
+        o6 = torch.empty(n6, dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            bq.check(bq.bq_iq2xs_quantize(x6, bq.BQ_BF16, n6, cols6, g6, s6, b6, r6), "iq2xs quantize")
+        for _ in range(3):
+            bq.check(bq.bq_iq2xs_dequantize(b6, g6, n6, cols6, bq.BQ_BF16, o6), "iq2xs dequantize")
+        del x6, o6
         src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
