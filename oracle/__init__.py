@@ -71,6 +71,10 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
         "iqo_iq2xs_encode_block": (ctypes.c_int, [fp, ctypes.c_uint16, u8p, u8p]),
         "iqo_iq2xs_quantize": (ctypes.c_int64, [vp, ctypes.c_int, i64, u8p, vp, u8p, i64, i64]),
         "iqo_iq2xs_dequantize": (ctypes.c_int, [u8p, u8p, i64, ctypes.c_int, vp]),
+        "iqo_iq1s_scale": (ctypes.c_uint16, [ctypes.c_float]),
+        "iqo_iq1s_encode_block": (None, [fp, u8p, u8p]),
+        "iqo_iq1s_quantize": (ctypes.c_int, [vp, ctypes.c_int, i64, u8p, u8p, i64, i64]),
+        "iqo_iq1s_dequantize": (ctypes.c_int, [u8p, u8p, i64, ctypes.c_int, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -306,6 +310,42 @@ class Oracle:
             raise ValueError("oracle iq2xs_dequantize rejected its arguments")
         return out[:n]
 
+    # IQ1_S-style superblocks ------------------------------------------------------------
+    IQ1S_BYTES = 50
+
+    @staticmethod
+    def _iq1_grid(grid: np.ndarray) -> np.ndarray:
+        g = np.ascontiguousarray(grid, dtype=np.int8).reshape(-1)
+        if g.size != 2048 * 8:
+            raise ValueError("the grid holds 2048 entries of 8 signed bytes")
+        return g
+
+    def iq1s_scale(self, amax: float) -> int:
+        return int(self.lib.iqo_iq1s_scale(float(np.float32(amax))))
+
+    def iq1s_encode_block(self, x: np.ndarray, grid: np.ndarray) -> np.ndarray:
+        xx = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+        if xx.size != 256:
+            raise ValueError("a superblock holds 256 values")
+        out = np.zeros(self.IQ1S_BYTES, np.uint8)
+        self.lib.iqo_iq1s_encode_block(_ptr(xx), _ptr(self._iq1_grid(grid)), _ptr(out))
+        return out
+
+    def iq1s_quantize(self, x: np.ndarray, dtype: int, grid: np.ndarray) -> np.ndarray:
+        xx = np.ascontiguousarray(x).reshape(-1)
+        n, nb = xx.size, xx.size // 256
+        out = np.zeros(max(nb * self.IQ1S_BYTES, 1), np.uint8)
+        if self.lib.iqo_iq1s_quantize(_ptr(xx), dtype, n, _ptr(self._iq1_grid(grid)), _ptr(out), 0, nb) != 0:
+            raise ValueError("oracle iq1s_quantize rejected its arguments")
+        return out[:nb * self.IQ1S_BYTES]
+
+    def iq1s_dequantize(self, blocks: np.ndarray, grid: np.ndarray, n: int, dtype: int = F32) -> np.ndarray:
+        b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(-1)
+        out = np.zeros(max(n, 1), np.float32 if dtype == F32 else np.uint16)
+        if self.lib.iqo_iq1s_dequantize(_ptr(b), _ptr(self._iq1_grid(grid)), n, dtype, _ptr(out)) != 0:
+            raise ValueError("oracle iq1s_dequantize rejected its arguments")
+        return out[:n]
+
 
 def default_threads() -> int:
     """Host threads for the range-split entry points: the CPU count, at most 16."""
@@ -399,6 +439,18 @@ class ParallelOracle(Oracle):
         if any(c < 0 for c in counts):
             raise ValueError("oracle iq2xs_quantize rejected its arguments")
         return out[:nb * self.IQ2XS_BYTES], int(sum(counts))
+
+    def iq1s_quantize(self, x: np.ndarray, dtype: int, grid: np.ndarray) -> np.ndarray:
+        xx = np.ascontiguousarray(x).reshape(-1)
+        n, nb = xx.size, xx.size // 256
+        g = self._iq1_grid(grid)
+        out = np.zeros(max(nb * self.IQ1S_BYTES, 1), np.uint8)
+        lib = self.lib
+
+        def job(b0, b1):
+            return lambda: lib.iqo_iq1s_quantize(_ptr(xx), dtype, n, _ptr(g), _ptr(out), b0, b1)
+        _run_all([job(b0, b1) for b0, b1 in self._parts(nb)], self.threads)
+        return out[:nb * self.IQ1S_BYTES]
 
     def nested_stats(self, absmax: np.ndarray, table2: np.ndarray, blocksize2: int = 256):
         """mean (one call over the whole array), then q2 / absmax2 over ranges of groups."""

@@ -639,3 +639,160 @@ int iqo_iq2xs_dequantize(const uint8_t* blocks, const uint8_t* grid, int64_t n, 
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------------------------ */
+/* IQ1_S-style encoding and its decoding ("[OMNIML-5899] Add CUDA kernels for IQ packing", */
+/* Model-Optimizer PR 2448: the Summary, "Provenance" (16.875 = 15 x (1 + 1/8), 0.61, the   */
+/* 0.125 delta), the review items "Wire format", "Scale anchors", "Search equivalence", the */
+/* round-3 "IQ1_S shifted objective" item and the reply on the shared helpers (qsum, the   */
+/* 8*delta^2 term)).                                                                        */
+/*                                                                                        */
+/* Superblock: 256 consecutive elements, 50 bytes:                                        */
+/*   bytes 0-1   binary16 scale d (little-endian);                                        */
+/*   bytes 2-33  qs[v] = the low 8 bits of vector v's 11-bit grid entry;                   */
+/*   bytes 34-49 8 little-endian 16-bit words qh[b], one per 32-element sub-block b (vectors */
+/*               4b .. 4b+3): bits 3l..3l+2 the high 3 bits of vector 4b+l's entry, bits    */
+/*               12-14 the local scale ls, bit 15 the delta sign (set: delta = -1/8).       */
+/* Decoded element j of vector v: fl32(d * (2 ls + 1) * fl32(g_j + delta)), g = the grid's  */
+/* signed byte (the IQ1_S grid is ternary: -1, 0, +1, where the product is exact).          */
+/* The grid (2048 entries of 8 signed bytes) is the caller's: the pages do not hold it.    */
+/*                                                                                        */
+/* Readings (restated where used):                                                        */
+/*  J1 non-finite elements read as +0.0 (as I1).                                           */
+/*  J2 the scale: amax = the largest |x| over the superblock (from +0), then              */
+/*     d = RN16(fl32(fl32(amax / 16.875) * 0.61)), saturated to the largest finite binary16;  */
+/*     a d with no magnitude bits gives the all-zero superblock.                            */
+/*  J3 a vector's error for entry e and choice (ls, sign), dl = d * (2 ls + 1) (exact),     */
+/*     delta = +-1/8: xn = fma-chain sum of x_j^2, dot = fma-chain sum of x_j * g_j, xsum =   */
+/*     fma-chain sum of x_j * 1 (all j ascending from +0); sdot = fma(delta, xsum, dot);     */
+/*     snorm = qn + 2 delta qs + 8 delta^2 (qn = sum g^2, qs = sum g: exact);              */
+/*     error = max(fma(dl * dl, snorm, fma(-2 dl, sdot, xn)), 0).                           */
+/*  J4 each sub-block takes the choice c = ls + 8 * sign (0..15) of least summed error over  */
+/*     its four vectors (sums in vector order; equal sums: the lower c), then each vector  */
+/*     the entry of least error at that choice (equal errors: the lower entry).            */
+/* ------------------------------------------------------------------------------------ */
+
+enum { IQ1_ENTRIES = 2048, IQ1_BYTES = 50 };
+
+/* J2: the superblock scale from its largest magnitude. */
+uint16_t iqo_iq1s_scale(float amax) {
+  float d = (amax / 16.875f) * 0.61f;
+  uint16_t h = bqo_f32_to_f16(d);
+  if ((h & 0x7c00) == 0x7c00) h = 0x7bff; /* saturate (amax is finite and >= 0) */
+  return h;
+}
+
+static float iq1_error(float xn, float dot, float xsum, float qn, float qs, float dl, float delta) {
+  float sdot = fmaf(delta, xsum, dot);
+  float snorm = qn + 2.0f * delta * qs + 8.0f * delta * delta; /* exact */
+  return fmaxf(fmaf(dl * dl, snorm, fmaf(-2.0f * dl, sdot, xn)), 0.0f);
+}
+
+/* Least error of a vector over the grid at choice (dl, delta); *entry gets the lowest index. */
+static float iq1_best_entry(const float* x, float xn, float xsum, const int8_t* grid, float dl, float delta,
+                            int* entry) {
+  float best = 0.0f;
+  for (int e = 0; e < IQ1_ENTRIES; ++e) {
+    const int8_t* g = grid + IQ_VEC * e;
+    float dot = 0.0f, qn = 0.0f, qs = 0.0f;
+    for (int j = 0; j < IQ_VEC; ++j) {
+      dot = fmaf(x[j], (float)g[j], dot);
+      qn += (float)g[j] * (float)g[j];
+      qs += (float)g[j];
+    }
+    float err = iq1_error(xn, dot, xsum, qn, qs, dl, delta);
+    if (e == 0 || err < best) {
+      best = err;
+      *entry = e;
+    }
+  }
+  return best;
+}
+
+/* Encodes one superblock of 256 binary32 values. */
+void iqo_iq1s_encode_block(const float* x_in, const int8_t* grid, uint8_t* out) {
+  float x[IQ_BLOCK], amax = 0.0f;
+  for (int i = 0; i < IQ_BLOCK; ++i) {
+    x[i] = isfinite(x_in[i]) ? x_in[i] : 0.0f; /* J1 */
+    amax = fmaxf(amax, fabsf(x[i]));
+  }
+  memset(out, 0, IQ1_BYTES);
+  const uint16_t d_bits = iqo_iq1s_scale(amax);
+  if ((d_bits & 0x7fff) == 0) return; /* J2: zero superblock */
+  const float d = bqo_f16_to_f32(d_bits);
+  out[0] = (uint8_t)(d_bits & 0xff);
+  out[1] = (uint8_t)(d_bits >> 8);
+  for (int b = 0; b < 8; ++b) {
+    float xn[4], xsum[4];
+    for (int l = 0; l < 4; ++l) {
+      const float* v = x + 32 * b + 8 * l;
+      xn[l] = 0.0f;
+      xsum[l] = 0.0f;
+      for (int j = 0; j < IQ_VEC; ++j) {
+        xn[l] = fmaf(v[j], v[j], xn[l]);
+        xsum[l] = fmaf(v[j], 1.0f, xsum[l]);
+      }
+    }
+    int best_c = 0;
+    float best_sum = 0.0f;
+    for (int c = 0; c < 16; ++c) { /* J4 */
+      const float dl = d * (float)(2 * (c & 7) + 1), delta = (c & 8) ? -0.125f : 0.125f;
+      float sum = 0.0f;
+      for (int l = 0; l < 4; ++l) {
+        int e;
+        sum += iq1_best_entry(x + 32 * b + 8 * l, xn[l], xsum[l], grid, dl, delta, &e);
+      }
+      if (c == 0 || sum < best_sum) {
+        best_sum = sum;
+        best_c = c;
+      }
+    }
+    const float dl = d * (float)(2 * (best_c & 7) + 1), delta = (best_c & 8) ? -0.125f : 0.125f;
+    uint32_t qh = (uint32_t)(best_c & 7) << 12 | (uint32_t)(best_c >> 3) << 15;
+    for (int l = 0; l < 4; ++l) {
+      int e = 0;
+      iq1_best_entry(x + 32 * b + 8 * l, xn[l], xsum[l], grid, dl, delta, &e);
+      out[2 + 4 * b + l] = (uint8_t)(e & 0xff);
+      qh |= (uint32_t)(e >> 8) << (3 * l);
+    }
+    out[34 + 2 * b] = (uint8_t)(qh & 0xff);
+    out[35 + 2 * b] = (uint8_t)(qh >> 8);
+  }
+}
+
+/* Superblocks [b_lo, b_hi) of an n-element input of `dtype` (n a multiple of 256). */
+int iqo_iq1s_quantize(const void* in, int dtype, int64_t n, const int8_t* grid, uint8_t* out, int64_t b_lo,
+                      int64_t b_hi) {
+  if (dtype != BQO_F32 && dtype != BQO_F16 && dtype != BQO_BF16) return -1;
+  if (n < 0 || n % IQ_BLOCK != 0 || b_lo < 0 || b_hi > n / IQ_BLOCK) return -1;
+  float x[IQ_BLOCK];
+  for (int64_t b = b_lo; b < b_hi; ++b) {
+    for (int i = 0; i < IQ_BLOCK; ++i) x[i] = load_elem(in, dtype, b * IQ_BLOCK + i);
+    iqo_iq1s_encode_block(x, grid, out + b * IQ1_BYTES);
+  }
+  return 0;
+}
+
+/* Decodes n/256 superblocks to `dtype`: fl32(fl32(d * (2 ls + 1)) * fl32(g + delta)), both
+ * inner values exact, then rounded once (R10). */
+int iqo_iq1s_dequantize(const uint8_t* blocks, const int8_t* grid, int64_t n, int dtype, void* out) {
+  if (dtype != BQO_F32 && dtype != BQO_F16 && dtype != BQO_BF16) return -1;
+  if (n < 0 || n % IQ_BLOCK != 0) return -1;
+  for (int64_t b = 0; b < n / IQ_BLOCK; ++b) {
+    const uint8_t* blk = blocks + b * IQ1_BYTES;
+    const float d = bqo_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));
+    for (int sb = 0; sb < 8; ++sb) {
+      const int qh = blk[34 + 2 * sb] | (blk[35 + 2 * sb] << 8);
+      const float dl = d * (float)(2 * ((qh >> 12) & 7) + 1);
+      const float delta = (qh & 0x8000) ? -0.125f : 0.125f;
+      for (int l = 0; l < 4; ++l) {
+        const int e = blk[2 + 4 * sb + l] | (((qh >> (3 * l)) & 7) << 8);
+        for (int j = 0; j < IQ_VEC; ++j) {
+          const float y = (float)grid[IQ_VEC * e + j] + delta;
+          store_elem(out, dtype, b * IQ_BLOCK + 32 * sb + 8 * l + j, dl * y);
+        }
+      }
+    }
+  }
+  return 0;
+}

@@ -1003,4 +1003,158 @@ def pin_iq2xs_decode_random(o):
                           t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
 
 
+# ------------------------------------------------------------------------------------------
+# IQ1_S-style encoding ('[OMNIML-5899] Add CUDA kernels for IQ packing')
+# ------------------------------------------------------------------------------------------
+
+def _iq1_grid(rng) -> np.ndarray:
+    """2048 distinct ternary entries (signed bytes -1, 0, +1), entry 0 all zero."""
+    rows, out = {(0,) * 8}, [(0,) * 8]
+    while len(out) < 2048:
+        r = tuple(int(v) for v in rng.integers(-1, 2, size=8))
+        if r not in rows:
+            rows.add(r)
+            out.append(r)
+    return np.array(out, np.int8)
+
+
+def _iq1_fields(block: np.ndarray):
+    """(d bits, entry per vector, ls per sub-block, delta sign per sub-block) of 50 bytes."""
+    b = [int(v) for v in block]
+    qh = [b[34 + 2 * k] | (b[35 + 2 * k] << 8) for k in range(8)]
+    entries = [b[2 + v] | (((qh[v // 4] >> (3 * (v % 4))) & 7) << 8) for v in range(32)]
+    return b[0] | (b[1] << 8), entries, [(h >> 12) & 7 for h in qh], [h >> 15 for h in qh]
+
+
+def pin_iq1s_scale_rule(o):
+    """d = RN16(fl32(fl32(amax / 16.875) * 0.61)), saturated: the hand-worked values of
+    tests/golden/iq1s_decode.json, and random maxima against numpy's binary32 arithmetic and
+    binary16 rounding."""
+    for amax, bits in _golden("iq1s_decode.json")["scales"]:
+        assert o.iq1s_scale(float(amax)) == int(bits, 16), amax
+    rng = _rng(81)
+    amaxes = np.float32(np.exp(rng.uniform(-20, 14, 100000)))
+    with np.errstate(over="ignore"):
+        want = ((amaxes / np.float32(16.875)) * np.float32(0.61)).astype(np.float16)
+    bits = np.where(np.isfinite(want), want.view(np.uint16), np.uint16(0x7BFF))
+    got = np.array([o.iq1s_scale(a) for a in amaxes], np.uint16)
+    bad = np.nonzero(got != bits)[0]
+    assert bad.size == 0, [(float(amaxes[i]), hex(got[i]), hex(bits[i])) for i in bad[:4]]
+    assert o.iq1s_scale(13.832) == 0x3800  # d = 0.5: used by the exact search below
+
+
+def pin_iq1s_exact_search(o):
+    """The element 13.832 (in sub-block 0) makes d = 0.5; sub-blocks 1-7 hold multiples of 1/16
+    of magnitude <= 5, so every binary32 step of their search is exact.  The test decodes every
+    candidate -- 16 choices (ls, delta sign) x 2048 entries -- sums squared differences in
+    integers (units of 1/256) and requires the least group error with the lowest choice
+    c = ls + 8 sign, then each vector's lowest entry of least error.  Sub-block 2 is zero (ls 0,
+    the two delta signs tie: the + sign wins); sub-block 3 is an exact fit of ls 2, delta -1/8,
+    entry 5, whose duplicate is entry 1500; sub-block 7 is sensitive to the 8 delta^2 term of the
+    shifted norm."""
+    rng = _rng(82)
+    grid = _iq1_grid(rng)
+    grid[1500] = grid[5]
+    x = (rng.integers(-80, 81, size=256) / 16.0).astype(np.float32)  # best ls mid-range
+    x[0] = 13.832
+    x[64:96] = 0.0
+    fit = 0.5 * 5 * (grid[5].astype(np.float64) - 0.125)
+    x[96:128] = np.tile(fit, 4).astype(np.float32)
+    # sub-block 7: data whose best choice (ls 2) beats ls 3 by less than the 8 delta^2 term of
+    # the shifted norm moves them (found by this test's own decoding brute force)
+    x[224:256] = (np.random.default_rng(24).integers(-80, 81, size=32) / 16.0).astype(np.float32)
+    block = o.iq1s_encode_block(x, grid)
+    d_bits, entries, ls, sign = _iq1_fields(block)
+    assert d_bits == 0x3800
+    G = grid.astype(np.int64)
+    for b in range(1, 8):
+        X = np.round(x[32 * b:32 * b + 32].astype(np.float64) * 16).astype(np.int64).reshape(4, 8)
+        E = np.zeros((16, 4), np.int64)
+        first = np.zeros((16, 4), np.int64)
+        for c in range(16):
+            S, sg = 2 * (c & 7) + 1, (-1 if c >= 8 else 1)
+            dec = S * (8 * G + sg)  # 16 * 0.5 * S * (g + sg/8)
+            for l in range(4):
+                err = ((X[l][None, :] - dec) ** 2).sum(axis=1)
+                E[c, l] = err.min()
+                first[c, l] = int(np.argmax(err == err.min()))
+        tot = E.sum(axis=1)
+        cstar = int(np.argmax(tot == tot.min()))
+        assert ls[b] == cstar & 7 and sign[b] == cstar >> 3, (b, ls[b], sign[b], cstar, tot)
+        for l in range(4):
+            assert entries[4 * b + l] == first[cstar, l], (b, l, entries[4 * b + l], first[cstar, l])
+    assert ls[2] == 0 and sign[2] == 0 and entries[8:12] == [0, 0, 0, 0]
+    assert entries[12:16] == [5, 5, 5, 5] and ls[3] == 2 and sign[3] == 1
+
+
+def pin_iq1s_special_inputs(o):
+    """A zero superblock encodes to 50 zero bytes; NaN and infinite elements encode as zeros;
+    fp32, fp16 and bf16 copies of the same values encode identically; a block whose scale
+    saturates still encodes (d = 65504)."""
+    rng = _rng(83)
+    grid = _iq1_grid(rng)
+    assert not o.iq1s_encode_block(np.zeros(256, np.float32), grid).any()
+    x = (rng.standard_normal(256) * 0.1).astype(np.float32)
+    y = x.copy()
+    for i, v in ((3, np.nan), (40, np.inf), (41, -np.inf)):
+        y[i] = v
+        x[i] = 0.0
+    assert np.array_equal(o.iq1s_encode_block(x, grid), o.iq1s_encode_block(y, grid))
+    z = (rng.integers(-64, 65, size=512) / 8.0).astype(np.float32)
+    ref = o.iq1s_quantize(z, oracle.F32, grid)
+    assert np.array_equal(o.iq1s_quantize(z.astype(np.float16).view(np.uint16), oracle.F16, grid), ref)
+    bf = torch.from_numpy(z).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(o.iq1s_quantize(bf, oracle.BF16, grid), ref)
+    big = o.iq1s_encode_block(x * np.float32(1e10), grid)
+    assert big[0] == 0xFF and big[1] == 0x7B
+
+
+def pin_iq1s_decode_golden(o):
+    """The hand-worked superblock of tests/golden/iq1s_decode.json decodes to its values."""
+    gd = _golden("iq1s_decode.json")
+    grid = np.array([gd["grid_default"]] * 2048, np.int8)
+    for e, row in gd["grid_entries"].items():
+        grid[int(e)] = row
+    block = np.zeros(50, np.uint8)
+    d = int(gd["d_bits"], 16)
+    block[0], block[1] = d & 0xFF, d >> 8
+    for v, q in gd["qs"].items():
+        block[2 + int(v)] = int(q, 16)
+    for k, h in gd["qh"].items():
+        h = int(h, 16)
+        block[34 + 2 * int(k)], block[35 + 2 * int(k)] = h & 0xFF, h >> 8
+    want = np.full(256, gd["vector_default"], np.float32)
+    for v, vals in gd["vectors"].items():
+        want[8 * int(v):8 * int(v) + 8] = vals
+    assert np.array_equal(o.iq1s_dequantize(block, grid, 256, oracle.F32), want)
+    assert np.array_equal(o.iq1s_dequantize(block, grid, 256, oracle.F16).view(np.float16).astype(np.float32), want)
+
+
+def pin_iq1s_decode_random(o):
+    """Random payloads (finite d) decode to fl32(d (2 ls + 1) (g + delta)) computed in binary64
+    from the byte layout here (exact for ternary grids; one rounding otherwise), and to torch's
+    round-to-nearest-even of it in fp16 and bf16, for a ternary and an arbitrary int8 grid."""
+    rng = _rng(84)
+    blocks = rng.integers(0, 256, size=(5, 50)).astype(np.uint8)
+    for k in range(5):
+        blocks[k, 1] &= 0x7B
+    for grid in (_iq1_grid(rng), rng.integers(-128, 128, size=(2048, 8)).astype(np.int8)):
+        want = []
+        for k in range(5):
+            d_bits, entries, ls, sign = _iq1_fields(blocks[k])
+            d = float(np.uint16(d_bits).view(np.float16))
+            for v in range(32):
+                dl = d * (2 * ls[v // 4] + 1)
+                delta = -0.125 if sign[v // 4] else 0.125
+                want += [float(np.float32(dl * (int(g) + delta))) for g in grid[entries[v]]]
+        want = np.array(want, np.float64)
+        got = o.iq1s_dequantize(blocks, grid, 5 * 256, oracle.F32)
+        assert np.array_equal(got.astype(np.float64), want)
+        t = torch.from_numpy(want.astype(np.float32))
+        assert np.array_equal(o.iq1s_dequantize(blocks, grid, 5 * 256, oracle.BF16),
+                              t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+        assert np.array_equal(o.iq1s_dequantize(blocks, grid, 5 * 256, oracle.F16),
+                              t.to(torch.float16).view(torch.int16).numpy().view(np.uint16))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

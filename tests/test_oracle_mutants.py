@@ -66,6 +66,22 @@ MUTANTS = {
     "iq_negative_zero_rejected": ("if ((d_bits & 0x7fff) == 0) return 0;", "if (d_bits == 0) return 0;"),
     "iq_group_of_one_vector": ("+ iq_best_entry(&vec[2 * g + 1], grid, s, &e1);", "; (void)e1;"),
     "iq_error_sign_flipped": ("fmaf(-2.0f * s, dot, xn)", "fmaf(2.0f * s, dot, xn)"),
+    "iq1_scale_order": ("float d = (amax / 16.875f) * 0.61f;", "float d = (amax * 0.61f) / 16.875f;"),
+    "iq1_scale_not_saturated": ("if ((h & 0x7c00) == 0x7c00) h = 0x7bff;", ""),
+    "iq1_choice_ties_to_higher": ("if (c == 0 || sum < best_sum)", "if (c == 0 || sum <= best_sum)"),
+    "iq1_entry_ties_to_higher": ("float err = iq1_error(xn, dot, xsum, qn, qs, dl, delta);\n    if (e == 0 || err < best)",
+                                 "float err = iq1_error(xn, dot, xsum, qn, qs, dl, delta);\n    if (e == 0 || err <= best)"),
+    "iq1_delta_sign_inverted": ("float sdot = fmaf(delta, xsum, dot);", "float sdot = fmaf(-delta, xsum, dot);"),
+    "iq1_no_delta_square_term": ("float snorm = qn + 2.0f * delta * qs + 8.0f * delta * delta;",
+                                 "float snorm = qn + 2.0f * delta * qs;"),
+    "iq1_first_vector_only": ("sum += iq1_best_entry(", "if (l == 0) sum += iq1_best_entry("),
+    "iq1_high_bits_shifted": ("qh |= (uint32_t)(e >> 8) << (3 * l);", "qh |= (uint32_t)(e >> 8) << (3 * l + 1);"),
+    "iq1_scale_bits_at_11": ("uint32_t qh = (uint32_t)(best_c & 7) << 12", "uint32_t qh = (uint32_t)(best_c & 7) << 11"),
+    "iq1_nonfinite_kept": ("x[i] = isfinite(x_in[i]) ? x_in[i] : 0.0f; /* J1 */", "x[i] = x_in[i];"),
+    "iq1_decode_delta_inverted": ("const float delta = (qh & 0x8000) ? -0.125f : 0.125f;",
+                                  "const float delta = (qh & 0x8000) ? 0.125f : -0.125f;"),
+    "iq1_decode_even_scale": ("const float dl = d * (float)(2 * ((qh >> 12) & 7) + 1);",
+                              "const float dl = d * (float)(2 * ((qh >> 12) & 7) + 2);"),
 }
 
 
