@@ -54,7 +54,8 @@ MUTANTS = {
     "iq_flip_strongest": ("      if (p < w) {", "      if (p > w) {"),
     "iq_no_parity_correction": ("    dot = fmaf(-2.0f, w, dot);\n", ""),
     "iq_scale_ties_to_higher": ("if (l == 0 || sum < best_sum)", "if (l == 0 || sum <= best_sum)"),
-    "iq_entry_ties_to_higher": ("if (e == 0 || err < best)", "if (e == 0 || err <= best)"),
+    "iq_entry_ties_to_higher": ("iq_entry_qnorm(q), s);\n    if (e == 0 || err < best)",
+                                "iq_entry_qnorm(q), s);\n    if (e == 0 || err <= best)"),
     "iq_sign_bits_at_8": ("(uint16_t)(e | ((signs & 0x7f) << 9))", "(uint16_t)(e | ((signs & 0x7f) << 8))"),
     "iq_scale_nibbles_swapped": ("(uint8_t)(ls[2 * i] | (ls[2 * i + 1] << 4))", "(uint8_t)(ls[2 * i + 1] | (ls[2 * i] << 4))"),
     "iq_local_scale_even": ("float s = d * (float)(2 * l + 1) * 0.125f; /* I4 */", "float s = d * (float)(2 * l + 2) * 0.125f; /* I4 */"),
