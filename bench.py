@@ -461,7 +461,7 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak (FMA = 2 flops, dual-
 
 
 def iq2xs(bq, synth, torch, dev, rows=4096, cols=14336, sets=4):
-    """The IQ2_XS-style encoder and decoder on a 4096 x 14336 bf16 weight (229,376
+    """The IQ2_XS- and IQ1_S-style encoders and decoders on a 4096 x 14336 bf16 weight (229,376
     superblocks).  The encoder is a search bound by VALU issue: its algorithmic work per
     superblock is 32 vectors x 512 entries x (an 8-term dot, 8 FMA, plus 2 FMA of the error
     for each of the 16 local scales), 1,310,720 flops counting an FMA as two, reported against
@@ -488,13 +488,38 @@ def iq2xs(bq, synth, torch, dev, rows=4096, cols=14336, sets=4):
     d_ms = statistics.median(time_calls(dec, torch, 8) for _ in range(ROUNDS))
     flops = nb * 32 * 512 * (16 + 16 * 4)
     dec_bytes = nb * 74 + 2 * n
-    return {"iq2xs encode bf16 4096x14336 (search over a 512-entry grid)": dict(
-                us=round(e_ms * 1e3, 1), superblocks_per_s=round(nb / e_ms * 1e3, 1),
-                tflops=round(flops / e_ms / 1e9, 1),
-                pct_fp32_vector_peak=round(100 * flops / e_ms / 1e9 / FP32_VECTOR_PEAK_TFLOPS, 1)),
-            "iq2xs decode to bf16 4096x14336": dict(
-                us=round(d_ms * 1e3, 2), rw_gbs=round(dec_bytes / d_ms / 1e6, 1),
-                pct_hbm_peak=round(100 * dec_bytes / d_ms / 1e6 / PEAK_GBS, 1))}
+    out = {"iq2xs encode bf16 4096x14336 (search over a 512-entry grid)": dict(
+               us=round(e_ms * 1e3, 1), superblocks_per_s=round(nb / e_ms * 1e3, 1),
+               tflops=round(flops / e_ms / 1e9, 1),
+               pct_fp32_vector_peak=round(100 * flops / e_ms / 1e9 / FP32_VECTOR_PEAK_TFLOPS, 1)),
+           "iq2xs decode to bf16 4096x14336": dict(
+               us=round(d_ms * 1e3, 2), rw_gbs=round(dec_bytes / d_ms / 1e6, 1),
+               pct_hbm_peak=round(100 * dec_bytes / d_ms / 1e6 / PEAK_GBS, 1))}
+    # IQ1_S-style: 32 vectors x 2048 entries x (an 8-term dot, 8 FMA; two shifted dots, 2 FMA;
+    # 2 FMA of the error for each of the 16 choices) per superblock, FMA = 2 flops.
+    grid1 = torch.from_numpy(synth.iq1s_grid().reshape(-1)).to(dev)
+    blocks1 = torch.empty(nb * 50, dtype=torch.uint8, device=dev)
+
+    def enc1():
+        bq.check(bq.bq_iq1s_quantize(x, bq.BQ_BF16, n, cols, grid1, blocks1), "iq1s quantize")
+    i[0] = 0
+
+    def dec1():
+        o = outs[i[0] % sets]
+        i[0] += 1
+        bq.check(bq.bq_iq1s_dequantize(blocks1, grid1, n, cols, bq.BQ_BF16, o), "iq1s dequantize")
+    enc1()
+    e1_ms = statistics.median(time_calls(enc1, torch, 2) for _ in range(ROUNDS))
+    d1_ms = statistics.median(time_calls(dec1, torch, 8) for _ in range(ROUNDS))
+    flops1 = nb * 32 * 2048 * (16 + 4 + 16 * 4)
+    dec1_bytes = nb * 50 + 2 * n
+    out["iq1s encode bf16 4096x14336 (search over a 2048-entry grid)"] = dict(
+        us=round(e1_ms * 1e3, 1), superblocks_per_s=round(nb / e1_ms * 1e3, 1), tflops=round(flops1 / e1_ms / 1e9, 1),
+        pct_fp32_vector_peak=round(100 * flops1 / e1_ms / 1e9 / FP32_VECTOR_PEAK_TFLOPS, 1))
+    out["iq1s decode to bf16 4096x14336"] = dict(
+        us=round(d1_ms * 1e3, 2), rw_gbs=round(dec1_bytes / d1_ms / 1e6, 1),
+        pct_hbm_peak=round(100 * dec1_bytes / d1_ms / 1e6 / PEAK_GBS, 1))
+    return out
 
 
 def loading_pipeline(bq, synth, torch, dev, table, chunks=8, chunk=1 << 25, B=64):
@@ -669,6 +694,12 @@ def main():
             bq.check(bq.bq_iq2xs_quantize(x6, bq.BQ_BF16, n6, cols6, g6, s6, b6, r6), "iq2xs quantize")
         for _ in range(3):
             bq.check(bq.bq_iq2xs_dequantize(b6, g6, n6, cols6, bq.BQ_BF16, o6), "iq2xs dequantize")
+        g7 = torch.from_numpy(synth.iq1s_grid().reshape(-1)).to(dev)
+        b7 = torch.empty(n6 // 256 * 50, dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            bq.check(bq.bq_iq1s_quantize(x6, bq.BQ_BF16, n6, cols6, g7, b7), "iq1s quantize")
+        for _ in range(3):
+            bq.check(bq.bq_iq1s_dequantize(b7, g7, n6, cols6, bq.BQ_BF16, o6), "iq1s dequantize")
         del x6, o6
         src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
         dst = torch.empty_like(src)

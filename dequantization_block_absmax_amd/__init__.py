@@ -22,7 +22,8 @@ BQ_Q32_Q4, BQ_Q32_Q8 = 0, 1
  BQ_ERR_FORMAT, BQ_ERR_WORKSPACE, BQ_ERR_HIP) = range(10)
 
 EXPORTS = ("bq_quantize_blockwise", "bq_dequantize_blockwise", "bq_quantize_nested",
-           "bq_dequantize_nested", "bq_dequant_q32", "bq_iq2xs_quantize", "bq_iq2xs_dequantize", "bq_nested_workspace_bytes", "bq_status_string",
+           "bq_dequantize_nested", "bq_dequant_q32", "bq_iq2xs_quantize", "bq_iq2xs_dequantize",
+           "bq_iq1s_quantize", "bq_iq1s_dequantize", "bq_nested_workspace_bytes", "bq_status_string",
            "bq_debug_nearest_codes", "bq_last_hip_error", "bq_linear_blockwise", "bq_gemm_blockwise",
            "bq_debug_time_next_kernel", "bq_quantize_nested_noalloc")
 
@@ -69,6 +70,8 @@ def _load() -> ctypes.CDLL:
         "bq_dequant_q32": [vp, st, i64, i32, st, vp, vp],
         "bq_iq2xs_quantize": [vp, st, i64, i64, vp, vp, vp, vp, vp],
         "bq_iq2xs_dequantize": [vp, vp, i64, i64, st, vp, vp],
+        "bq_iq1s_quantize": [vp, st, i64, i64, vp, vp, vp],
+        "bq_iq1s_dequantize": [vp, vp, i64, i64, st, vp, vp],
         "bq_linear_blockwise": [vp, st, i64, i64, i64, i32, tp, vp, vp, vp, vp],
         "bq_gemm_blockwise": [vp, st, i64, i64, i64, i32, tp, vp, vp, vp, vp],
     }
@@ -202,6 +205,16 @@ def bq_iq2xs_quantize(x, dtype, n: int, row_len: int, grid, scales, blocks, reje
 def bq_iq2xs_dequantize(blocks, grid, n: int, row_len: int, dtype, out, stream=None) -> int:
     return _lib.bq_iq2xs_dequantize(_addr(blocks), _addr(grid), int(n), int(row_len), dtype_code(dtype), _addr(out),
                                     _stream(stream))
+
+
+def bq_iq1s_quantize(x, dtype, n: int, row_len: int, grid, blocks, stream=None) -> int:
+    return _lib.bq_iq1s_quantize(_addr(x), dtype_code(dtype), int(n), int(row_len), _addr(grid), _addr(blocks),
+                                 _stream(stream))
+
+
+def bq_iq1s_dequantize(blocks, grid, n: int, row_len: int, dtype, out, stream=None) -> int:
+    return _lib.bq_iq1s_dequantize(_addr(blocks), _addr(grid), int(n), int(row_len), dtype_code(dtype), _addr(out),
+                                   _stream(stream))
 
 
 def bq_linear_blockwise(x, dtype, M: int, K: int, N: int, blocksize: int, table, absmax, packed, y,

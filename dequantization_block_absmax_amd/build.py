@@ -25,7 +25,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math", "
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 SOURCES = ["bq_api.cpp", "bq_table.cpp", "k_quant.hip", "k_dequant.hip", "k_nested.hip", "k_q32.hip",
-           "k_linear.hip", "k_gemm.hip", "k_scratch.hip", "k_iq2xs.hip"]
+           "k_linear.hip", "k_gemm.hip", "k_scratch.hip", "k_iq2xs.hip",
+           "k_iq1s.hip"]
 
 
 def _cmd(src: str, obj: str) -> list[str]:

@@ -329,7 +329,7 @@ bq_status bq_dequant_q32(const void* blocks, bq_dtype dtype, int64_t n, int32_t 
   return hip_status(bq::launch_q32(blocks, dtype, n, (int)format, out, stream));
 }
 
-static bq_status check_iq2xs_shape(bq_dtype dtype, int64_t n, int64_t row_len) {
+static bq_status check_superblock_shape(bq_dtype dtype, int64_t n, int64_t row_len) {
   if (!valid_dtype(dtype)) return BQ_ERR_DTYPE;
   if (row_len <= 0 || row_len % 256 != 0) return BQ_ERR_FORMAT;
   if (n < 0 || n % row_len != 0 || n / 256 > INT32_MAX) return BQ_ERR_SIZE;
@@ -338,7 +338,7 @@ static bq_status check_iq2xs_shape(bq_dtype dtype, int64_t n, int64_t row_len) {
 
 bq_status bq_iq2xs_quantize(const void* in, bq_dtype dtype, int64_t n, int64_t row_len, const uint8_t* grid,
                             const uint16_t* scales, uint8_t* blocks, uint32_t* rejected, hipStream_t stream) {
-  const bq_status st = check_iq2xs_shape(dtype, n, row_len);
+  const bq_status st = check_superblock_shape(dtype, n, row_len);
   if (st != BQ_OK || n == 0) return st;
   if (in == nullptr || grid == nullptr || scales == nullptr || blocks == nullptr || rejected == nullptr)
     return BQ_ERR_NULL;
@@ -347,9 +347,27 @@ bq_status bq_iq2xs_quantize(const void* in, bq_dtype dtype, int64_t n, int64_t r
   return hip_status(bq::launch_iq2xs_quantize(in, dtype, n, grid, scales, blocks, rejected, stream));
 }
 
+bq_status bq_iq1s_quantize(const void* in, bq_dtype dtype, int64_t n, int64_t row_len, const int8_t* grid,
+                           uint8_t* blocks, hipStream_t stream) {
+  const bq_status st = check_superblock_shape(dtype, n, row_len);
+  if (st != BQ_OK || n == 0) return st;
+  if (in == nullptr || grid == nullptr || blocks == nullptr) return BQ_ERR_NULL;
+  if (!aligned(in, 16) || !aligned(grid, 16) || !aligned(blocks, 2)) return BQ_ERR_ALIGNMENT;
+  return hip_status(bq::launch_iq1s_quantize(in, dtype, n, grid, blocks, stream));
+}
+
+bq_status bq_iq1s_dequantize(const uint8_t* blocks, const int8_t* grid, int64_t n, int64_t row_len,
+                             bq_dtype dtype, void* out, hipStream_t stream) {
+  const bq_status st = check_superblock_shape(dtype, n, row_len);
+  if (st != BQ_OK || n == 0) return st;
+  if (blocks == nullptr || grid == nullptr || out == nullptr) return BQ_ERR_NULL;
+  if (!aligned(blocks, 2) || !aligned(grid, 8) || !aligned(out, 16)) return BQ_ERR_ALIGNMENT;
+  return hip_status(bq::launch_iq1s_dequantize(blocks, grid, n, dtype, out, stream));
+}
+
 bq_status bq_iq2xs_dequantize(const uint8_t* blocks, const uint8_t* grid, int64_t n, int64_t row_len,
                               bq_dtype dtype, void* out, hipStream_t stream) {
-  const bq_status st = check_iq2xs_shape(dtype, n, row_len);
+  const bq_status st = check_superblock_shape(dtype, n, row_len);
   if (st != BQ_OK || n == 0) return st;
   if (blocks == nullptr || grid == nullptr || out == nullptr) return BQ_ERR_NULL;
   if (!aligned(blocks, 2) || !aligned(grid, 8) || !aligned(out, 16)) return BQ_ERR_ALIGNMENT;

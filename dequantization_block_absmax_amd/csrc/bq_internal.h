@@ -161,6 +161,9 @@ int launch_iq2xs_quantize(const void* in, int dtype, int64_t n, const uint8_t* g
                           uint8_t* blocks, uint32_t* rejected, void* stream);
 int launch_iq2xs_dequantize(const uint8_t* blocks, const uint8_t* grid, int64_t n, int dtype, void* out,
                             void* stream);
+int launch_iq1s_quantize(const void* in, int dtype, int64_t n, const int8_t* grid, uint8_t* blocks, void* stream);
+int launch_iq1s_dequantize(const uint8_t* blocks, const int8_t* grid, int64_t n, int dtype, void* out,
+                           void* stream);
 
 // The library-owned scratch of bq_quantize_nested_noalloc (k_scratch.hip): kScratchBytes per
 // device, 256-byte aligned.  scratch_buffer sets *ptr to the current device's copy (its device

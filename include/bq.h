@@ -65,7 +65,7 @@ typedef enum {
   BQ_ERR_TABLE = 5,     /* code table: size, order, range or spacing (see bq_code_table) */
   BQ_ERR_ALIGNMENT = 6, /* a device pointer is not aligned as required */
   BQ_ERR_FORMAT = 7,    /* unknown bq_q32_format, or row_len not a multiple of 32 (of 256 for
-                           the IQ2_XS-style calls) */
+                           the IQ2_XS- and IQ1_S-style calls) */
   BQ_ERR_WORKSPACE = 8, /* nested workspace missing or smaller than bq_nested_workspace_bytes */
   BQ_ERR_HIP = 9        /* the HIP runtime rejected a launch */
 } bq_status;
@@ -264,6 +264,50 @@ bq_status bq_iq2xs_quantize(const void* in, bq_dtype dtype, int64_t n, int64_t r
  * Errors: as bq_iq2xs_quantize. */
 bq_status bq_iq2xs_dequantize(const uint8_t* blocks, const uint8_t* grid, int64_t n, int64_t row_len,
                               bq_dtype dtype, void* out, hipStream_t stream);
+
+/* IQ1_S-style encoding ("[OMNIML-5899] Add CUDA kernels for IQ packing", Model-Optimizer PR
+ * 2448: "Provenance" (16.875 = 15 x (1 + 1/8), the 0.61 scale predictor, the 0.125 delta), the
+ * review items "Wire format", "Scale anchors" and "Search equivalence", the round-3 item on
+ * the shifted objective).  A superblock is 256 consecutive elements, stored in 50 bytes:
+ *   bytes 0-1   binary16 scale d (little-endian);
+ *   bytes 2-33  byte v = the low 8 bits of vector v's 11-bit grid entry (vector v = elements
+ *               8v .. 8v+7);
+ *   bytes 34-49 8 little-endian 16-bit words, one per 32-element sub-block b (vectors
+ *               4b .. 4b+3): bits 3l..3l+2 the high 3 bits of vector 4b+l's entry, bits 12-14
+ *               the local scale ls, bit 15 the delta sign (set: delta = -1/8, else +1/8).
+ * Element j of vector v decodes to fl32(d * (2 ls + 1) * (g_j + delta)), g the grid's signed
+ * byte (exact for the ternary IQ1_S grid), rounded once to the output type.
+ * The grid is the caller's: 2048 entries of 8 signed bytes (entry e, element j at byte 8e + j),
+ * for the IQ1_S format those of the GGML ternary grid (-1, 0, +1).
+ *
+ * The encoder, per superblock (binary32 throughout, fused multiply-adds where written fma):
+ *   x_j = the element, a NaN or infinite element read as +0;
+ *   d = RN16(fl32(fl32(amax / 16.875) * 0.61)), amax = max |x_j| over the superblock,
+ *   saturated to the largest finite binary16; d = 0 gives an all-zero superblock;
+ *   per vector: xn, dot_e and xsum are fma chains of x_j^2, x_j * g_j and x_j * 1 (j = 0..7,
+ *   from +0); for a choice c = ls + 8 * sign, dl = d * (2 ls + 1), delta = +-1/8:
+ *   error(e, c) = max(fma(dl*dl, sn, fma(-2 dl, fma(delta, xsum, dot_e), xn)), 0),
+ *   sn = qn_e + 2 delta qs_e + 8 delta^2 (qn, qs = sum of g^2 and of g);
+ *   each sub-block takes the choice whose summed error over its four vectors (in vector
+ *   order) is least (equal sums: the lower c), then each vector the entry of least error at
+ *   that choice (equal errors: the lower entry).
+ *   in        [device] n elements of `dtype`, 16-byte aligned.
+ *   n, row_len  row_len a positive multiple of 256 dividing n (n = 0: nothing enqueued).
+ *   grid      [device] 16384 bytes, 16-byte aligned.
+ *   blocks    [device] out: (n / 256) * 50 bytes, 2-byte aligned.
+ * Errors: BQ_ERR_DTYPE, BQ_ERR_FORMAT (row_len), BQ_ERR_SIZE (n negative or not a multiple of
+ * row_len, more than INT32_MAX superblocks), BQ_ERR_NULL, BQ_ERR_ALIGNMENT, BQ_ERR_HIP. */
+bq_status bq_iq1s_quantize(const void* in, bq_dtype dtype, int64_t n, int64_t row_len, const int8_t* grid,
+                           uint8_t* blocks, hipStream_t stream);
+
+/* Decodes n / 256 superblocks laid out as bq_iq1s_quantize writes them (any bytes) to n
+ * elements of `dtype`.
+ *   blocks    [device] (n / 256) * 50 bytes, 2-byte aligned.
+ *   grid      [device] 16384 bytes, 8-byte aligned.
+ *   out       [device] out: n elements of `dtype`, 16-byte aligned.
+ * Errors: as bq_iq1s_quantize. */
+bq_status bq_iq1s_dequantize(const uint8_t* blocks, const int8_t* grid, int64_t n, int64_t row_len,
+                             bq_dtype dtype, void* out, hipStream_t stream);
 
 /* The hipError_t (as int) of the most recent launch that failed on the calling thread with
  * BQ_ERR_HIP, or 0 if none has. */

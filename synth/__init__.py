@@ -174,6 +174,20 @@ def iq2xs_grid(seed: int = 512, alphabet=(8, 25, 43)) -> np.ndarray:
     return np.array(out, np.uint8)
 
 
+def iq1s_grid(seed: int = 2048) -> np.ndarray:
+    """2048 distinct grid entries of 8 signed ternary bytes (-1, 0, +1: the IQ1_S alphabet;
+    the grid itself is the caller's), as a (2048, 8) int8 array."""
+    rows, out, start = set(), [], 0
+    while len(out) < 2048:
+        idx = (_srl(u64(seed, 10, start, 8), 33) % 3).numpy()
+        start += 8
+        r = tuple(int(i) - 1 for i in idx)
+        if r not in rows:
+            rows.add(r)
+            out.append(r)
+    return np.array(out, np.int8)
+
+
 def iq2xs_scales(x: torch.Tensor, ratio: float = 0.8) -> torch.Tensor:
     """A caller's binary16 superblock scales for x (n a multiple of 256): ratio * (largest
     finite |x| of the superblock) / 166.625, 166.625 being the largest decoded magnitude per

@@ -230,6 +230,36 @@ def test_iq2xs_validation():
     assert dec(out=FAKE + 8) == bq.BQ_ERR_ALIGNMENT
 
 
+def test_iq1s_validation():
+    def enc(**kw):
+        args = dict(x=FAKE, dtype=bq.BQ_BF16, n=4096 * 16, row_len=4096, grid=FAKE, blocks=FAKE, stream=0)
+        args.update(kw)
+        return bq.bq_iq1s_quantize(**args)
+
+    def dec(**kw):
+        args = dict(blocks=FAKE, grid=FAKE, n=4096 * 16, row_len=4096, dtype=bq.BQ_BF16, out=FAKE, stream=0)
+        args.update(kw)
+        return bq.bq_iq1s_dequantize(**args)
+
+    for call in (enc, dec):
+        assert call(dtype=3) == bq.BQ_ERR_DTYPE
+        assert call(row_len=384) == bq.BQ_ERR_FORMAT  # rows must hold whole superblocks
+        assert call(row_len=0) == bq.BQ_ERR_FORMAT
+        assert call(n=4096 * 16 + 256) == bq.BQ_ERR_SIZE
+        assert call(n=-4096) == bq.BQ_ERR_SIZE
+        assert call(n=(1 << 31) * 256, row_len=256) == bq.BQ_ERR_SIZE
+        assert call(n=0) == bq.BQ_OK
+        assert call(grid=None) == bq.BQ_ERR_NULL
+        assert call(blocks=None) == bq.BQ_ERR_NULL
+        assert call(blocks=FAKE + 1) == bq.BQ_ERR_ALIGNMENT  # 50-byte records are 2-byte aligned
+    assert enc(x=None) == bq.BQ_ERR_NULL
+    assert dec(out=None) == bq.BQ_ERR_NULL
+    assert enc(x=FAKE + 8) == bq.BQ_ERR_ALIGNMENT
+    assert enc(grid=FAKE + 8) == bq.BQ_ERR_ALIGNMENT
+    assert dec(grid=FAKE + 4) == bq.BQ_ERR_ALIGNMENT
+    assert dec(out=FAKE + 8) == bq.BQ_ERR_ALIGNMENT
+
+
 def test_linear_validation():
     def call(**kw):
         args = dict(x=FAKE, dtype=bq.BQ_BF16, M=2, K=4096, N=14336, blocksize=64, table=T16, absmax=FAKE,
