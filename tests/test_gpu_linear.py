@@ -117,3 +117,44 @@ def test_linear_decode_shape_sampled_rows(dev, o, K_table, M):
     sub_absmax = np.concatenate([absmax[r * (K // B):(r + 1) * (K // B)] for r in rows])
     check_linear_against_oracle(o, y[:, rows], x, "bfloat16", len(rows), B, table, sub_absmax, sub_packed,
                          "decode shape table=%d M=%d" % (K_table, M))
+
+
+# Tall weights with 4-bit codes at M = 3 or 4 take the matrix-core form (at least 32 weight
+# rows per CU: 8192 on MI355X's 256 CUs; K a multiple of 64 up to 4096; blocks of 64 or more):
+# a ragged last tile and run of tiles, waves and lane blocks past K, blocks longer than a row.
+# (8200, 1040, 64) has K % 64 != 0 and takes the vector form.
+MATRIX_CORE_SHAPES = [(8195, 4096, 64), (8200, 1088, 256), (8193, 64, 64), (8196, 3008, 4096), (8200, 1040, 64)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_linear_matrix_core_form(dev, o, dtype):
+    """Seeded random codes and log-normal block maxima (the product reads them as given), every
+    output checked against the oracle within the stated bound."""
+    table = TABLES[16]
+    for i, (N, K, B) in enumerate(MATRIX_CORE_SHAPES):
+        rng = np.random.default_rng(300 + i)
+        packed = rng.integers(0, 256, size=N * K // 2, dtype=np.uint8)
+        absmax = (0.02 * np.exp(rng.standard_normal(-(-N * K // B)))).astype(np.float32)
+        for M in (3, 4):
+            x = activations(M, K, dtype, seed=400 + 10 * i + M)
+            y = run_gpu(dev, x, dtype, N, B, table, absmax, packed)
+            check_linear_against_oracle(o, y, x, dtype, N, B, table, absmax, packed,
+                                        "%s N=%d K=%d B=%d M=%d" % (dtype, N, K, B, M))
+
+
+@pytest.mark.parametrize("M", [3, 4])
+def test_linear_matrix_core_exact(dev, o, M):
+    """The dyadic case of test_linear_exact_when_all_terms_exact on a weight tall enough for the
+    matrix-core form: every product and partial sum is exact, so the result must equal the
+    oracle's exactly (a lane, row or block mixed up in the matrix layout changes it)."""
+    table = np.float32([-1, -0.875, -0.75, -0.625, -0.5, -0.375, -0.25, -0.125, 0, 0.125, 0.25, 0.375,
+                        0.5, 0.625, 0.75, 1])
+    N, K, B = 8196, 2048, 64
+    q = (np.arange(N)[:, None] * 5 + np.arange(K)[None, :] * 3 + np.arange(N)[:, None] // 7) % 16
+    flat = q.reshape(-1)
+    packed = ((flat[0::2] << 4) | flat[1::2]).astype(np.uint8)
+    absmax = np.ldexp(np.float32(1), (np.arange(N * K // B) % 5) - 2).astype(np.float32)
+    x = torch.from_numpy(((np.arange(M * K).reshape(M, K) * 7) % 11 - 5).astype(np.float32)).to(torch.bfloat16)
+    y = run_gpu(dev, x, "bfloat16", N, B, table, absmax, packed)
+    ref = o.linear_blockwise(host_bits(x), oracle.BF16, M, K, N, B, table, absmax, packed)
+    assert np.array_equal(y.astype(np.float64), ref)
