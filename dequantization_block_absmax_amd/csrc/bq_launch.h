@@ -20,6 +20,9 @@
 
 namespace bq {
 
+// Compute units of the current device (queried once per device; 256 if the query fails).
+int cu_count();
+
 // A launch's threads per dimension (workgroups times workgroup size) must fit in 32 bits;
 // larger grids are refused here rather than left to the runtime.
 template <typename... KArgs, typename... Args>

@@ -1,5 +1,6 @@
 // k_gemm.hip -- fused dequantize + GEMM on the gfx950 matrix cores, for batches of rows
-// (gemm_kernel up to 128 rows of x, gemm_tiled_kernel above):
+// (gemm_kernel up to 128 rows of x, gemm_tiled_kernel above, gemm_wide_kernel for the largest
+// grids of 8-bit codes):
 // y = x . W16^T, where W16 = RN16(fl32(c[q] * a)) is exactly the 16-bit tensor that
 // bq_dequantize_blockwise writes for W, formed in registers and never stored (the
 // 16-bit-activation, 4-bit-weight GEMM of "stable-diffusion.cpp PR 2278", Summary, on the
@@ -401,6 +402,143 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint8_t* x, int64
     }
 }
 
+// Large batches, wide form: a 256 x 128 output tile per workgroup (256 rows of x, 128 rows of
+// W), its four waves stacked along x (64 x 128 each: 2 x 4 accumulator tiles).  Each wave
+// loads its own 64 rows of x straight into MFMA fragments (lane group g takes the 32
+// consecutive k from 32 g of its row, MFMA step s the 8 from 32 g + 8 s, and the weight
+// fragments read from LDS follow the same assignment), so x never passes through LDS; only the
+// 16-bit weights do, formed once per workgroup and read by all four waves.  Per 64-k step that
+// is 16 KB of LDS writes and 64 KB of reads for 2 M multiply-adds, against 32 KB and 64 KB for
+// 1 M in the 128 x 128 form.  x is loaded one step ahead.  The kernel is held to two waves per
+// SIMD (242 registers, the accumulators among them): with 128 accumulator registers on top of
+// 172 it ran one wave per SIMD and was slower than the 128 x 128 form.
+constexpr int kWideM = 256;
+constexpr int kWideN = 128;
+
+struct AFrag {
+  u32x4 v[2][4];  // row tile i (32 rows), MFMA step s
+};
+
+template <int KB>
+struct WStage {
+  u32x4 codes[KB == 4 ? 1 : 2];
+  float a;
+};
+
+template <int DT, int KB>
+__global__ __launch_bounds__(256, 2) void gemm_wide_kernel(const uint8_t* x, int64_t M, int64_t K, int64_t N,
+                                                        int log2b, const float* absmax, const uint8_t* packed,
+                                                        float* __restrict__ y, DequantArgs da) {
+  __shared__ float2 s_pair[KB == 4 ? 256 : 1];
+  __shared__ float s_c[KB == 8 ? 256 : 1];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[2][kWideN * kRowPad];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, r = lane & 31;
+  if constexpr (KB == 4) s_pair[tid] = make_float2(da.c[tid >> 4], da.c[tid & 15]);
+  else s_c[tid] = da.c[tid];
+  __syncthreads();
+
+  const int64_t m0 = (int64_t)blockIdx.y * kWideM + 64 * wave;
+  const int64_t n0 = (int64_t)blockIdx.x * kWideN;
+  // x rows of this lane (rows past M read the last row and are never stored)
+  const uint8_t* xrow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) xrow[i] = x + (min(m0 + 32 * i + r, M - 1) * K + 32 * g) * 2;
+  // staging: W row tid / 2 of the tile, k half tid % 2
+  const int srow = tid >> 1, shalf = tid & 1;
+  const int64_t wf = min(n0 + srow, N - 1) * K + 32 * shalf;
+  const int64_t nk = K / kTileK;
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  auto load_a = [&](int64_t kt, AFrag& a) {
+    const int64_t k0 = min(kt, nk - 1) * kTileK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) a.v[i][s] = *reinterpret_cast<const u32x4*>(xrow[i] + (k0 + 8 * s) * 2);
+  };
+  auto load_w = [&](int64_t kt) {
+    WStage<KB> st;
+    const int64_t f = wf + min(kt, nk - 1) * kTileK;
+    if constexpr (KB == 4) {
+      st.codes[0] = *reinterpret_cast<const u32x4*>(packed + (f >> 1));
+    } else {
+      st.codes[0] = *reinterpret_cast<const u32x4*>(packed + f);
+      st.codes[1] = *reinterpret_cast<const u32x4*>(packed + f + 16);
+    }
+    st.a = absmax[f >> log2b];
+    return st;
+  };
+  auto store_w = [&](const WStage<KB>& st, uint16_t* sw, int s) {
+    uint32_t codes[KB == 4 ? 4 : 8];
+#pragma unroll
+    for (int h = 0; h < (KB == 4 ? 1 : 2); ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) codes[4 * h + i] = st.codes[h][i];
+    const uint4 w = weight_frag<DT, KB>(codes, s, st.a, s_pair, s_c);
+    *reinterpret_cast<u32x4*>(sw + srow * kRowPad + 32 * shalf + 8 * s) = u32x4{w.x, w.y, w.z, w.w};
+  };
+  // MFMAs of the step in buffer buf with x fragments a; with st, the next step's weights are
+  // formed and written into the other buffer a quarter at a time between them.
+  auto multiply = [&](int buf, const AFrag& a, const WStage<KB>* st) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint4 b[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = *reinterpret_cast<const uint4*>(&s_w[buf][(32 * j + r) * kRowPad + 32 * g + 8 * s]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = mfma32x32x16<DT>(__builtin_bit_cast(uint4, a.v[i][s]), b[j], acc[i][j]);
+      if (st != nullptr) store_w(*st, s_w[buf ^ 1], s);
+    }
+  };
+
+  AFrag a0, a1;
+  load_a(0, a0);
+  WStage<KB> w0 = load_w(0), w1 = load_w(1);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) store_w(w0, s_w[0], s);
+  __syncthreads();
+  int64_t kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    load_a(kt + 1, a1);
+    w0 = load_w(kt + 2);
+    prefetch_fence();
+    multiply(0, a0, &w1);  // step kt; step kt + 1's weights into buffer 1
+    __syncthreads();
+    load_a(kt + 2, a0);
+    w1 = load_w(kt + 3);
+    prefetch_fence();
+    multiply(1, a1, &w0);  // step kt + 1; step kt + 2's weights into buffer 0
+    __syncthreads();
+  }
+  if (kt < nk) multiply(0, a0, nullptr);
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = n0 + 32 * j + r;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = m0 + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+        if (row < M && col < N) y[row * N + col] = acc[i][j][v];
+      }
+    }
+}
+
 // 64 rows of W per workgroup (two column tiles: x is loaded once for both), 32, 64 or 128 rows
 // of x, and NW waves splitting K.  Measured at 14336 x 4096 against 32 rows of W and against
 // other wave counts: 8 waves for 32 rows of x (M = 8: 17.4 against 21.7 us with 4; the grid
@@ -424,6 +562,18 @@ hipError_t launch_kb(const void* x, int64_t M, int64_t K, int64_t N, int log2b, 
   // Above 128 rows the LDS-tiled kernel: x and W16 read once per 128 x 128 tile (at 14336 x
   // 4096: M = 256 56.4 against 95.3 us, M = 1024 181 against 335; M = 128 55.6 against 52.1)
   if (M <= 128) return launch_mt<DT, KB, 4, 4>(x, M, K, N, log2b, absmax, packed, y, da, s);
+  // The wide form for 8-bit codes, where its grid holds at least 1.5 workgroups per CU (two
+  // fit on each).  8-bit weights take a table read each, so forming them once per 256 rows of
+  // x instead of 128 pays most: at 14336 x 4096, M = 1024 (448 tiles) 170.9 against 202.0 us,
+  // M = 2048 341.8 against 369.0.  For 4-bit codes it was within a few percent either way
+  // (M = 1024 164.8 against 171.8, M = 2048 322.8 against 315.7), and with fewer tiles
+  // (M = 512: 224, M = 768: 336) it was slower.
+  const int64_t wide_tiles = ((N + kWideN - 1) / kWideN) * ((M + kWideM - 1) / kWideM);
+  if (KB == 8 && 2 * wide_tiles >= 3 * (int64_t)cu_count()) {
+    const dim3 grid((unsigned)((N + kWideN - 1) / kWideN), (unsigned)((M + kWideM - 1) / kWideM));
+    return launch_kernel(gemm_wide_kernel<DT, KB>, grid, dim3(256), s, static_cast<const uint8_t*>(x), M, K, N,
+                         log2b, absmax, packed, y, da);
+  }
   const dim3 grid((unsigned)((N + kTileB - 1) / kTileB), (unsigned)((M + kTileB - 1) / kTileB));
   return launch_kernel(gemm_tiled_kernel<DT, KB>, grid, dim3(256), s, static_cast<const uint8_t*>(x), M, K, N,
                        log2b, absmax, packed, y, da);

@@ -339,18 +339,6 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void linear_mfma_kernel(
   }
 }
 
-int cu_count() {
-  static std::atomic<int> cus[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int c = cus[dev].load(std::memory_order_relaxed);
-  if (c == 0) {
-    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
-    cus[dev].store(c, std::memory_order_relaxed);
-  }
-  return c;
-}
-
 template <int DT, int KB>
 hipError_t launch_mt(const void* x, int M, int64_t K, int64_t N, int log2b, const float* absmax,
                      const uint8_t* packed, float* y, const DequantArgs& da, hipStream_t s) {
@@ -380,6 +368,18 @@ hipError_t launch_kb(const void* x, int M, int64_t K, int64_t N, int log2b, cons
 }
 
 }  // namespace
+
+int cu_count() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int c = cus[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    cus[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
 
 int launch_linear(const void* x, int dtype, int64_t M, int64_t K, int64_t N, int blocksize, const DequantArgs& da,
                   const float* absmax, const uint8_t* packed, float* y, void* stream) {

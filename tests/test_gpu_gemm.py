@@ -120,7 +120,7 @@ def test_gemm_weights_match_the_16_bit_dequantize(dev, o, dtype, K_table):
         assert np.array_equal(y.astype(np.float64), w16.reshape(N, K)[:, ks].T), len(ks)
 
 
-@pytest.mark.parametrize("K_table,M", [(16, 64), (256, 200), (16, 1024)])
+@pytest.mark.parametrize("K_table,M", [(16, 64), (256, 200), (16, 1024), (256, 1024)])
 def test_gemm_prefill_shape_sampled_rows(dev, o, K_table, M):
     """A 14336 x 4096 weight (bf16 activations, B = 64), every output computed on the GPU; the
     oracle checks 24 sampled weight rows (first, last and random) for every activation row.
@@ -142,3 +142,53 @@ def test_gemm_prefill_shape_sampled_rows(dev, o, K_table, M):
     sub_absmax = np.concatenate([absmax[r * (K // B):(r + 1) * (K // B)] for r in rows])
     check_gemm_against_oracle(o, y[:, rows], x, "bfloat16", len(rows), B, table, sub_absmax, sub_packed,
                          "prefill shape table=%d M=%d" % (K_table, M))
+
+
+# With 8-bit codes, grids of at least 1.5 workgroups of 256 x 128 outputs per CU (384 on
+# MI355X's 256 CUs) take the wide form: 1100 x 12290 gives 5 x 97 tiles with ragged last rows
+# and columns, K = 320 an odd number of 64-k steps.  (The 16-entry table runs the same shapes
+# through the 128 x 128 form.)
+
+
+@pytest.mark.parametrize("dtype", ["bfloat16", "float16"])
+@pytest.mark.parametrize("K_table", [16, 256])
+def test_gemm_wide_form_ragged(dev, o, dtype, K_table):
+    """Seeded random codes and log-normal block maxima; the oracle checks 24 sampled weight
+    rows (first, last and random) for every activation row; a second call gives the same bits."""
+    table = TABLES[K_table]
+    M, N, K, B = 1100, 12290, 320, 64
+    rng = np.random.default_rng(21 + K_table)
+    packed = rng.integers(0, 256, size=N * K // 2 if K_table == 16 else N * K, dtype=np.uint8)
+    absmax = (0.02 * np.exp(rng.standard_normal(N * K // B))).astype(np.float32)
+    x = activations(M, K, dtype, seed=22)
+    y = run_gpu(dev, x, dtype, N, B, table, absmax, packed)
+    y2 = run_gpu(dev, x, dtype, N, B, table, absmax, packed)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    rows = np.unique(np.concatenate([[0, 127, 128, N - 1], np.random.default_rng(23).integers(0, N, 20)]))
+    per_row = K // 2 if K_table == 16 else K
+    sub_packed = np.concatenate([packed[r * per_row:(r + 1) * per_row] for r in rows])
+    sub_absmax = np.concatenate([absmax[r * (K // B):(r + 1) * (K // B)] for r in rows])
+    check_gemm_against_oracle(o, y[:, rows], x, dtype, len(rows), B, table, sub_absmax, sub_packed,
+                              "wide form %s table=%d" % (dtype, K_table))
+
+
+def test_gemm_wide_form_exact(dev, o):
+    """A dyadic 256-entry table (k / 128 for k = -128 .. 127, each exact in both 16-bit types),
+    power-of-two block maxima and small integer activations on a grid the wide form takes
+    (1030 x 9860: 5 x 78 tiles): every weight and partial sum is exact, so sampled weight rows
+    must equal the oracle's values exactly (a row, column or k mixed up in the fragment layout
+    changes them)."""
+    table = (np.arange(-128, 128) / 128.0).astype(np.float32)
+    M, N, K, B = 1030, 9860, 128, 64
+    q = (np.arange(N)[:, None] * 5 + np.arange(K)[None, :] * 3 + np.arange(N)[:, None] // 9) % 256
+    packed = q.reshape(-1).astype(np.uint8)
+    absmax = np.ldexp(np.float32(1), (np.arange(N * K // B) % 5) - 2).astype(np.float32)
+    xi = ((np.arange(M * K).reshape(M, K) * 7 + np.arange(M)[:, None] // 13) % 11 - 5).astype(np.float32)
+    rows = np.unique(np.concatenate([[0, 31, 32, 127, 128, N - 1], np.random.default_rng(24).integers(0, N, 30)]))
+    sub_packed = np.concatenate([packed[r * K:(r + 1) * K] for r in rows])
+    sub_absmax = np.concatenate([absmax[r * (K // B):(r + 1) * (K // B)] for r in rows])
+    for dtype in ("bfloat16", "float16"):
+        x = torch.from_numpy(xi).to(TORCH_DT[dtype])
+        y = run_gpu(dev, x, dtype, N, B, table, absmax, packed)
+        ref = o.gemm_blockwise(host_bits(x), ORACLE_DT[dtype], M, K, len(rows), B, table, sub_absmax, sub_packed)
+        assert np.array_equal(y[:, rows].astype(np.float64), ref), dtype
