@@ -172,7 +172,8 @@ __device__ __forceinline__ LutWords<MODE, M, NT> lut_fetch(const QuantArgs& qa, 
   }
   // Every entry of the base array is read, not just the nbuckets in use: the host zero-fills
   // the rest, and a bound known at compile time leaves no branch between the loads.  F16B
-  // entries of negative y take their base from index - 1087, and the hole reads a valid index.
+  // entries of negative y (index 1024 on) take their base from index - 63, and the hole reads
+  // a valid index.
   constexpr int kSize = LutLayout<MODE, M>::kSize;
 #pragma unroll
   for (int k = 0; k < L::kLutIt; ++k) {
