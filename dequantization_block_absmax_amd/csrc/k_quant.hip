@@ -12,10 +12,14 @@
 // stores of consecutive lanes are contiguous.  A block of B elements is G = B/32 consecutive
 // lanes: G <= 64 reduce the absmax within the wave by xor-shuffles, G = 128 (B = 4096) adds
 // one LDS exchange between the two waves.  A 256-lane workgroup quantizes one tile of 8192
-// elements.  (Workgroups that each took several tiles, with the next tile's loads issued
-// ahead of the current tile's arithmetic, measured slower on MI355X: 41.2 against 36.9 us for
-// 2^26 bf16 elements with 8-bit codes, B = 4096; the second register buffer costs more
-// occupancy than the overlap gains.)
+// elements.  With 16-bit input, 8-bit codes and blocks of 2048 or more, a whole tile takes an
+// interleaved chunk instead (load_chunk_il: each of the wave's four loads reads 1 KB of
+// consecutive bytes and each code store writes 512), which needs no LDS exchange for the
+// stores (bf16 2^26, B = 4096: 36.8 against 37.8 us, identical output).  (Workgroups that
+// each took several tiles, with the next tile's loads issued ahead of the current tile's
+// arithmetic, measured slower on MI355X: 41.2 against 36.9 us for 2^26 bf16 elements with
+// 8-bit codes, B = 4096; the second register buffer costs more occupancy than the overlap
+// gains.)
 //
 // The absmax uses an integer key: k = (bits << 1) + OFF (mod 2^w) drops the sign and wraps
 // NaN/Inf below every finite value, so max(k) excludes non-finite elements without a compare.
@@ -120,6 +124,23 @@ __device__ __forceinline__ float key_to_absmax(uint32_t k) {
   } else {
     unsigned short h = (unsigned short)(k >= 0x0800u ? (k - 0x0800u) >> 1 : 0u);
     return (float)__builtin_bit_cast(_Float16, h);
+  }
+}
+
+// Interleaved chunk (16-bit input, 8-bit codes, blocks of 2048 or more): the lane's 32
+// elements are 8 consecutive ones from each of the wave's four 512-element segments, so that
+// each of the four 16-byte loads of the wave reads 1 KB of consecutive bytes and each 8-byte
+// store of codes writes 512.  The wave's 2048 elements lie in one block either way.
+template <int DT>
+__device__ __forceinline__ void load_chunk_il(const uint8_t* __restrict__ in, int64_t wave0, int lane, uint32_t* w) {
+  const uint4* src = reinterpret_cast<const uint4*>(in + (wave0 + 8 * lane) * 2);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint4 v = src[64 * k];
+    w[4 * k] = v.x;
+    w[4 * k + 1] = v.y;
+    w[4 * k + 2] = v.z;
+    w[4 * k + 3] = v.w;
   }
 }
 
@@ -236,7 +257,7 @@ struct QuantShared {
 // (the data pass of a nested quantize) stores the block maxima in the input's own format
 // (binary32 for fp32 input, the 16 bits of fp16 / bf16 input, which hold them exactly);
 // otherwise they are binary32.
-template <int DT, int KB, int MODE, int M, bool NESTED>
+template <int DT, int KB, int MODE, int M, bool NESTED, bool IL = false>
 __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, int64_t elem0, int64_t n, int log2g,
                                                void* __restrict__ absmax, uint8_t* __restrict__ packed,
                                                const QuantArgs& qa, const typename Entry<M>::type* s_lut,
@@ -332,7 +353,14 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t* w, int nvalid, in
   constexpr int kBytes = kOut * 4;
   const int64_t off = KB == 4 ? elem0 >> 1 : elem0;
   const int64_t wave_off = off - (int64_t)lane * kBytes;
-  if (KB == 8 && wave_off + 64 * kBytes <= packed_bytes) {  // whole wave in range (uniform)
+  if (IL) {  // interleaved chunk of a whole tile: word pair 2k holds segment k's 8 codes
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const u32x2 v = {o[(2 * k) % kOut], o[(2 * k + 1) % kOut]};
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(packed + wave_off + 512 * k + 8 * lane));
+    }
+  } else if (KB == 8 && wave_off + 64 * kBytes <= packed_bytes) {  // whole wave in range (uniform)
     // Two rounds through a 1 KB region: lanes 0-31, then 32-63, stage their bytes and the
     // whole wave stores them.
     uint8_t* dst = packed + wave_off;
@@ -388,7 +416,14 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint8_t* __res
   // a path of unconditional loads of its own: where a load under a condition joins a path
   // without it, the compiler can only wait for every outstanding load, the tile's included,
   // before the LUT fill.
-  if ((tile0 + 1) * kTile <= n) {
+  constexpr bool kCanIL = KB == 8 && DT != F32;
+  if (kCanIL && log2g >= 6 && (tile0 + 1) * kTile <= n) {  // uniform
+    const auto lw = lut_fetch<MODE, M, kThreads>(qa, tid);
+    load_chunk_il<DT>(in, elem0 - (int64_t)(tid & 63) * kEPT, tid & 63, w);
+    lut_fill<MODE, M, kThreads>(qa, lw, s_lut, s_thr, tid);
+    quantize_chunk<DT, KB, MODE, M, NESTED, kCanIL>(w, kEPT, elem0, n, log2g, absmax, packed, qa, s_lut, s_thr, sh,
+                                                    stage);
+  } else if ((tile0 + 1) * kTile <= n) {
     const auto lw = lut_fetch<MODE, M, kThreads>(qa, tid);
     if constexpr (kViaLds) {
       const auto chunks = load_chunk_lds_issue<DT>(in, elem0 - (int64_t)(tid & 63) * kEPT, tid & 63);

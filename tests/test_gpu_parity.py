@@ -378,7 +378,7 @@ def test_bf16_2pow26_8bit_blocksize4096(dev, po):
 N_MANY = 3 * (1 << 23) + 3 * 8192 + 77
 
 
-@pytest.mark.parametrize("dtype,B", [("bfloat16", 4096), ("float32", 64), ("float16", 256)])
+@pytest.mark.parametrize("dtype,B", [("bfloat16", 4096), ("float32", 64), ("float16", 256), ("float16", 2048)])
 def test_8bit_several_tiles_per_workgroup(dev, po, dtype, B):
     n = N_MANY
     t256 = synth.table256()
