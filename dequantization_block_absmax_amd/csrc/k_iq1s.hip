@@ -23,8 +23,8 @@
 // end; an xn that overflows makes an error NaN exactly where the shifted dot is +inf or NaN
 // (its clamped error is 0) and +inf elsewhere, which a rare branch reproduces per sign.
 //
-// Decoder: one lane per 8-element vector: d * (2 ls + 1) (exact) times (g + delta) (exact),
-// rounded once to binary32 and once to the output type.
+// Decoder: one lane per 8-element vector (four vectors per lane, 256 apart): d * (2 ls + 1)
+// (exact) times (g + delta) (exact), rounded once to binary32 and once to the output type.
 #include <hip/hip_runtime.h>
 
 #include "bq_internal.h"
@@ -40,6 +40,9 @@ constexpr int kThreads = 256;
 constexpr int kSlices = 8;
 constexpr int kPerSlice = kEntries / kSlices;
 constexpr int kDecodeThreads = 256;
+// Vectors per decoder lane, 256 apart (8.2% faster than one at 4096 x 14336 to bf16; eight
+// were slower)
+constexpr int kDecVPL = 4;
 static_assert(kThreads == (kBlockElems / 8) * kSlices, "one lane per (vector, slice)");
 static_assert(kEntries % kThreads == 0, "each lane stages whole grid entries");
 
@@ -326,23 +329,26 @@ template <int DT>
 __global__ __launch_bounds__(kDecodeThreads) void iq1s_decode_kernel(const uint8_t* __restrict__ blocks,
                                                                      const int8_t* __restrict__ grid, int64_t nvec,
                                                                      uint8_t* __restrict__ out) {
-  const int64_t vec = (int64_t)blockIdx.x * kDecodeThreads + threadIdx.x;
-  if (vec >= nvec) return;
-  const uint8_t* blk = blocks + (vec >> 5) * kBlockBytes;
-  const int v = (int)(vec & 31);
-  const uint16_t dbits = *reinterpret_cast<const uint16_t*>(blk);
-  const uint32_t qh = *reinterpret_cast<const uint16_t*>(blk + 34 + 2 * (v >> 2));
-  const uint32_t e = blk[2 + v] | (((qh >> (3 * (v & 3))) & 7u) << 8);
-  const float dl = (float)__builtin_bit_cast(_Float16, dbits) * (float)(2 * ((qh >> 12) & 7u) + 1);
-  const float delta = (qh & 0x8000u) ? -0.125f : 0.125f;
-  const uint2 g = *reinterpret_cast<const uint2*>(grid + 8 * e);
-  float val[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int q = (int)(int8_t)((j < 4 ? g.x : g.y) >> (8 * (j & 3)));
-    val[j] = dl * ((float)q + delta);
+  for (int k = 0; k < kDecVPL; ++k) {
+    const int64_t vec0 = ((int64_t)blockIdx.x * kDecVPL + k) * kDecodeThreads + threadIdx.x;
+    const int64_t vec = min(vec0, nvec - 1);
+    const uint8_t* blk = blocks + (vec >> 5) * kBlockBytes;
+    const int v = (int)(vec & 31);
+    const uint16_t dbits = *reinterpret_cast<const uint16_t*>(blk);
+    const uint32_t qh = *reinterpret_cast<const uint16_t*>(blk + 34 + 2 * (v >> 2));
+    const uint32_t e = blk[2 + v] | (((qh >> (3 * (v & 3))) & 7u) << 8);
+    const float dl = (float)__builtin_bit_cast(_Float16, dbits) * (float)(2 * ((qh >> 12) & 7u) + 1);
+    const float delta = (qh & 0x8000u) ? -0.125f : 0.125f;
+    const uint2 g = *reinterpret_cast<const uint2*>(grid + 8 * e);
+    float val[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = (int)(int8_t)((j < 4 ? g.x : g.y) >> (8 * (j & 3)));
+      val[j] = dl * ((float)q + delta);
+    }
+    if (vec0 < nvec) store_vector<DT>(out, vec0, val);
   }
-  store_vector<DT>(out, vec, val);
 }
 
 template <int DT>
@@ -354,7 +360,8 @@ hipError_t launch_encode_dt(const void* in, int64_t n, const int8_t* grid, uint8
 template <int DT>
 hipError_t launch_decode_dt(const uint8_t* blocks, const int8_t* grid, int64_t n, void* out, hipStream_t s) {
   const int64_t nvec = n / 8;
-  return launch_kernel(iq1s_decode_kernel<DT>, dim3((unsigned)((nvec + kDecodeThreads - 1) / kDecodeThreads)),
+  return launch_kernel(iq1s_decode_kernel<DT>,
+                       dim3((unsigned)((nvec + kDecodeThreads * kDecVPL - 1) / (kDecodeThreads * kDecVPL))),
                        dim3(kDecodeThreads), s, blocks, grid, nvec, static_cast<uint8_t*>(out));
 }
 
