@@ -100,9 +100,9 @@ def test_linear_exact_when_all_terms_exact(dev, o):
 @pytest.mark.parametrize("K_table,M", [(16, 4), (256, 1)])
 def test_linear_decode_shape_sampled_rows(dev, o, K_table, M):
     """The 14336 x 4096 weight of the benchmark (bf16 activations, B = 64), every output
-    computed on the GPU; the oracle checks 40 sampled rows (first, last and random).  The
-    codes are seeded random bytes and the block maxima seeded log-normal values: the fused
-    product reads them as given, whatever quantizer made them."""
+    computed on the GPU; the oracle checks 40 sampled rows (first, last and random), and then
+    every row.  The codes are seeded random bytes and the block maxima seeded log-normal
+    values: the fused product reads them as given, whatever quantizer made them."""
     table = TABLES[K_table]
     N, K, B = 14336, 4096, 64
     rng = np.random.default_rng(7)
@@ -117,6 +117,8 @@ def test_linear_decode_shape_sampled_rows(dev, o, K_table, M):
     sub_absmax = np.concatenate([absmax[r * (K // B):(r + 1) * (K // B)] for r in rows])
     check_linear_against_oracle(o, y[:, rows], x, "bfloat16", len(rows), B, table, sub_absmax, sub_packed,
                          "decode shape table=%d M=%d" % (K_table, M))
+    check_linear_against_oracle(o, y, x, "bfloat16", N, B, table, absmax, packed,
+                                "decode shape, every row, table=%d M=%d" % (K_table, M))
 
 
 # Tall weights with 4-bit codes at M = 3 or 4 take the matrix-core form (at least 32 weight
