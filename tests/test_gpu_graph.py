@@ -46,12 +46,20 @@ def test_graph_replay_matches_oracle(dev, po):
     q4 = synth.q32_blocks(m // 32, "q4", seed=42, device=dev)
     gen = torch.Generator(device=dev)
     gen.manual_seed(43)
-    Ml, Kl, Nl = 3, 4096, 1000  # fused linear: seeded codes and block maxima of a 1000 x 4096 weight
+    # fused linear: seeded codes and block maxima of an 8200 x 4096 weight, tall enough for the
+    # matrix-core form at three rows (32 rows per CU on MI355X)
+    Ml, Kl, Nl = 3, 4096, 8200
     wpk = torch.randint(0, 256, (Nl * Kl // 2,), dtype=torch.uint8, device=dev, generator=gen)
     wam = 0.01 + 0.02 * torch.rand(Nl * Kl // B, device=dev, generator=gen)
     xl = torch.randn(Ml, Kl, device=dev, generator=gen).to(torch.bfloat16)
-    Mg = 40  # fused GEMM on the same weight
+    Mg, Ng = 40, 1000  # fused GEMM on the first 1000 rows of that weight
     xg = torch.randn(Mg, Kl, device=dev, generator=gen).to(torch.bfloat16)
+    # fused GEMM in its wide form: 8-bit codes, 1024 x 12288 outputs (4 x 96 tiles), K = 128
+    Mw, Kw, Nw = 1024, 128, 12288
+    wpk8 = torch.randint(0, 256, (Nw * Kw,), dtype=torch.uint8, device=dev, generator=gen)
+    wam8 = 0.01 + 0.02 * torch.rand(Nw * Kw // B, device=dev, generator=gen)
+    xw = torch.randn(Mw, Kw, device=dev, generator=gen).to(torch.bfloat16)
+    wrows = np.unique(np.concatenate([[0, 127, 128, Nw - 1], np.random.default_rng(44).integers(0, Nw, 12)]))
 
     # the oracle's outputs for the same inputs
     xb = host_bits(x)
@@ -60,6 +68,9 @@ def test_graph_replay_matches_oracle(dev, po):
                                    t256_np, B2)
     ref_out4 = po.dequant_q32(q4.cpu().numpy(), m, cols, oracle.Q4, oracle.BF16)
     wpk_h, wam_h = wpk.cpu().numpy(), wam.cpu().numpy()
+    wpk8_h, wam8_h = wpk8.cpu().numpy(), wam8.cpu().numpy()
+    wpk8_rows = np.concatenate([wpk8_h[r * Kw:(r + 1) * Kw] for r in wrows])
+    wam8_rows = np.concatenate([wam8_h[r * (Kw // B):(r + 1) * (Kw // B)] for r in wrows])
 
     def buffers():
         ws_bytes = bq.bq_nested_workspace_bytes(n, B, B2)
@@ -71,7 +82,8 @@ def test_graph_replay_matches_oracle(dev, po):
                     out=torch.zeros(n, dtype=torch.bfloat16, device=dev),
                     out4=torch.zeros(m, dtype=torch.bfloat16, device=dev),
                     y=torch.zeros(Ml, Nl, dtype=torch.float32, device=dev),
-                    yg=torch.zeros(Mg, Nl, dtype=torch.float32, device=dev))
+                    yg=torch.zeros(Mg, Ng, dtype=torch.float32, device=dev),
+                    yw=torch.zeros(Mw, Nw, dtype=torch.float32, device=dev))
 
     def run(b, stream=None):
         st = bq.nested_stats(b["q2"], b["a2"], b["mean"], t256, B2, b["ws"])
@@ -80,7 +92,8 @@ def test_graph_replay_matches_oracle(dev, po):
                  "dequantize_nested")
         bq.check(bq.bq_dequant_q32(q4, bq.BQ_BF16, m, cols, bq.BQ_Q32_Q4, b["out4"], stream), "dequant_q32")
         bq.check(bq.bq_linear_blockwise(xl, bq.BQ_BF16, Ml, Kl, Nl, B, t16, wam, wpk, b["y"], stream), "linear")
-        bq.check(bq.bq_gemm_blockwise(xg, bq.BQ_BF16, Mg, Kl, Nl, B, t16, wam, wpk, b["yg"], stream), "gemm")
+        bq.check(bq.bq_gemm_blockwise(xg, bq.BQ_BF16, Mg, Kl, Ng, B, t16, wam, wpk, b["yg"], stream), "gemm")
+        bq.check(bq.bq_gemm_blockwise(xw, bq.BQ_BF16, Mw, Kw, Nw, B, t256, wam8, wpk8, b["yw"], stream), "gemm wide")
 
     def check_against_oracle(b, what):
         assert_bytes_equal(b["packed"].cpu().numpy(), ref["packed"], what + " packed")
@@ -91,14 +104,16 @@ def test_graph_replay_matches_oracle(dev, po):
         assert_bytes_equal(host_bits(b["out4"]), ref_out4, what + " q32")
         check_linear_against_oracle(po, b["y"].cpu().numpy(), xl.cpu(), "bfloat16", Nl, B, t16_np, wam_h, wpk_h,
                                     what + " linear")
-        check_gemm_against_oracle(po, b["yg"].cpu().numpy(), xg.cpu(), "bfloat16", Nl, B, t16_np, wam_h, wpk_h,
-                                  what + " gemm")
+        check_gemm_against_oracle(po, b["yg"].cpu().numpy(), xg.cpu(), "bfloat16", Ng, B, t16_np,
+                                  wam_h[:Ng * Kl // B], wpk_h[:Ng * Kl // 2], what + " gemm")
+        check_gemm_against_oracle(po, b["yw"].cpu().numpy()[:, wrows], xw.cpu(), "bfloat16", len(wrows), B, t256_np,
+                                  wam8_rows, wpk8_rows, what + " gemm wide (sampled rows)")
 
     eager = buffers()
     run(eager)
     torch.cuda.synchronize()
     check_against_oracle(eager, "eager")
-    y_eager, yg_eager = eager["y"].clone(), eager["yg"].clone()
+    y_eager, yg_eager, yw_eager = eager["y"].clone(), eager["yg"].clone(), eager["yw"].clone()
 
     g = buffers()
     graph = torch.cuda.CUDAGraph()
@@ -121,6 +136,7 @@ def test_graph_replay_matches_oracle(dev, po):
         # the fused products are not unique, but every call gives the same bits
         assert torch.equal(g["y"].view(torch.int32), y_eager.view(torch.int32)), replay
         assert torch.equal(g["yg"].view(torch.int32), yg_eager.view(torch.int32)), replay
+        assert torch.equal(g["yw"].view(torch.int32), yw_eager.view(torch.int32)), replay
 
 
 def test_two_stream_copy_quantize_pipeline(dev, po):
