@@ -75,7 +75,10 @@ __device__ __forceinline__ void widen_x16(const XRaw<DT>& r, float* v) {
   }
 }
 
-// Codes of a lane's 16 elements of one row: 8 bytes (4-bit) or 16 bytes (8-bit).
+// Codes of a lane's 16 elements of one row: 8 bytes (4-bit) or 16 bytes (8-bit), loaded
+// non-temporally: each load instruction of a wave reads 512 or 1024 consecutive bytes of the
+// row, whole cache lines, read once (1-5% faster at 14336 x 4096 and 4096 x 14336; 8-bit
+// M = 4: 19.0 against 20.0 us).
 template <int KB>
 struct Codes {
   uint32_t w[KB == 4 ? 2 : 4];
@@ -84,12 +87,14 @@ struct Codes {
 template <int KB>
 __device__ __forceinline__ Codes<KB> load_codes(const uint8_t* __restrict__ packed, int64_t flat) {
   Codes<KB> c;
+  typedef unsigned int u32x2_nt __attribute__((ext_vector_type(2)));
+  typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
   if constexpr (KB == 4) {
-    const uint2 u = *reinterpret_cast<const uint2*>(packed + (flat >> 1));
+    const u32x2_nt u = __builtin_nontemporal_load(reinterpret_cast<const u32x2_nt*>(packed + (flat >> 1)));
     c.w[0] = u.x;
     c.w[1] = u.y;
   } else {
-    const uint4 u = *reinterpret_cast<const uint4*>(packed + flat);
+    const u32x4_nt u = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(packed + flat));
     c.w[0] = u.x;
     c.w[1] = u.y;
     c.w[2] = u.z;
