@@ -40,8 +40,10 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Non-temporal 16-byte store of the codes: they stream to memory without displacing the input
-// from the caches (2^29 bf16, 4-bit: 224 us against 234 us with ordinary stores on MI355X;
-// the same hint on the loads or the absmax stores measured slower).
+// from the caches (2^29 bf16, 4-bit: 224 us against 234 us with ordinary stores on MI355X; the
+// same hint on the absmax stores measured slower).  The hint suits loads only where each load
+// instruction of a wave reads whole cache lines (the LDS-transposed and interleaved chunks):
+// on lane-contiguous chunks, whose lines are shared by four instructions, it doubled the time.
 __device__ __forceinline__ void store16_nt(uint8_t* p, uint4 v) {
   const u32x4 w = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
