@@ -1,6 +1,6 @@
 // k_gemm.hip -- fused dequantize + GEMM on the gfx950 matrix cores, for batches of rows
-// (gemm_kernel up to 128 rows of x, gemm_tiled_kernel above, gemm_wide_kernel for the largest
-// grids of 8-bit codes):
+// (gemm_kernel up to 128 rows of x, gemm_tiled_kernel above, gemm_big_kernel for grids of
+// 256 x 256 tiles that fill most of the CUs):
 // y = x . W16^T, where W16 = RN16(fl32(c[q] * a)) is exactly the 16-bit tensor that
 // bq_dequantize_blockwise writes for W, formed in registers and never stored (the
 // 16-bit-activation, 4-bit-weight GEMM of "stable-diffusion.cpp PR 2278", Summary, on the
@@ -402,138 +402,163 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint8_t* x, int64
     }
 }
 
-// Large batches, wide form: a 256 x 128 output tile per workgroup (256 rows of x, 128 rows of
-// W), its four waves stacked along x (64 x 128 each: 2 x 4 accumulator tiles).  Each wave
-// loads its own 64 rows of x straight into MFMA fragments (lane group g takes the 32
-// consecutive k from 32 g of its row, MFMA step s the 8 from 32 g + 8 s, and the weight
-// fragments read from LDS follow the same assignment), so x never passes through LDS; only the
-// 16-bit weights do, formed once per workgroup and read by all four waves.  Per 64-k step that
-// is 16 KB of LDS writes and 64 KB of reads for 2 M multiply-adds, against 32 KB and 64 KB for
-// 1 M in the 128 x 128 form.  x is loaded one step ahead.  The kernel is held to two waves per
-// SIMD (242 registers, the accumulators among them): with 128 accumulator registers on top of
-// 172 it ran one wave per SIMD and was slower than the 128 x 128 form.
-constexpr int kWideM = 256;
-constexpr int kWideN = 128;
-
-struct AFrag {
-  u32x4 v[2][4];  // row tile i (32 rows), MFMA step s
-};
+// Large batches, big tiles: a 256 x 256 output tile per workgroup (256 rows of x, 256 rows of
+// W), eight waves arranged 2 x 4, each owning 128 x 64 outputs (4 x 2 accumulator tiles), two
+// waves per SIMD.  K in LDS-staged steps of 64 with two buffers that alternate.
+//
+// Staging: the step's tiles are loaded as 16-byte chunks, chunk c of a tile going to thread
+// c % 512 (consecutive threads take consecutive chunks of a row, so each load instruction
+// covers whole rows): x has 8 chunks per row (64 k), W 2 (4-bit codes, 32 k each) or 4 (8-bit,
+// 16 k each), each W chunk with the scale of its block (B >= 32, so one scale serves a chunk).
+// A step's loads are issued one step ahead into one of two register stages, and the stage of
+// the next step is formed and written into the other LDS buffer a quarter at a time between
+// the current step's MFMAs.
+constexpr int kBigM = 256;
+constexpr int kBigN = 256;
+constexpr int kBigThreads = 512;
 
 template <int KB>
-struct WStage {
-  u32x4 codes[KB == 4 ? 1 : 2];
-  float a;
+struct BigStage {
+  static constexpr int kW = kBigN * (KB == 4 ? 2 : 4) / kBigThreads;  // W chunks per thread
+  u32x4 x[4];
+  u32x4 w[kW];
+  float a[kW];
 };
 
 template <int DT, int KB>
-__global__ __launch_bounds__(256, 2) void gemm_wide_kernel(const uint8_t* x, int64_t M, int64_t K, int64_t N,
-                                                        int log2b, const float* absmax, const uint8_t* packed,
-                                                        float* __restrict__ y, DequantArgs da) {
+__global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const uint8_t* x, int64_t M, int64_t K,
+                                                                  int64_t N, int log2b, const float* absmax,
+                                                                  const uint8_t* packed, float* __restrict__ y,
+                                                                  DequantArgs da) {
+  constexpr int NI = 4, NJ = 2;           // accumulator tiles per wave (128 x 64 outputs)
+  constexpr int kCpr = KB == 4 ? 2 : 4;   // W chunks per row
+  constexpr int kW = BigStage<KB>::kW;
   __shared__ float2 s_pair[KB == 4 ? 256 : 1];
   __shared__ float s_c[KB == 8 ? 256 : 1];
-  __shared__ __attribute__((aligned(16))) uint16_t s_w[2][kWideN * kRowPad];
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[2][kBigM * kRowPad];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[2][kBigN * kRowPad];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r = lane & 31;
-  if constexpr (KB == 4) s_pair[tid] = make_float2(da.c[tid >> 4], da.c[tid & 15]);
-  else s_c[tid] = da.c[tid];
+  const int wm = wave >> 2, wn = wave & 3;
+  if (tid < 256) {
+    if constexpr (KB == 4) s_pair[tid] = make_float2(da.c[tid >> 4], da.c[tid & 15]);
+    else s_c[tid] = da.c[tid];
+  }
   __syncthreads();
 
-  const int64_t m0 = (int64_t)blockIdx.y * kWideM + 64 * wave;
-  const int64_t n0 = (int64_t)blockIdx.x * kWideN;
-  // x rows of this lane (rows past M read the last row and are never stored)
-  const uint8_t* xrow[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) xrow[i] = x + (min(m0 + 32 * i + r, M - 1) * K + 32 * g) * 2;
-  // staging: W row tid / 2 of the tile, k half tid % 2
-  const int srow = tid >> 1, shalf = tid & 1;
-  const int64_t wf = min(n0 + srow, N - 1) * K + 32 * shalf;
+  const int64_t m0 = (int64_t)blockIdx.y * kBigM;
+  const int64_t n0 = (int64_t)blockIdx.x * kBigN;
   const int64_t nk = K / kTileK;
+  // x chunk i of this thread: row 64 i + tid / 8 of the tile, bytes 16 (tid % 8) of its 128;
+  // rows past M read the last row and are never stored
+  const uint8_t* xsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xsrc[i] = x + (min(m0 + 64 * i + (tid >> 3), M - 1) * K) * 2 + 16 * (tid & 7);
+  // W chunk i of this thread: c = 512 i + tid, row c / kCpr, chunk c % kCpr
+  int64_t wflat[kW];
+#pragma unroll
+  for (int i = 0; i < kW; ++i) {
+    const int c = kBigThreads * i + tid;
+    wflat[i] = min(n0 + c / kCpr, N - 1) * K + (c % kCpr) * (KB == 4 ? 32 : 16);
+  }
 
-  f32x16 acc[2][4];
+  f32x16 acc[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  auto load_a = [&](int64_t kt, AFrag& a) {
+  auto load = [&](int64_t kt, BigStage<KB>& st) {
     const int64_t k0 = min(kt, nk - 1) * kTileK;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i) st.x[i] = *reinterpret_cast<const u32x4*>(xsrc[i] + k0 * 2);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) a.v[i][s] = *reinterpret_cast<const u32x4*>(xrow[i] + (k0 + 8 * s) * 2);
-  };
-  auto load_w = [&](int64_t kt) {
-    WStage<KB> st;
-    const int64_t f = wf + min(kt, nk - 1) * kTileK;
-    if constexpr (KB == 4) {
-      st.codes[0] = *reinterpret_cast<const u32x4*>(packed + (f >> 1));
-    } else {
-      st.codes[0] = *reinterpret_cast<const u32x4*>(packed + f);
-      st.codes[1] = *reinterpret_cast<const u32x4*>(packed + f + 16);
+    for (int i = 0; i < kW; ++i) {
+      const int64_t f = wflat[i] + k0;
+      st.w[i] = *reinterpret_cast<const u32x4*>(packed + (KB == 4 ? (f >> 1) : f));
+      st.a[i] = absmax[f >> log2b];
     }
-    st.a = absmax[f >> log2b];
-    return st;
   };
-  auto store_w = [&](const WStage<KB>& st, uint16_t* sw, int s) {
-    uint32_t codes[KB == 4 ? 4 : 8];
+  // Quarter q of a stage into LDS buffer buf: x chunk q, and a quarter of each W chunk's
+  // weights (4-bit: 8 of its 32; 8-bit: 4 of its 16).
+  auto store_quarter = [&](const BigStage<KB>& st, int buf, int q) {
+    *reinterpret_cast<u32x4*>(&s_x[buf][(64 * q + (tid >> 3)) * kRowPad + 8 * (tid & 7)]) = st.x[q];
 #pragma unroll
-    for (int h = 0; h < (KB == 4 ? 1 : 2); ++h)
+    for (int i = 0; i < kW; ++i) {
+      const int c = kBigThreads * i + tid;
+      const int row = c / kCpr, ch = c % kCpr;
+      const uint32_t word = st.w[i][q];
+      if constexpr (KB == 4) {
+        u32x4 w;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) codes[4 * h + i] = st.codes[h][i];
-    const uint4 w = weight_frag<DT, KB>(codes, s, st.a, s_pair, s_c);
-    *reinterpret_cast<u32x4*>(sw + srow * kRowPad + 32 * shalf + 8 * s) = u32x4{w.x, w.y, w.z, w.w};
+        for (int b = 0; b < 4; ++b) {
+          const float2 pr = s_pair[(word >> (8 * b)) & 0xffu];
+          w[b] = weight_pair<DT>(pr.x, pr.y, st.a[i]);
+        }
+        *reinterpret_cast<u32x4*>(&s_w[buf][row * kRowPad + 32 * ch + 8 * q]) = w;
+      } else {
+        uint2 w;
+        w.x = weight_pair<DT>(s_c[word & 0xffu], s_c[(word >> 8) & 0xffu], st.a[i]);
+        w.y = weight_pair<DT>(s_c[(word >> 16) & 0xffu], s_c[word >> 24], st.a[i]);
+        *reinterpret_cast<uint2*>(&s_w[buf][row * kRowPad + 16 * ch + 4 * q]) = w;
+      }
+    }
   };
-  // MFMAs of the step in buffer buf with x fragments a; with st, the next step's weights are
-  // formed and written into the other buffer a quarter at a time between them.
-  auto multiply = [&](int buf, const AFrag& a, const WStage<KB>* st) {
+  auto frags = [&](int buf, int s, uint4 (&fa)[NI], uint4 (&fb)[NJ]) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      uint4 b[4];
+    for (int i = 0; i < NI; ++i)
+      fa[i] = *reinterpret_cast<const uint4*>(&s_x[buf][(128 * wm + 32 * i + r) * kRowPad + 16 * s + 8 * g]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const uint4*>(&s_w[buf][(32 * j + r) * kRowPad + 32 * g + 8 * s]);
+    for (int j = 0; j < NJ; ++j)
+      fb[j] = *reinterpret_cast<const uint4*>(&s_w[buf][(64 * wn + 32 * j + r) * kRowPad + 16 * s + 8 * g]);
+  };
+  // The step in buffer buf; with st, the next step's stage is written into the other buffer
+  // a quarter per 16-k piece.  The fragments of piece s + 1 are read before the MFMAs of piece s.
+  auto multiply = [&](int buf, const BigStage<KB>* st) {
+    uint4 fa[2][NI], fb[2][NJ];
+    frags(buf, 0, fa[0], fb[0]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int s = 0; s < kTileK / 16; ++s) {
+      if (s + 1 < kTileK / 16) frags(buf, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = mfma32x32x16<DT>(__builtin_bit_cast(uint4, a.v[i][s]), b[j], acc[i][j]);
-      if (st != nullptr) store_w(*st, s_w[buf ^ 1], s);
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32x32x16<DT>(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+      if (st != nullptr) store_quarter(*st, buf ^ 1, s);
     }
   };
 
-  AFrag a0, a1;
-  load_a(0, a0);
-  WStage<KB> w0 = load_w(0), w1 = load_w(1);
+  BigStage<KB> s0, s1;
+  load(0, s0);
+  load(1, s1);
 #pragma unroll
-  for (int s = 0; s < 4; ++s) store_w(w0, s_w[0], s);
+  for (int q = 0; q < 4; ++q) store_quarter(s0, 0, q);
   __syncthreads();
   int64_t kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    load_a(kt + 1, a1);
-    w0 = load_w(kt + 2);
+    load(kt + 2, s0);
     prefetch_fence();
-    multiply(0, a0, &w1);  // step kt; step kt + 1's weights into buffer 1
+    multiply(0, &s1);  // step kt; step kt + 1 into buffer 1
     __syncthreads();
-    load_a(kt + 2, a0);
-    w1 = load_w(kt + 3);
+    load(kt + 3, s1);
     prefetch_fence();
-    multiply(1, a1, &w0);  // step kt + 1; step kt + 2's weights into buffer 0
+    multiply(1, &s0);  // step kt + 1; step kt + 2 into buffer 0
     __syncthreads();
   }
-  if (kt < nk) multiply(0, a0, nullptr);
+  if (kt < nk) multiply(0, nullptr);
 
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + 32 * j + r;
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t col = n0 + 64 * wn + 32 * j + r;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+        const int64_t row = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
         if (row < M && col < N) y[row * N + col] = acc[i][j][v];
       }
     }
@@ -559,20 +584,20 @@ hipError_t launch_kb(const void* x, int64_t M, int64_t K, int64_t N, int log2b, 
                      const uint8_t* packed, float* y, const DequantArgs& da, hipStream_t s) {
   if (M <= 32) return launch_mt<DT, KB, 1, 8>(x, M, K, N, log2b, absmax, packed, y, da, s);
   if (M <= 64) return launch_mt<DT, KB, 2, 4>(x, M, K, N, log2b, absmax, packed, y, da, s);
-  // Above 128 rows the LDS-tiled kernel: x and W16 read once per 128 x 128 tile (at 14336 x
-  // 4096: M = 256 56.4 against 95.3 us, M = 1024 181 against 335; M = 128 55.6 against 52.1)
+  // Above 128 rows the LDS-tiled kernels: x and W16 read once per tile (at 14336 x 4096: M =
+  // 256 56.4 against 95.3 us with the register-tiled kernel, M = 1024 181 against 335; M = 128
+  // 55.6 against 52.1).
   if (M <= 128) return launch_mt<DT, KB, 4, 4>(x, M, K, N, log2b, absmax, packed, y, da, s);
-  // The wide form for 8-bit codes, where its grid holds at least 1.5 workgroups per CU (two
-  // fit on each).  8-bit weights take a table read each, so forming them once per 256 rows of
-  // x instead of 128 pays most: at 14336 x 4096, M = 1024 (448 tiles) 170.9 against 202.0 us,
-  // M = 2048 341.8 against 369.0.  For 4-bit codes it was within a few percent either way
-  // (M = 1024 164.8 against 171.8, M = 2048 322.8 against 315.7), and with fewer tiles
-  // (M = 512: 224, M = 768: 336) it was slower.
-  const int64_t wide_tiles = ((N + kWideN - 1) / kWideN) * ((M + kWideM - 1) / kWideM);
-  if (KB == 8 && 2 * wide_tiles >= 3 * (int64_t)cu_count()) {
-    const dim3 grid((unsigned)((N + kWideN - 1) / kWideN), (unsigned)((M + kWideM - 1) / kWideM));
-    return launch_kernel(gemm_wide_kernel<DT, KB>, grid, dim3(256), s, static_cast<const uint8_t*>(x), M, K, N,
-                         log2b, absmax, packed, y, da);
+  // 256 x 256 tiles where the grid keeps at least three quarters of the CUs busy (one
+  // workgroup fills a CU): at 14336 x 4096, M = 1024 (224 tiles), 4-bit 131-144 against
+  // 176-184 us in the 128 x 128 form, 8-bit 143-160 against 180-195 in a 256 x 128 form that
+  // loads x straight into fragments; M = 2048 269 against 332 (4-bit).  With
+  // fewer tiles (M = 512: 112) the CUs left idle cost more than the larger tile saves.
+  const int64_t big_tiles = ((N + kBigN - 1) / kBigN) * ((M + kBigM - 1) / kBigM);
+  if (4 * big_tiles >= 3 * (int64_t)cu_count()) {
+    const dim3 grid((unsigned)((N + kBigN - 1) / kBigN), (unsigned)((M + kBigM - 1) / kBigM));
+    return launch_kernel(gemm_big_kernel<DT, KB>, grid, dim3(kBigThreads), s, static_cast<const uint8_t*>(x), M, K,
+                         N, log2b, absmax, packed, y, da);
   }
   const dim3 grid((unsigned)((N + kTileB - 1) / kTileB), (unsigned)((M + kTileB - 1) / kTileB));
   return launch_kernel(gemm_tiled_kernel<DT, KB>, grid, dim3(256), s, static_cast<const uint8_t*>(x), M, K, N,

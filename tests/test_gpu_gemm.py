@@ -144,17 +144,17 @@ def test_gemm_prefill_shape_sampled_rows(dev, o, K_table, M):
                          "prefill shape table=%d M=%d" % (K_table, M))
 
 
-# With 8-bit codes, grids of at least 1.5 workgroups of 256 x 128 outputs per CU (384 on
-# MI355X's 256 CUs) take the wide form: 1100 x 12290 gives 5 x 97 tiles with ragged last rows
-# and columns, K = 320 an odd number of 64-k steps.  (The 16-entry table runs the same shapes
-# through the 128 x 128 form.)
+# Grids of 256 x 256 tiles that fill at least three quarters of the CUs (192 on MI355X's 256)
+# take the big-tile kernel: 1100 x 12290 gives 5 x 49 tiles, with 76 rows in the last tile row
+# and 2 columns in the last tile column, and K = 320 an odd number of 64-k steps.
 
 
 @pytest.mark.parametrize("dtype", ["bfloat16", "float16"])
 @pytest.mark.parametrize("K_table", [16, 256])
-def test_gemm_wide_form_ragged(dev, o, dtype, K_table):
-    """Seeded random codes and log-normal block maxima; the oracle checks 24 sampled weight
-    rows (first, last and random) for every activation row; a second call gives the same bits."""
+def test_gemm_big_tiles_ragged(dev, o, dtype, K_table):
+    """Seeded random codes and log-normal block maxima; the oracle checks 28 sampled weight
+    rows (tile edges, the last row and random ones) for every activation row; a second call
+    gives the same bits."""
     table = TABLES[K_table]
     M, N, K, B = 1100, 12290, 320, 64
     rng = np.random.default_rng(21 + K_table)
@@ -164,28 +164,37 @@ def test_gemm_wide_form_ragged(dev, o, dtype, K_table):
     y = run_gpu(dev, x, dtype, N, B, table, absmax, packed)
     y2 = run_gpu(dev, x, dtype, N, B, table, absmax, packed)
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
-    rows = np.unique(np.concatenate([[0, 127, 128, N - 1], np.random.default_rng(23).integers(0, N, 20)]))
+    edges = [0, 63, 64, 127, 128, 255, 256, N - 3, N - 2, N - 1]
+    rows = np.unique(np.concatenate([edges, np.random.default_rng(23).integers(0, N, 18)]))
     per_row = K // 2 if K_table == 16 else K
     sub_packed = np.concatenate([packed[r * per_row:(r + 1) * per_row] for r in rows])
     sub_absmax = np.concatenate([absmax[r * (K // B):(r + 1) * (K // B)] for r in rows])
     check_gemm_against_oracle(o, y[:, rows], x, dtype, len(rows), B, table, sub_absmax, sub_packed,
-                              "wide form %s table=%d" % (dtype, K_table))
+                              "big tiles %s table=%d" % (dtype, K_table))
 
 
-def test_gemm_wide_form_exact(dev, o):
-    """A dyadic 256-entry table (k / 128 for k = -128 .. 127, each exact in both 16-bit types),
-    power-of-two block maxima and small integer activations on a grid the wide form takes
-    (1030 x 9860: 5 x 78 tiles): every weight and partial sum is exact, so sampled weight rows
-    must equal the oracle's values exactly (a row, column or k mixed up in the fragment layout
-    changes them)."""
-    table = (np.arange(-128, 128) / 128.0).astype(np.float32)
+@pytest.mark.parametrize("K_table", [16, 256])
+def test_gemm_big_tiles_exact(dev, o, K_table):
+    """A dyadic table (k / 8 for k = -8 .. 7, or k / 128 for k = -128 .. 127, each exact in both
+    16-bit types), power-of-two block maxima and small integer activations on a grid the
+    big-tile kernel takes (1030 x 9860: 5 x 39 tiles): every weight and partial sum is exact,
+    so sampled weight rows must equal the oracle's values exactly (a row, column or k mixed up
+    in the fragment or staging layout changes them)."""
+    half = K_table // 2
+    table = (np.arange(-half, half) / half).astype(np.float32)
     M, N, K, B = 1030, 9860, 128, 64
-    q = (np.arange(N)[:, None] * 5 + np.arange(K)[None, :] * 3 + np.arange(N)[:, None] // 9) % 256
-    packed = q.reshape(-1).astype(np.uint8)
+    q = (np.arange(N)[:, None] * 5 + np.arange(K)[None, :] * 3 + np.arange(N)[:, None] // 9) % K_table
+    if K_table == 16:  # two codes per byte, the first in the high nibble
+        q = q.reshape(-1)
+        packed = ((q[0::2] << 4) | q[1::2]).astype(np.uint8)
+    else:
+        packed = q.reshape(-1).astype(np.uint8)
+    per_row = K // 2 if K_table == 16 else K
     absmax = np.ldexp(np.float32(1), (np.arange(N * K // B) % 5) - 2).astype(np.float32)
     xi = ((np.arange(M * K).reshape(M, K) * 7 + np.arange(M)[:, None] // 13) % 11 - 5).astype(np.float32)
-    rows = np.unique(np.concatenate([[0, 31, 32, 127, 128, N - 1], np.random.default_rng(24).integers(0, N, 30)]))
-    sub_packed = np.concatenate([packed[r * K:(r + 1) * K] for r in rows])
+    edges = [0, 31, 32, 63, 64, 127, 128, 255, 256, N - 1]
+    rows = np.unique(np.concatenate([edges, np.random.default_rng(24).integers(0, N, 30)]))
+    sub_packed = np.concatenate([packed[r * per_row:(r + 1) * per_row] for r in rows])
     sub_absmax = np.concatenate([absmax[r * (K // B):(r + 1) * (K // B)] for r in rows])
     for dtype in ("bfloat16", "float16"):
         x = torch.from_numpy(xi).to(TORCH_DT[dtype])

@@ -54,12 +54,12 @@ def test_graph_replay_matches_oracle(dev, po):
     xl = torch.randn(Ml, Kl, device=dev, generator=gen).to(torch.bfloat16)
     Mg, Ng = 40, 1000  # fused GEMM on the first 1000 rows of that weight
     xg = torch.randn(Mg, Kl, device=dev, generator=gen).to(torch.bfloat16)
-    # fused GEMM in its wide form: 8-bit codes, 1024 x 12288 outputs (4 x 96 tiles), K = 128
+    # fused GEMM in its 256 x 256 tile form: 8-bit codes, 1024 x 12288 outputs (4 x 48 tiles), K = 128
     Mw, Kw, Nw = 1024, 128, 12288
     wpk8 = torch.randint(0, 256, (Nw * Kw,), dtype=torch.uint8, device=dev, generator=gen)
     wam8 = 0.01 + 0.02 * torch.rand(Nw * Kw // B, device=dev, generator=gen)
     xw = torch.randn(Mw, Kw, device=dev, generator=gen).to(torch.bfloat16)
-    wrows = np.unique(np.concatenate([[0, 127, 128, Nw - 1], np.random.default_rng(44).integers(0, Nw, 12)]))
+    wrows = np.unique(np.concatenate([[0, 127, 128, 255, 256, Nw - 1], np.random.default_rng(44).integers(0, Nw, 12)]))
 
     # the oracle's outputs for the same inputs
     xb = host_bits(x)
