@@ -402,46 +402,50 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint8_t* x, int64
     }
 }
 
-// Large batches, big tiles: a 256 x 256 output tile per workgroup (256 rows of x, 256 rows of
-// W), eight waves arranged 2 x 4, each owning 128 x 64 outputs (4 x 2 accumulator tiles), two
-// waves per SIMD.  K in LDS-staged steps of 64 with two buffers that alternate.
+// Large batches, big tiles: a 256 x TW output tile per workgroup (256 rows of x, TW = 256 or 128
+// rows of W), eight waves, each owning 64 columns: arranged 2 x 4 (128 x 64 outputs, 4 x 2
+// accumulator tiles) for TW = 256, 4 x 2 (64 x 64, 2 x 2 tiles) for TW = 128; two waves per
+// SIMD.  K in LDS-staged steps of 64 with two buffers that alternate.
 //
 // Staging: the step's tiles are loaded as 16-byte chunks, chunk c of a tile going to thread
 // c % 512 (consecutive threads take consecutive chunks of a row, so each load instruction
 // covers whole rows): x has 8 chunks per row (64 k), W 2 (4-bit codes, 32 k each) or 4 (8-bit,
 // 16 k each), each W chunk with the scale of its block (B >= 32, so one scale serves a chunk).
+// With 128 rows of 4-bit codes (256 chunks) the first four waves stage W.
 // A step's loads are issued one step ahead into one of two register stages, and the stage of
 // the next step is formed and written into the other LDS buffer a quarter at a time between
 // the current step's MFMAs.
 constexpr int kBigM = 256;
-constexpr int kBigN = 256;
 constexpr int kBigThreads = 512;
 
-template <int KB>
+template <int KB, int TW>
 struct BigStage {
-  static constexpr int kW = kBigN * (KB == 4 ? 2 : 4) / kBigThreads;  // W chunks per thread
+  static constexpr int kWtot = TW * (KB == 4 ? 2 : 4);  // W chunks per tile
+  static constexpr int kW = kWtot >= kBigThreads ? kWtot / kBigThreads : 1;  // per thread
   u32x4 x[4];
   u32x4 w[kW];
   float a[kW];
 };
 
-template <int DT, int KB>
+template <int DT, int KB, int TW>
 __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const uint8_t* x, int64_t M, int64_t K,
                                                                   int64_t N, int log2b, const float* absmax,
                                                                   const uint8_t* packed, float* __restrict__ y,
                                                                   DequantArgs da) {
-  constexpr int NI = 4, NJ = 2;           // accumulator tiles per wave (128 x 64 outputs)
+  constexpr int WGN = TW / 64;            // waves along W (64 columns each)
+  constexpr int NI = 256 / (8 / WGN) / 32, NJ = 2;  // accumulator tiles per wave
   constexpr int kCpr = KB == 4 ? 2 : 4;   // W chunks per row
-  constexpr int kW = BigStage<KB>::kW;
+  constexpr int kW = BigStage<KB, TW>::kW;
+  const bool wstage = BigStage<KB, TW>::kWtot >= kBigThreads || threadIdx.x < BigStage<KB, TW>::kWtot;  // uniform per wave
   __shared__ float2 s_pair[KB == 4 ? 256 : 1];
   __shared__ float s_c[KB == 8 ? 256 : 1];
   __shared__ __attribute__((aligned(16))) uint16_t s_x[2][kBigM * kRowPad];
-  __shared__ __attribute__((aligned(16))) uint16_t s_w[2][kBigN * kRowPad];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[2][TW * kRowPad];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r = lane & 31;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / WGN, wn = wave % WGN;
   if (tid < 256) {
     if constexpr (KB == 4) s_pair[tid] = make_float2(da.c[tid >> 4], da.c[tid & 15]);
     else s_c[tid] = da.c[tid];
@@ -449,7 +453,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const uint8_t*
   __syncthreads();
 
   const int64_t m0 = (int64_t)blockIdx.y * kBigM;
-  const int64_t n0 = (int64_t)blockIdx.x * kBigN;
+  const int64_t n0 = (int64_t)blockIdx.x * TW;
   const int64_t nk = K / kTileK;
   // x chunk i of this thread: row 64 i + tid / 8 of the tile, bytes 16 (tid % 8) of its 128;
   // rows past M read the last row and are never stored
@@ -472,12 +476,13 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const uint8_t*
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  auto load = [&](int64_t kt, BigStage<KB>& st) {
+  auto load = [&](int64_t kt, BigStage<KB, TW>& st) {
     const int64_t k0 = min(kt, nk - 1) * kTileK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) st.x[i] = *reinterpret_cast<const u32x4*>(xsrc[i] + k0 * 2);
 #pragma unroll
     for (int i = 0; i < kW; ++i) {
+      if (!wstage) break;
       const int64_t f = wflat[i] + k0;
       st.w[i] = *reinterpret_cast<const u32x4*>(packed + (KB == 4 ? (f >> 1) : f));
       st.a[i] = absmax[f >> log2b];
@@ -485,10 +490,11 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const uint8_t*
   };
   // Quarter q of a stage into LDS buffer buf: x chunk q, and a quarter of each W chunk's
   // weights (4-bit: 8 of its 32; 8-bit: 4 of its 16).
-  auto store_quarter = [&](const BigStage<KB>& st, int buf, int q) {
+  auto store_quarter = [&](const BigStage<KB, TW>& st, int buf, int q) {
     *reinterpret_cast<u32x4*>(&s_x[buf][(64 * q + (tid >> 3)) * kRowPad + 8 * (tid & 7)]) = st.x[q];
 #pragma unroll
     for (int i = 0; i < kW; ++i) {
+      if (!wstage) break;
       const int c = kBigThreads * i + tid;
       const int row = c / kCpr, ch = c % kCpr;
       const uint32_t word = st.w[i][q];
@@ -511,14 +517,14 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const uint8_t*
   auto frags = [&](int buf, int s, uint4 (&fa)[NI], uint4 (&fb)[NJ]) {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      fa[i] = *reinterpret_cast<const uint4*>(&s_x[buf][(128 * wm + 32 * i + r) * kRowPad + 16 * s + 8 * g]);
+      fa[i] = *reinterpret_cast<const uint4*>(&s_x[buf][(32 * NI * wm + 32 * i + r) * kRowPad + 16 * s + 8 * g]);
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
       fb[j] = *reinterpret_cast<const uint4*>(&s_w[buf][(64 * wn + 32 * j + r) * kRowPad + 16 * s + 8 * g]);
   };
   // The step in buffer buf; with st, the next step's stage is written into the other buffer
   // a quarter per 16-k piece.  The fragments of piece s + 1 are read before the MFMAs of piece s.
-  auto multiply = [&](int buf, const BigStage<KB>* st) {
+  auto multiply = [&](int buf, const BigStage<KB, TW>* st) {
     uint4 fa[2][NI], fb[2][NJ];
     frags(buf, 0, fa[0], fb[0]);
 #pragma unroll
@@ -532,7 +538,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const uint8_t*
     }
   };
 
-  BigStage<KB> s0, s1;
+  BigStage<KB, TW> s0, s1;
   load(0, s0);
   load(1, s1);
 #pragma unroll
@@ -558,7 +564,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const uint8_t*
       const int64_t col = n0 + 64 * wn + 32 * j + r;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+        const int64_t row = m0 + 32 * NI * wm + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
         if (row < M && col < N) y[row * N + col] = acc[i][j][v];
       }
     }
@@ -588,16 +594,26 @@ hipError_t launch_kb(const void* x, int64_t M, int64_t K, int64_t N, int log2b, 
   // 256 56.4 against 95.3 us with the register-tiled kernel, M = 1024 181 against 335; M = 128
   // 55.6 against 52.1).
   if (M <= 128) return launch_mt<DT, KB, 4, 4>(x, M, K, N, log2b, absmax, packed, y, da, s);
-  // 256 x 256 tiles where the grid keeps at least three quarters of the CUs busy (one
-  // workgroup fills a CU): at 14336 x 4096, M = 1024 (224 tiles), 4-bit 131-144 against
-  // 176-184 us in the 128 x 128 form, 8-bit 143-160 against 180-195 in a 256 x 128 form that
-  // loads x straight into fragments; M = 2048 269 against 332 (4-bit).  With
-  // fewer tiles (M = 512: 112) the CUs left idle cost more than the larger tile saves.
-  const int64_t big_tiles = ((N + kBigN - 1) / kBigN) * ((M + kBigM - 1) / kBigM);
-  if (4 * big_tiles >= 3 * (int64_t)cu_count()) {
-    const dim3 grid((unsigned)((N + kBigN - 1) / kBigN), (unsigned)((M + kBigM - 1) / kBigM));
-    return launch_kernel(gemm_big_kernel<DT, KB>, grid, dim3(kBigThreads), s, static_cast<const uint8_t*>(x), M, K,
-                         N, log2b, absmax, packed, y, da);
+  // 256-row tiles (one workgroup fills a CU).  256 x 128 tiles when they fill at least three
+  // quarters of the CUs in one round: at 14336 x 4096, M = 512 (224 tiles) 4-bit 77 against
+  // 90 us in the 128 x 128 form, 8-bit 84 against 108; M = 384 75 against 82 and 80 against
+  // 102.  Otherwise 256 x 256 tiles when they fill at least half of the CUs: M = 1024 (224
+  // tiles), 4-bit 131-144 against 176-184 us in the 128 x 128 form, 8-bit 143-160 against
+  // 180-195 in a 256 x 128 form that loads x straight into fragments; M = 2048 269 against
+  // 332 (4-bit); M = 768 (168 tiles) about the M = 1024 time, against 138 (in two rounds of
+  // 256 x 128 tiles 146).  Smaller grids keep the 128 x 128 form, two workgroups per CU.
+  const int64_t mt = (M + kBigM - 1) / kBigM;
+  const int64_t cus = cu_count();
+  const int64_t t128 = ((N + 127) / 128) * mt, t256 = ((N + 255) / 256) * mt;
+  if (t128 <= cus && 4 * t128 >= 3 * cus) {
+    const dim3 grid((unsigned)((N + 127) / 128), (unsigned)mt);
+    return launch_kernel(gemm_big_kernel<DT, KB, 128>, grid, dim3(kBigThreads), s, static_cast<const uint8_t*>(x), M,
+                         K, N, log2b, absmax, packed, y, da);
+  }
+  if (2 * t256 >= cus) {
+    const dim3 grid((unsigned)((N + 255) / 256), (unsigned)mt);
+    return launch_kernel(gemm_big_kernel<DT, KB, 256>, grid, dim3(kBigThreads), s, static_cast<const uint8_t*>(x), M,
+                         K, N, log2b, absmax, packed, y, da);
   }
   const dim3 grid((unsigned)((N + kTileB - 1) / kTileB), (unsigned)((M + kTileB - 1) / kTileB));
   return launch_kernel(gemm_tiled_kernel<DT, KB>, grid, dim3(256), s, static_cast<const uint8_t*>(x), M, K, N,

@@ -144,19 +144,22 @@ def test_gemm_prefill_shape_sampled_rows(dev, o, K_table, M):
                          "prefill shape table=%d M=%d" % (K_table, M))
 
 
-# Grids of 256 x 256 tiles that fill at least three quarters of the CUs (192 on MI355X's 256)
-# take the big-tile kernel: 1100 x 12290 gives 5 x 49 tiles, with 76 rows in the last tile row
-# and 2 columns in the last tile column, and K = 320 an odd number of 64-k steps.
+# Grids of 256-row tiles take the big-tile kernel (on MI355X's 256 CUs): 256 x 128 tiles when
+# 192 to 256 of them cover the output, else 256 x 256 tiles when at least 128 do.  300 x 12200
+# gives 2 x 96 tiles of 256 x 128 (44 rows in the last tile row, 40 columns in the last tile
+# column); 1100 x 12290 gives 5 x 49 tiles of 256 x 256 (76 rows, 2 columns); K = 320 is an
+# odd number of 64-k steps.
 
 
 @pytest.mark.parametrize("dtype", ["bfloat16", "float16"])
 @pytest.mark.parametrize("K_table", [16, 256])
-def test_gemm_big_tiles_ragged(dev, o, dtype, K_table):
-    """Seeded random codes and log-normal block maxima; the oracle checks 28 sampled weight
+@pytest.mark.parametrize("M,N", [(300, 12200), (1100, 12290)])
+def test_gemm_big_tiles_ragged(dev, o, dtype, K_table, M, N):
+    """Seeded random codes and log-normal block maxima; the oracle checks about 30 sampled weight
     rows (tile edges, the last row and random ones) for every activation row; a second call
     gives the same bits."""
     table = TABLES[K_table]
-    M, N, K, B = 1100, 12290, 320, 64
+    K, B = 320, 64
     rng = np.random.default_rng(21 + K_table)
     packed = rng.integers(0, 256, size=N * K // 2 if K_table == 16 else N * K, dtype=np.uint8)
     absmax = (0.02 * np.exp(rng.standard_normal(N * K // B))).astype(np.float32)
@@ -164,7 +167,7 @@ def test_gemm_big_tiles_ragged(dev, o, dtype, K_table):
     y = run_gpu(dev, x, dtype, N, B, table, absmax, packed)
     y2 = run_gpu(dev, x, dtype, N, B, table, absmax, packed)
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
-    edges = [0, 63, 64, 127, 128, 255, 256, N - 3, N - 2, N - 1]
+    edges = [0, 63, 64, 127, 128, 255, 256, N - 41, N - 40, N - 3, N - 2, N - 1]
     rows = np.unique(np.concatenate([edges, np.random.default_rng(23).integers(0, N, 18)]))
     per_row = K // 2 if K_table == 16 else K
     sub_packed = np.concatenate([packed[r * per_row:(r + 1) * per_row] for r in rows])
@@ -174,15 +177,17 @@ def test_gemm_big_tiles_ragged(dev, o, dtype, K_table):
 
 
 @pytest.mark.parametrize("K_table", [16, 256])
-def test_gemm_big_tiles_exact(dev, o, K_table):
+@pytest.mark.parametrize("M,N", [(500, 12250), (1030, 9860)])
+def test_gemm_big_tiles_exact(dev, o, K_table, M, N):
     """A dyadic table (k / 8 for k = -8 .. 7, or k / 128 for k = -128 .. 127, each exact in both
     16-bit types), power-of-two block maxima and small integer activations on a grid the
-    big-tile kernel takes (1030 x 9860: 5 x 39 tiles): every weight and partial sum is exact,
+    big-tile kernel takes (500 x 12250: 2 x 96 tiles of 256 x 128; 1030 x 9860: 5 x 39 tiles of
+    256 x 256): every weight and partial sum is exact,
     so sampled weight rows must equal the oracle's values exactly (a row, column or k mixed up
     in the fragment or staging layout changes them)."""
     half = K_table // 2
     table = (np.arange(-half, half) / half).astype(np.float32)
-    M, N, K, B = 1030, 9860, 128, 64
+    K, B = 128, 64
     q = (np.arange(N)[:, None] * 5 + np.arange(K)[None, :] * 3 + np.arange(N)[:, None] // 9) % K_table
     if K_table == 16:  # two codes per byte, the first in the high nibble
         q = q.reshape(-1)
