@@ -66,6 +66,7 @@ SHAPES = [  # (M, K, N, B): single tiles, ragged rows and columns, several chunk
     # M = 129 the LDS-tiled kernel, with an odd number of 64-k steps (K = 192, 320)
     (1, 64, 1, 32), (5, 128, 33, 64), (32, 256, 64, 128), (33, 512, 65, 32), (64, 1024, 100, 256),
     (70, 192, 130, 4096), (129, 2048, 37, 1024), (257, 192, 131, 64), (300, 320, 260, 512),
+    (200, 256, 100, 32),
 ]
 
 
@@ -153,16 +154,16 @@ def test_gemm_prefill_shape_sampled_rows(dev, o, K_table, M):
 
 @pytest.mark.parametrize("dtype", ["bfloat16", "float16"])
 @pytest.mark.parametrize("K_table", [16, 256])
-@pytest.mark.parametrize("M,N", [(300, 12200), (1100, 12290)])
-def test_gemm_big_tiles_ragged(dev, o, dtype, K_table, M, N):
+@pytest.mark.parametrize("M,N,B", [(300, 12200, 32), (300, 12200, 64), (1100, 12290, 32), (1100, 12290, 64)])
+def test_gemm_big_tiles_ragged(dev, o, dtype, K_table, M, N, B):
     """Seeded random codes and log-normal block maxima; the oracle checks about 30 sampled weight
     rows (tile edges, the last row and random ones) for every activation row; a second call
     gives the same bits."""
     table = TABLES[K_table]
-    K, B = 320, 64
+    K = 320
     rng = np.random.default_rng(21 + K_table)
     packed = rng.integers(0, 256, size=N * K // 2 if K_table == 16 else N * K, dtype=np.uint8)
-    absmax = (0.02 * np.exp(rng.standard_normal(N * K // B))).astype(np.float32)
+    absmax = (0.02 * np.exp(rng.standard_normal(-(-N * K // B)))).astype(np.float32)
     x = activations(M, K, dtype, seed=22)
     y = run_gpu(dev, x, dtype, N, B, table, absmax, packed)
     y2 = run_gpu(dev, x, dtype, N, B, table, absmax, packed)
@@ -174,6 +175,22 @@ def test_gemm_big_tiles_ragged(dev, o, dtype, K_table, M, N):
     sub_absmax = np.concatenate([absmax[r * (K // B):(r + 1) * (K // B)] for r in rows])
     check_gemm_against_oracle(o, y[:, rows], x, dtype, len(rows), B, table, sub_absmax, sub_packed,
                               "big tiles %s table=%d" % (dtype, K_table))
+
+
+@pytest.mark.parametrize("K_table", [16, 256])
+def test_gemm_big_tiles_blocks_across_rows(dev, o, K_table):
+    """Blocks of 256 over rows of K = 64 (each block spans four weight rows, so the scale of a
+    staged chunk is not the scale of its row's first chunk) on a grid of 3 x 43 tiles of
+    256 x 256 (520 x 11000: ragged in both directions); every output against the oracle."""
+    table = TABLES[K_table]
+    M, N, K, B = 520, 11000, 64, 256
+    rng = np.random.default_rng(31 + K_table)
+    packed = rng.integers(0, 256, size=N * K // 2 if K_table == 16 else N * K, dtype=np.uint8)
+    absmax = (0.02 * np.exp(rng.standard_normal(-(-N * K // B)))).astype(np.float32)
+    x = activations(M, K, "bfloat16", seed=32)
+    y = run_gpu(dev, x, "bfloat16", N, B, table, absmax, packed)
+    check_gemm_against_oracle(o, y, x, "bfloat16", N, B, table, absmax, packed,
+                              "blocks across rows table=%d" % K_table)
 
 
 @pytest.mark.parametrize("K_table", [16, 256])
