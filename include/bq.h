@@ -205,7 +205,7 @@ bq_status bq_linear_blockwise(const void* x, bq_dtype dtype, int64_t M, int64_t 
  * Each product x[m][k] * w16[n][k] is exact in binary32; the products are accumulated in
  * binary32 in an unspecified order, so y[m][n] lies within (K + 64) * 2^-24 * sum_k
  * |x[m][k] w16[n][k]| of the exact sum (products below the binary32 normal range may be
- * flushed to zero by the matrix cores).  The result is the same on every call.
+ * flushed to zero by the matrix cores).  The result is the same on every call on one device.
  * Errors: BQ_ERR_DTYPE for BQ_F32; BQ_ERR_SIZE for M outside [1, 4194240], K not a positive
  * multiple of 64, N outside [0, 536870848], or more than INT32_MAX blocks; otherwise as
  * bq_dequantize_blockwise. */
