@@ -655,8 +655,9 @@ def cpu_baseline_and_parity(w: Workload, torch, gpu: dict):
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the method needs no cross-GPU communication, and each GPU "
-              "would quantize its own shard independently; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: each GPU would run these kernels on its own shard of "
+              "whole blocks, with no communication except, for nested statistics, one all-gather of "
+              "8-byte partial sums of the mean; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
 
