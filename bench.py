@@ -20,8 +20,9 @@ oracle's outputs are also this run's parity reference (`parity`: every output by
 step's calls against the oracle's).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 40] [--no-detail] [--no-cpu-baseline]
-    python bench.py --profile     (a few launches of each kernel, the bf16 2^26 8-bit calls and the
-                                   IQ2_XS encode / decode, then a 1 GiB copy, for rocprofv3)
+    python bench.py --profile     (a few launches of each kernel, the bf16 2^26 8-bit calls, the
+                                   IQ2_XS and IQ1_S encode / decode and the fused GEMM at
+                                   14336 x 4096, then a 1 GiB copy, for rocprofv3)
 """
 from __future__ import annotations
 
@@ -702,6 +703,20 @@ def main():
         for _ in range(3):
             bq.check(bq.bq_iq1s_dequantize(b7, g7, n6, cols6, bq.BQ_BF16, o6), "iq1s dequantize")
         del x6, o6
+        # the fused dequantize + GEMM on a 14336 x 4096 weight at M = 256, 512 and 1024 (the
+        # 128 x 128, 256 x 128 and 256 x 256 tile forms), 4- and 8-bit codes
+        gN, gK = 14336, 4096
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(5)
+        for table, per in ((w.t16, gN * gK // 2), (w.t256, gN * gK)):
+            gp = torch.randint(0, 256, (per,), dtype=torch.uint8, device=dev, generator=gen)
+            ga = (0.02 * torch.exp(torch.randn(gN * gK // 64, device=dev, generator=gen))).float()
+            for M in (256, 512, 1024):
+                gx = torch.randn(M, gK, device=dev, generator=gen).to(torch.bfloat16)
+                gy = torch.empty(M, gN, device=dev)
+                for _ in range(3):
+                    bq.check(bq.bq_gemm_blockwise(gx, bq.BQ_BF16, M, gK, gN, 64, table, ga, gp, gy), "gemm")
+            del gp, ga, gx, gy
         src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
